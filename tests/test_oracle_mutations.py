@@ -1,0 +1,96 @@
+"""Planted mistakes: each mutant copy of the oracle (built on the CPU from its source with one
+plausible error) must fail at least one of the pins, showing that the pins constrain the oracle."""
+import inspect
+import types
+
+import numpy as np
+import pytest
+
+from oracle import mla_oracle as O
+import tests.test_oracle_attention as TA
+import tests.test_oracle_codec_norms as TC
+
+MUTANTS = {
+    "rope_sign": ("ra = a * c - b * s", "ra = a * c + b * s",
+                  [(TC, "test_rope_hand_case"), (TA, "test_query_path_matches_torch_complex_route")]),
+    "kv_halves_swapped": ("return w[:, :NOPE, :], w[:, NOPE:, :]", "return w[:, V_DIM:, :], w[:, :V_DIM, :]",
+                          [(TA, "test_value_half_is_last_rows_of_each_head")]),
+    "query_heads_transposed": ("q = q.reshape(q.shape[0], n_heads, QK)",
+                               "q = q.reshape(q.shape[0], QK, n_heads).transpose(0, 2, 1).copy()",
+                               [(TA, "test_query_path_shape_and_head_column_ownership")]),
+    "rotary_score_dropped": ("s = scale * (q_lat @ c.T + np.asarray(q_pe, np.float64) @ pe.T)",
+                             "s = scale * (q_lat @ c.T)",
+                             [(TA, "test_decode_matches_torch_sdpa")]),
+    "scale_dropped": ("s = scale * (q_lat @ c.T + np.asarray(q_pe, np.float64) @ pe.T)",
+                      "s = (q_lat @ c.T + np.asarray(q_pe, np.float64) @ pe.T)",
+                      [(TA, "test_decode_matches_torch_sdpa")]),
+    "absorb_through_value_half": ("uk, _ = wkv_b_heads(bf16_decode(wkv_b_bits), q.shape[0])",
+                                  "_, uk = wkv_b_heads(bf16_decode(wkv_b_bits), q.shape[0])",
+                                  [(TA, "test_absorbed_equals_expanded")]),
+    "causal_diagonal_dropped": ("s = scale * (k[: t + 1] @ q_h[t])", "s = scale * (k[: max(t, 1)] @ q_h[t])",
+                                [(TA, "test_prefill_first_row_future_rows_and_sdpa")]),
+    "rms_sum_not_mean": ("m2 = np.mean(x * x, axis=-1, keepdims=True)", "m2 = np.sum(x * x, axis=-1, keepdims=True)",
+                         [(TC, "test_rmsnorm_hand_case"), (TC, "test_rmsnorm_unit_rms_and_eps_shrink")]),
+    "layernorm_unbiased": ("var = np.mean((x - mu) ** 2, axis=-1, keepdims=True)",
+                           "var = np.var(x, axis=-1, ddof=1, keepdims=True)",
+                           [(TC, "test_layernorm_hand_case")]),
+    "combine_weight_sign": ("w = np.where(np.isfinite(ls), np.exp(ls - safe_M), 0.0)",
+                            "w = np.where(np.isfinite(ls), np.exp(safe_M - ls), 0.0)",
+                            [(TA, "test_split_partition_invariance")]),
+    "bf16_truncates": ("r = np.rint(flat[fin] * np.exp2(-q)) * np.exp2(q)",
+                       "r = np.trunc(flat[fin] * np.exp2(-q)) * np.exp2(q)",
+                       [(TC, "test_bf16_encode_matches_torch_on_fp32_values")]),
+    "gain_ignored": ("y = np.asarray(gamma, dtype=np.float64) * (x * inv)", "y = (x * inv) + 0 * np.asarray(gamma)",
+                     [(TA, "test_query_path_matches_torch_complex_route")]),
+}
+
+
+def _mutant(old, new):
+    src = inspect.getsource(O)
+    assert src.count(old) == 1, old
+    m = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), m.__dict__)
+    return m
+
+
+def _call(fn):
+    sig = inspect.signature(fn)
+    if not sig.parameters:
+        fn()
+        return
+    # parametrised pins: run every parameter set of the pin
+    marks = [m for m in getattr(fn, "pytestmark", []) if m.name == "parametrize"]
+    names, values = marks[0].args
+    names = [n.strip() for n in names.split(",")]
+    for v in values:
+        v = v if isinstance(v, (tuple, list)) and len(names) > 1 else (v,)
+        fn(**dict(zip(names, v)))
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, monkeypatch):
+    old, new, pins = MUTANTS[name]
+    m = _mutant(old, new)
+    caught = []
+    for mod, pin in pins:
+        monkeypatch.setattr(mod, "O", m)
+        try:
+            with np.errstate(all="ignore"):
+                _call(getattr(mod, pin))
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            caught.append(pin)
+        finally:
+            monkeypatch.setattr(mod, "O", O)
+    assert caught, f"mutant {name} survived {pins}"
+
+
+def test_unmutated_source_passes_the_same_pins():
+    m = _mutant("import numpy as np", "import numpy as np")
+    for _, (old, new, pins) in MUTANTS.items():
+        for mod, pin in pins:
+            orig = mod.O
+            mod.O = m
+            try:
+                _call(getattr(mod, pin))
+            finally:
+                mod.O = orig
