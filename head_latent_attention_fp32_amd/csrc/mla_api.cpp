@@ -1,0 +1,156 @@
+// C ABI of libmla: host-side argument validation, workspace sizing and kernel dispatch.
+// Validation runs before any HIP call; a rejected call enqueues nothing.
+#include <math.h>
+
+#include "../../include/mla.h"
+#include "mla_internal.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+mla_status_t check_dims(const mla_dims_t* d) {
+  if (!d) return MLA_ERR_INVALID_ARG;
+  if (d->q_lora_rank != 1536 || d->kv_lora_rank != 512 || d->qk_nope_dim != 128 || d->qk_rope_dim != 64 ||
+      d->v_head_dim != 128)
+    return MLA_ERR_UNSUPPORTED;
+  if (d->n_heads != 16 && d->n_heads != 32 && d->n_heads != 64 && d->n_heads != 128) return MLA_ERR_UNSUPPORTED;
+  if (!isfinite(d->softmax_scale) || !(d->softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
+  if (!isfinite(d->rms_eps) || d->rms_eps < 0.f) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+// The largest decode batch: the combine kernel's grid x and the int32 sequence index.
+constexpr int64_t kMaxBatch = 1 << 24;
+// The largest query-path token count (grid y = ceil(n / 64) stays far below 2^31).
+constexpr int64_t kMaxTokens = int64_t(1) << 36;
+
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_dims_default(int32_t n_heads, mla_dims_t* dims) {
+  if (!dims) return MLA_ERR_INVALID_ARG;
+  dims->n_heads = n_heads;
+  dims->q_lora_rank = 1536;
+  dims->kv_lora_rank = 512;
+  dims->qk_nope_dim = 128;
+  dims->qk_rope_dim = 64;
+  dims->v_head_dim = 128;
+  dims->softmax_scale = 1.0f / sqrtf(192.0f);
+  dims->rms_eps = 1e-6f;
+  return check_dims(dims);
+}
+
+mla_status_t mla_query_path_ex(const mla_dims_t* dims, int64_t n_tokens, const uint16_t* q_latent,
+                               const float* q_norm_w, const uint16_t* wq_b, const float* rope_cs, uint16_t* q_out,
+                               float* inv_rms, hipStream_t stream, hipEvent_t* stage_events) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_tokens < 0 || n_tokens > kMaxTokens) return MLA_ERR_SHAPE;
+  if (n_tokens == 0) return MLA_OK;
+  if (!q_latent || !q_norm_w || !wq_b || !rope_cs || !q_out) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q_latent) || !aligned16(q_norm_w) || !aligned16(wq_b) || !aligned16(rope_cs) ||
+      !aligned16(q_out) || (inv_rms && !aligned16(inv_rms)))
+    return MLA_ERR_ALIGNMENT;
+  hipError_t e = mla::launch_query_path(dims->n_heads, n_tokens, q_latent, q_norm_w, wq_b, rope_cs, q_out, inv_rms,
+                                        dims->rms_eps, stream, stage_events);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_query_path(const mla_dims_t* dims, int64_t n_tokens, const uint16_t* q_latent,
+                            const float* q_norm_w, const uint16_t* wq_b, const float* rope_cs, uint16_t* q_out,
+                            float* inv_rms, hipStream_t stream) {
+  return mla_query_path_ex(dims, n_tokens, q_latent, q_norm_w, wq_b, rope_cs, q_out, inv_rms, stream, nullptr);
+}
+
+mla_status_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch, int64_t max_seqlen, size_t* bytes) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!bytes) return MLA_ERR_INVALID_ARG;
+  if (batch < 0 || batch > kMaxBatch || max_seqlen < 0 || max_seqlen > (int64_t(1) << 40)) return MLA_ERR_SHAPE;
+  *bytes = batch == 0 ? 0 : mla::decode_layout(dims->n_heads, batch, max_seqlen).total;
+  return MLA_OK;
+}
+
+mla_status_t mla_decode_ex(const mla_dims_t* dims, int32_t batch, const uint16_t* q, const uint16_t* wkv_b,
+                           const uint16_t* kv_cache, const uint16_t* pe_cache, const int64_t* cache_row_offset,
+                           const int32_t* cache_seqlens, int64_t max_seqlen, void* workspace,
+                           size_t workspace_bytes, uint16_t* out, float* lse, hipStream_t stream,
+                           hipEvent_t* stage_events) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || batch > kMaxBatch || max_seqlen < 0 || max_seqlen > (int64_t(1) << 40)) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!q || !wkv_b || !kv_cache || !pe_cache || !cache_seqlens || !workspace || !out) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(wkv_b) || !aligned16(kv_cache) || !aligned16(pe_cache) ||
+      !aligned16(cache_seqlens) || !aligned16(workspace) || !aligned16(out) ||
+      (cache_row_offset && !aligned16(cache_row_offset)) || (lse && !aligned16(lse)))
+    return MLA_ERR_ALIGNMENT;
+  const mla::DecodeLayout lay = mla::decode_layout(dims->n_heads, batch, max_seqlen);
+  if (workspace_bytes < lay.total) return MLA_ERR_WORKSPACE;
+  hipError_t e = mla::launch_decode(dims->n_heads, batch, q, wkv_b, kv_cache, pe_cache, cache_row_offset,
+                                    cache_seqlens, max_seqlen, workspace, lay, out, lse, dims->softmax_scale, stream,
+                                    stage_events);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, const uint16_t* q, const uint16_t* wkv_b,
+                        const uint16_t* kv_cache, const uint16_t* pe_cache, const int64_t* cache_row_offset,
+                        const int32_t* cache_seqlens, int64_t max_seqlen, void* workspace, size_t workspace_bytes,
+                        uint16_t* out, float* lse, hipStream_t stream) {
+  return mla_decode_ex(dims, batch, q, wkv_b, kv_cache, pe_cache, cache_row_offset, cache_seqlens, max_seqlen,
+                       workspace, workspace_bytes, out, lse, stream, nullptr);
+}
+
+mla_status_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t seqlen, size_t* bytes) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!bytes) return MLA_ERR_INVALID_ARG;
+  if (batch < 0 || batch > 65535 || seqlen < 0) return MLA_ERR_SHAPE;
+  *bytes = (batch == 0 || seqlen == 0) ? 0 : mla::prefill_layout(dims->n_heads, batch, seqlen).total;
+  return MLA_OK;
+}
+
+mla_status_t mla_prefill_ex(const mla_dims_t* dims, int32_t batch, int32_t seqlen, const uint16_t* q,
+                            const uint16_t* kv_latent, const uint16_t* k_pe, const uint16_t* wkv_b, void* workspace,
+                            size_t workspace_bytes, uint16_t* out, float* lse, hipStream_t stream,
+                            hipEvent_t* stage_events) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || batch > 65535 || seqlen < 0) return MLA_ERR_SHAPE;
+  if (batch == 0 || seqlen == 0) return MLA_OK;
+  if (!q || !kv_latent || !k_pe || !wkv_b || !workspace || !out) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kv_latent) || !aligned16(k_pe) || !aligned16(wkv_b) || !aligned16(workspace) ||
+      !aligned16(out) || (lse && !aligned16(lse)))
+    return MLA_ERR_ALIGNMENT;
+  const mla::PrefillLayout lay = mla::prefill_layout(dims->n_heads, batch, seqlen);
+  if (workspace_bytes < lay.total) return MLA_ERR_WORKSPACE;
+  hipError_t e = mla::launch_prefill(dims->n_heads, batch, seqlen, q, kv_latent, k_pe, wkv_b, workspace, lay, out,
+                                     lse, dims->softmax_scale, stream, stage_events);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_prefill(const mla_dims_t* dims, int32_t batch, int32_t seqlen, const uint16_t* q,
+                         const uint16_t* kv_latent, const uint16_t* k_pe, const uint16_t* wkv_b, void* workspace,
+                         size_t workspace_bytes, uint16_t* out, float* lse, hipStream_t stream) {
+  return mla_prefill_ex(dims, batch, seqlen, q, kv_latent, k_pe, wkv_b, workspace, workspace_bytes, out, lse, stream,
+                        nullptr);
+}
+
+const char* mla_status_string(mla_status_t s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: a required pointer is NULL or a parameter is invalid";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: model widths or head count the kernels are not built for";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: a size is negative or out of range";
+    case MLA_ERR_ALIGNMENT: return "MLA_ERR_ALIGNMENT: a tensor base pointer is not 16-byte aligned";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace smaller than the *_workspace_size query reports";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: a kernel launch failed";
+  }
+  return "unknown mla_status_t";
+}
+
+const char* mla_version(void) { return "0.1.0"; }
+
+}  // extern "C"

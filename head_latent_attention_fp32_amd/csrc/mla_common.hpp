@@ -1,0 +1,81 @@
+// Device-side helpers shared by the MLA kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Model widths the kernels are built for (DeepSeek-V3.2-Exp / Kimi-K2 attention).
+constexpr int kQLora = 1536;   // query latent width
+constexpr int kKvLora = 512;   // cached latent width
+constexpr int kNope = 128;     // per-head content features of q and k
+constexpr int kRope = 64;      // rotary features (32 pairs), shared rotary key
+constexpr int kVDim = 128;     // per-head value features
+constexpr int kQk = kNope + kRope;          // 192 features per query head
+constexpr int kKvRows = kNope + kVDim;      // 256 rows of wkv_b per head
+constexpr int kLat = kKvLora + kRope;       // 576 features of one cached row (latent | rotary key)
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+// D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16). Lane l holds A row l%16 and B column l%16,
+// eight consecutive k of group l/16 each; D column l%16, rows 4*(l/16) .. 4*(l/16)+3.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t u) {
+  return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ float round_bf16(float f) {
+  return bf16_bits_to_f32(f32_to_bf16_bits(f));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16_bits(lo)) | (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ uint4 as_uint4(bf16x8 v) { return __builtin_bit_cast(uint4, v); }
+
+__device__ __forceinline__ uint4 ldg16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ uint16_t u4_elem(const uint4& v, int e) {
+  const uint32_t w = (e < 2) ? v.x : (e < 4) ? v.y : (e < 6) ? v.z : v.w;
+  return static_cast<uint16_t>((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+}
+
+__device__ __forceinline__ bf16x8 bf16x8_from_f32(const float* v) {
+  uint4 u;
+  u.x = pack_bf16x2(v[0], v[1]);
+  u.y = pack_bf16x2(v[2], v[3]);
+  u.z = pack_bf16x2(v[4], v[5]);
+  u.w = pack_bf16x2(v[6], v[7]);
+  return as_bf16x8(u);
+}
+
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48): the k-groups
+// of an MFMA operand / the row groups of its 16x16 result.
+__device__ __forceinline__ float max_over_rows(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+__device__ __forceinline__ float sum_over_rows(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+}  // namespace mla

@@ -1,0 +1,49 @@
+// Host-side internals of libmla: workspace layouts and kernel launchers (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Records stage-boundary event i (if the caller supplied one) on the stream.
+inline void mark(hipEvent_t* ev, int i, hipStream_t stream) {
+  if (ev && ev[i]) (void)hipEventRecord(ev[i], stream);
+}
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+// Split-KV decode. The cached tokens of all sequences, taken back to back, are cut into at most
+// `units` equal runs; one workgroup attends one run (which may span several sequences) and writes
+// one partial result per (run, sequence) pair it touches, in slot run + sequence.
+struct DecodeLayout {
+  int units;            // workgroups launched for the split attention
+  int min_unit_tokens;  // fewer tokens than this per run are not worth a partial
+  size_t plan_off, cum_off, qlat_off, part_o_off, part_l_off, olat_off, total;
+};
+DecodeLayout decode_layout(int n_heads, int batch, int64_t max_seqlen);
+
+struct PrefillLayout {
+  int64_t t_pad;        // sequence length padded to the key tile
+  size_t knope_off, vt_off, total;
+};
+PrefillLayout prefill_layout(int n_heads, int batch, int seqlen);
+
+hipError_t launch_query_path(int n_heads, int64_t n_tokens, const uint16_t* q_latent, const float* gamma,
+                             const uint16_t* wq_b, const float* rope_cs, uint16_t* q_out, float* inv_rms,
+                             float eps, hipStream_t stream, hipEvent_t* ev);
+
+hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16_t* wkv_b,
+                         const uint16_t* kv_cache, const uint16_t* pe_cache, const int64_t* row_offset,
+                         const int32_t* seqlens, int64_t max_seqlen, void* workspace,
+                         const DecodeLayout& lay, uint16_t* out, float* lse, float scale,
+                         hipStream_t stream, hipEvent_t* ev);
+
+hipError_t launch_prefill(int n_heads, int batch, int seqlen, const uint16_t* q, const uint16_t* kv_latent,
+                          const uint16_t* k_pe, const uint16_t* wkv_b, void* workspace,
+                          const PrefillLayout& lay, uint16_t* out, float* lse, float scale,
+                          hipStream_t stream, hipEvent_t* ev);
+
+}  // namespace mla

@@ -1,0 +1,175 @@
+/*
+ * mla.h -- C ABI of libmla: multi-head latent attention (MLA) for AMD Instinct MI355X (gfx950).
+ *
+ * Three entry points follow the hot path of DeepSeek/Kimi-style MLA:
+ *   mla_query_path  RMSNorm of the query latent (fp32, learned gain) -> wq_b up-projection to
+ *                   H heads of 128 content + 64 rotary features -> RoPE on the rotary part.
+ *                   Source: "DeepSeek-V3.2-Exp · Query heads" (equations, in/out shapes, query code
+ *                   excerpt) and "DeepSeek V4.1 · Query RMSNorm" (equation, RMSNorm excerpt).
+ *   mla_decode      absorbed decode of one new token per sequence over the cached latent:
+ *                   q_nope folded through the key half of wkv_b, scores = 512-wide latent dot +
+ *                   64-wide rotary dot, scaled softmax, weighted latent sum projected out through
+ *                   the value half of wkv_b.
+ *                   Source: "DeepSeek-V3.2-Exp · Attention update", mla-decode (MQA decode) excerpt;
+ *                   "Kimi-K2 · value_states" (value reconstruction shapes).
+ *   mla_prefill     non-absorbed causal prefill: latent expanded through wkv_b to per-head k_nope
+ *                   and values, keys joined with the shared rotary key, causal softmax attention.
+ *                   Source: "Kimi-K2 · value_states", mla-prefill excerpt.
+ *
+ * Conventions for every call
+ *   - Tensor pointers are DEVICE pointers. bf16 tensors are passed as uint16_t (raw bf16 bits).
+ *     Every tensor is dense, row-major, with the layout stated at its argument. Every base
+ *     pointer must be 16-byte aligned.
+ *   - The caller owns all memory. The library never allocates or frees device memory and never
+ *     synchronises: a call validates its arguments on the host, enqueues its kernels on `stream`
+ *     and returns. Outputs must not alias inputs. Calls on one stream are ordered; the library
+ *     keeps no mutable state besides a cached device-property record, so different streams may
+ *     call concurrently if their workspaces differ.
+ *   - Errors: host validation runs before any HIP call and returns MLA_ERR_* with nothing
+ *     enqueued: a NULL required pointer -> MLA_ERR_INVALID_ARG; model widths the kernels are not
+ *     built for -> MLA_ERR_UNSUPPORTED; negative or out-of-range sizes -> MLA_ERR_SHAPE;
+ *     misaligned pointers -> MLA_ERR_ALIGNMENT; a workspace smaller than *_workspace_size
+ *     reports -> MLA_ERR_WORKSPACE. A launch failure reports MLA_ERR_HIP. Faults inside kernels
+ *     surface at the caller's next synchronisation. The library never aborts or prints.
+ *   - Sizes of zero (n_tokens = 0, batch = 0, seqlen = 0) are valid and enqueue nothing.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,
+  MLA_ERR_UNSUPPORTED = 2,
+  MLA_ERR_SHAPE = 3,
+  MLA_ERR_ALIGNMENT = 4,
+  MLA_ERR_WORKSPACE = 5,
+  MLA_ERR_HIP = 6
+} mla_status_t;
+
+/* Model widths. The kernels are built for q_lora_rank 1536, kv_lora_rank 512, qk_nope_dim 128,
+ * qk_rope_dim 64, v_head_dim 128 (DeepSeek-V3.2-Exp / Kimi-K2: "DeepSeek-V3.2-Exp · Query heads",
+ * MLA __init__ excerpt; "Kimi-K2 · value_states", mla-init excerpt) and n_heads in {16, 32, 64, 128}
+ * (one GPU's share of the heads). softmax_scale is (qk_nope_dim + qk_rope_dim)^-0.5 = 192^-0.5 in
+ * the pages' configuration; rms_eps is 1e-6 (RMSNorm code default). Both are used as given. */
+typedef struct {
+  int32_t n_heads;
+  int32_t q_lora_rank;
+  int32_t kv_lora_rank;
+  int32_t qk_nope_dim;
+  int32_t qk_rope_dim;
+  int32_t v_head_dim;
+  float softmax_scale;
+  float rms_eps;
+} mla_dims_t;
+
+/* Fill *dims with the pages' widths for n_heads heads, scale 192^-0.5 and eps 1e-6. */
+mla_status_t mla_dims_default(int32_t n_heads, mla_dims_t* dims);
+
+/* Query path ("DeepSeek-V3.2-Exp · Query heads": q^C = c^Q W_UQ, q^pe = c^Q W_QR,
+ * Q^R = RoPE(Q^pe, R), Q = [Q^C; Q^R]; c^Q = RMSNorm(q latent) per "DeepSeek V4.1 · Query RMSNorm").
+ *   q_latent  bf16 [n_tokens, q_lora_rank]           query latent (output of wq_a)
+ *   q_norm_w  fp32 [q_lora_rank]                      RMSNorm gain
+ *   wq_b      bf16 [q_lora_rank, n_heads*192]         input x output; head h owns columns
+ *                                                     h*192 .. h*192+191 (128 content, then 64 rotary)
+ *   rope_cs   fp32 [n_tokens, 32, 2]                  R row of each token: (cos, sin) of each pair
+ *   q_out     bf16 [n_tokens, n_heads, 192]           token-major query heads
+ *   inv_rms   fp32 [n_tokens] or NULL                 1/sqrt(mean(x^2) + eps) of each token
+ * Arithmetic: inv_rms in fp32; y = bf16(gain * x * inv_rms) (rounded before the product, as the
+ * RMSNorm excerpt casts back to the input dtype); q = bf16(y @ wq_b) with fp32 accumulation; rotary
+ * pairs (2i, 2i+1) of each head rotate as (a,b) -> (a cos - b sin, a sin + b cos) from the bf16
+ * product and are rounded to bf16 again. */
+mla_status_t mla_query_path(const mla_dims_t* dims, int64_t n_tokens,
+                            const uint16_t* q_latent, const float* q_norm_w, const uint16_t* wq_b,
+                            const float* rope_cs, uint16_t* q_out, float* inv_rms,
+                            hipStream_t stream);
+
+/* Bytes of device workspace mla_decode needs for `batch` sequences of at most max_seqlen cached
+ * rows each. Host-only; no HIP call. */
+mla_status_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch, int64_t max_seqlen,
+                                       size_t* bytes);
+
+/* Absorbed decode ("DeepSeek-V3.2-Exp · Attention update", mla-decode excerpt), one query token
+ * per sequence, dense over all cached rows of the sequence:
+ *   q_lat[b,h,:] = bf16(q_nope[b,h,:] . W_UK[h])                     (W_UK[h] = wkv_b rows h*256 .. +127)
+ *   s[b,h,t]     = scale * (q_lat[b,h,:] . kv[t,:] + q_pe[b,h,:] . pe[t,:]),   t < L_b
+ *   o_lat[b,h,:] = sum_t softmax_t(s) kv[t,:]                         (fp32 softmax and sums)
+ *   out[b,h,d]   = bf16(sum_c o_lat[b,h,c] W_UV[h,d,c])              (W_UV[h] = wkv_b rows h*256+128 .. +255)
+ *   lse[b,h]     = ln sum_t exp(s[b,h,t])
+ *   q                 bf16 [batch, n_heads, 192]   query heads of the new token (mla_query_path output)
+ *   wkv_b             bf16 [n_heads*256, 512]      output x input
+ *   kv_cache          bf16 rows of 512             cached (normalised) latent
+ *   pe_cache          bf16 rows of 64              cached rotated rotary key
+ *   cache_row_offset  int64 [batch] or NULL        first cache row of sequence b; NULL = b*max_seqlen
+ *   cache_seqlens     int32 [batch]                L_b (device); values are clamped to [0, max_seqlen]
+ *   max_seqlen        host upper bound on L_b (>= 0)
+ *   workspace         >= mla_decode_workspace_size bytes of device memory (contents need not be
+ *                     initialised; overwritten by the call)
+ *   out               bf16 [batch, n_heads, 128]
+ *   lse               fp32 [batch, n_heads] or NULL
+ * A sequence with L_b = 0 gets out = 0 and lse = -inf. Rows beyond L_b are never read. */
+mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, const uint16_t* q, const uint16_t* wkv_b,
+                        const uint16_t* kv_cache, const uint16_t* pe_cache,
+                        const int64_t* cache_row_offset, const int32_t* cache_seqlens, int64_t max_seqlen,
+                        void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
+                        hipStream_t stream);
+
+/* Bytes of device workspace mla_prefill needs (holds the expanded per-head k_nope and values).
+ * Host-only; no HIP call. */
+mla_status_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t seqlen, size_t* bytes);
+
+/* Non-absorbed causal prefill ("Kimi-K2 · value_states", mla-prefill excerpt), start position 0:
+ *   k_nope[b,t,h,:] = bf16(W_UK[h] kv_latent[b,t,:]),  v[b,t,h,:] = bf16(W_UV[h] kv_latent[b,t,:])
+ *   key[b,t,h] = [k_nope[b,t,h,:] ; k_pe[b,t,:]]       (the rotary key is shared by every head)
+ *   s = scale * q . key, keys t' <= t only; fp32 online softmax; out = bf16(sum_t' p v)
+ *   q          bf16 [batch, seqlen, n_heads, 192]   query heads (mla_query_path output)
+ *   kv_latent  bf16 [batch, seqlen, 512]            normalised latent, as it would be cached
+ *   k_pe       bf16 [batch, seqlen, 64]             rotated rotary key, as it would be cached
+ *   wkv_b      bf16 [n_heads*256, 512]
+ *   workspace  >= mla_prefill_workspace_size bytes
+ *   out        bf16 [batch, seqlen, n_heads, 128]
+ *   lse        fp32 [batch, n_heads, seqlen] or NULL */
+mla_status_t mla_prefill(const mla_dims_t* dims, int32_t batch, int32_t seqlen, const uint16_t* q,
+                         const uint16_t* kv_latent, const uint16_t* k_pe, const uint16_t* wkv_b,
+                         void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
+                         hipStream_t stream);
+
+/* Instrumented variants: identical work, plus hipEventRecord of caller-created events on `stream`
+ * at the boundaries of the library's kernel stages, so a caller can time each stage on the stream
+ * it runs on. stage_events is NULL or an array of (number of stages + 1) events, any of which may be
+ * NULL: event i is recorded before stage i and the last after the final stage.
+ *   mla_query_path_ex: 2 stages (row statistics -- empty when fused into the product --, product + RoPE)
+ *   mla_decode_ex:     4 stages (absorb + run plan, split-KV attention, log-sum-exp combine, value projection)
+ *   mla_prefill_ex:    2 stages (latent expansion, causal attention) */
+mla_status_t mla_query_path_ex(const mla_dims_t* dims, int64_t n_tokens,
+                               const uint16_t* q_latent, const float* q_norm_w, const uint16_t* wq_b,
+                               const float* rope_cs, uint16_t* q_out, float* inv_rms,
+                               hipStream_t stream, hipEvent_t* stage_events);
+mla_status_t mla_decode_ex(const mla_dims_t* dims, int32_t batch, const uint16_t* q, const uint16_t* wkv_b,
+                           const uint16_t* kv_cache, const uint16_t* pe_cache,
+                           const int64_t* cache_row_offset, const int32_t* cache_seqlens, int64_t max_seqlen,
+                           void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
+                           hipStream_t stream, hipEvent_t* stage_events);
+mla_status_t mla_prefill_ex(const mla_dims_t* dims, int32_t batch, int32_t seqlen, const uint16_t* q,
+                            const uint16_t* kv_latent, const uint16_t* k_pe, const uint16_t* wkv_b,
+                            void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
+                            hipStream_t stream, hipEvent_t* stage_events);
+
+/* Static description of a status code. */
+const char* mla_status_string(mla_status_t status);
+
+/* Library version, "major.minor.patch". */
+const char* mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

@@ -273,13 +273,15 @@ def combine_segments(parts: Sequence[Tuple[np.ndarray, np.ndarray]]) -> Tuple[np
 
 
 def decode_absorbed(q, wkv_b_bits, kv_bits, pe_bits, scale: float, staged: bool = True,
-                    segments: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+                    segments: Optional[Sequence[int]] = None, round_output: bool = True
+                    ) -> Tuple[np.ndarray, np.ndarray]:
     """[AU] mla-decode for one sequence: absorb q_nope through W_UK, attend the cached latent and
     rotary key, project the latent sum out through W_UV:
       out[h, d] = sum_c o_lat[h, c] W_UV[h, d, c].
     `segments` optionally gives cut points inside [0, L] at which the rows are attended
     separately and merged with combine_segments (the split form; identical by algebra).
-    q [H,192] fp64 values. Returns (out [H,128] -- bf16-valued when staged, lse [H])."""
+    q [H,192] fp64 values. Returns (out [H,128] -- bf16-valued when staged and round_output,
+    lse [H])."""
     q = np.asarray(q, np.float64)
     H = q.shape[0]
     _, uv = wkv_b_heads(bf16_decode(wkv_b_bits), H)
@@ -290,11 +292,11 @@ def decode_absorbed(q, wkv_b_bits, kv_bits, pe_bits, scale: float, staged: bool 
              for a, b in zip(cuts[:-1], cuts[1:])]
     o_lat, lse = parts[0] if len(parts) == 1 else combine_segments(parts)
     out = np.einsum("hc,hdc->hd", o_lat, uv)
-    return _maybe_round(out, staged), lse
+    return _maybe_round(out, staged and round_output), lse
 
 
 def decode_batch(q, wkv_b_bits, kv_cache_bits, pe_cache_bits, row_offset, lengths, scale: float,
-                 staged: bool = True, batch_ids: Optional[Sequence[int]] = None
+                 staged: bool = True, batch_ids: Optional[Sequence[int]] = None, round_output: bool = True
                  ) -> Tuple[np.ndarray, np.ndarray]:
     """Absorbed decode of every (or each listed) sequence b over cache rows
     [row_offset[b], row_offset[b] + lengths[b]). q [B, H, 192]. Returns (out [n, H, 128], lse [n, H])."""
@@ -309,7 +311,7 @@ def decode_batch(q, wkv_b_bits, kv_cache_bits, pe_cache_bits, row_offset, length
             lses.append(np.full(q.shape[1], -np.inf))
             continue
         o, l = decode_absorbed(q[b], wkv_b_bits, kv_cache_bits[r0:r0 + L], pe_cache_bits[r0:r0 + L],
-                               scale, staged)
+                               scale, staged, round_output=round_output)
         outs.append(o)
         lses.append(l)
     return np.stack(outs), np.stack(lses)
@@ -352,10 +354,11 @@ def prefill_head(q_h, k_nope_h, v_h, k_pe, scale: float, rows: Optional[Sequence
 
 
 def prefill_causal(q, kv_latent_bits, k_pe_bits, wkv_b_bits, scale: float, staged: bool = True,
-                   heads: Optional[Sequence[int]] = None, rows: Optional[Sequence[int]] = None
-                   ) -> Tuple[np.ndarray, np.ndarray]:
+                   heads: Optional[Sequence[int]] = None, rows: Optional[Sequence[int]] = None,
+                   round_output: bool = True) -> Tuple[np.ndarray, np.ndarray]:
     """Causal non-absorbed prefill of one sequence. q [T, H, 192] fp64 values.
-    Returns (out [n_rows, n_heads_sel, 128] -- bf16-valued when staged, lse [n_heads_sel, n_rows])."""
+    Returns (out [n_rows, n_heads_sel, 128] -- bf16-valued when staged and round_output,
+    lse [n_heads_sel, n_rows])."""
     q = np.asarray(q, np.float64)
     T, H, _ = q.shape
     heads = list(range(H)) if heads is None else list(heads)
@@ -369,4 +372,38 @@ def prefill_causal(q, kv_latent_bits, k_pe_bits, wkv_b_bits, scale: float, stage
         o, l = prefill_head(q[:need, h, :], k_h[:, 0, :], v_h[:, 0, :], pe, scale, rows)
         out[:, j, :] = o
         lse[j] = l
-    return _maybe_round(out, staged), lse
+    return _maybe_round(out, staged and round_output), lse
+
+
+# ---------------------------------------------------------------------------------------------
+# Magnitude of the score dot products (the scale against which their rounding error is measured)
+# ---------------------------------------------------------------------------------------------
+def decode_score_magnitude(q, wkv_b_bits, kv_bits, pe_bits, scale: float, staged: bool = True) -> np.ndarray:
+    """Per head, max_t of scale * sum_i |q_i k_t,i| over the terms of the absorbed score
+    (|q_lat|.|c_t| + |q_pe|.|pe_t|): the size of the sum whose rounding a score inherits. [H]."""
+    q = np.asarray(q, np.float64)
+    q_lat = absorb_query(q, wkv_b_bits, staged)
+    c = np.abs(bf16_decode(kv_bits))
+    pe = np.abs(bf16_decode(pe_bits))
+    if c.shape[0] == 0:
+        return np.zeros(q.shape[0])
+    return scale * np.max(np.abs(q_lat) @ c.T + np.abs(q[:, NOPE:]) @ pe.T, axis=1)
+
+
+def prefill_score_magnitude(q, kv_latent_bits, k_pe_bits, wkv_b_bits, scale: float, staged: bool = True,
+                            heads: Optional[Sequence[int]] = None, rows: Optional[Sequence[int]] = None
+                            ) -> np.ndarray:
+    """For each listed head and query row t, max_{t' <= t} scale * sum_i |q_t,i k_t',i|. [n_heads_sel, n_rows]."""
+    q = np.asarray(q, np.float64)
+    T, H, _ = q.shape
+    heads = list(range(H)) if heads is None else list(heads)
+    rows = list(range(T)) if rows is None else list(rows)
+    need = max(rows) + 1 if rows else 0
+    pe = np.abs(bf16_decode(k_pe_bits[:need]))
+    mag = np.empty((len(heads), len(rows)))
+    for j, h in enumerate(heads):
+        k_h, _ = expand_latent(kv_latent_bits[:need], wkv_b_bits, H, staged, heads=[h])
+        k = np.concatenate([np.abs(k_h[:, 0, :]), pe], axis=1)
+        for i, t in enumerate(rows):
+            mag[j, i] = scale * np.max(k[: t + 1] @ np.abs(q[t, h]))
+    return mag

@@ -1,0 +1,144 @@
+"""C ABI checks that need no GPU: the library loads, exports every function include/mla.h declares,
+and host-side validation rejects bad arguments before any HIP call (fake pointers are never used)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+binding = pytest.importorskip("head_latent_attention_fp32_amd.binding")
+
+
+def _lib():
+    try:
+        return binding.lib()
+    except ImportError as e:  # pragma: no cover - build() runs before the suite
+        pytest.skip(str(e))
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for f in ("mla_query_path", "mla_decode", "mla_prefill", "mla_decode_workspace_size",
+              "mla_prefill_workspace_size", "mla_status_string"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def _dims(h=128):
+    d = binding.MlaDims()
+    assert _lib().mla_dims_default(h, ctypes.byref(d)) == 0
+    return d
+
+
+def test_dims_default_values():
+    d = _dims(64)
+    assert (d.n_heads, d.q_lora_rank, d.kv_lora_rank, d.qk_nope_dim, d.qk_rope_dim, d.v_head_dim) == (
+        64, 1536, 512, 128, 64, 128)
+    assert abs(d.softmax_scale - 192 ** -0.5) < 1e-8 and abs(d.rms_eps - 1e-6) < 1e-12
+    bad = binding.MlaDims()
+    assert _lib().mla_dims_default(48, ctypes.byref(bad)) == 2
+
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced
+MIS = 0x10002           # misaligned
+
+
+def test_query_path_validation():
+    lib = _lib()
+    d = _dims()
+    q = lib.mla_query_path
+    assert q(None, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 1
+    assert q(ctypes.byref(d), -1, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 3
+    assert q(ctypes.byref(d), 0, None, None, None, None, None, None, None) == 0       # nothing to do
+    assert q(ctypes.byref(d), 4, None, FAKE, FAKE, FAKE, FAKE, None, None) == 1
+    assert q(ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, MIS, None, None) == 4
+    assert q(ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, FAKE, MIS, None) == 4
+    d2 = _dims()
+    d2.q_lora_rank = 1024
+    assert q(ctypes.byref(d2), 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 2
+    d3 = _dims()
+    d3.softmax_scale = float("nan")
+    assert q(ctypes.byref(d3), 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 1
+
+
+def test_decode_validation_and_workspace():
+    lib = _lib()
+    d = _dims()
+    n = ctypes.c_size_t(0)
+    assert lib.mla_decode_workspace_size(ctypes.byref(d), 32, 4096, ctypes.byref(n)) == 0
+    need = n.value
+    assert need > 32 * 128 * 512 * 2 * 2          # at least q_lat and o_lat
+    assert lib.mla_decode_workspace_size(ctypes.byref(d), -1, 4096, ctypes.byref(n)) == 3
+    assert lib.mla_decode_workspace_size(ctypes.byref(d), 1, -5, ctypes.byref(n)) == 3
+    assert lib.mla_decode_workspace_size(ctypes.byref(d), 0, 10, ctypes.byref(n)) == 0 and n.value == 0
+    dec = lib.mla_decode
+    args = lambda **kw: [kw.get(k, v) for k, v in [
+        ("dims", ctypes.byref(d)), ("batch", 32), ("q", FAKE), ("w", FAKE), ("kv", FAKE), ("pe", FAKE),
+        ("off", None), ("lens", FAKE), ("maxl", 4096), ("ws", FAKE), ("wsb", need), ("out", FAKE),
+        ("lse", None), ("stream", None)]]
+    assert dec(*args(batch=0, q=None)) == 0
+    assert dec(*args(batch=-2)) == 3
+    assert dec(*args(maxl=-1)) == 3
+    assert dec(*args(kv=None)) == 1
+    assert dec(*args(lens=None)) == 1
+    assert dec(*args(ws=None)) == 1
+    assert dec(*args(pe=MIS)) == 4
+    assert dec(*args(off=MIS)) == 4
+    assert dec(*args(lse=MIS)) == 4
+    assert dec(*args(wsb=need - 1)) == 5
+    d2 = _dims()
+    d2.n_heads = 96
+    assert dec(*args(dims=ctypes.byref(d2))) == 2
+
+
+def test_prefill_validation_and_workspace():
+    lib = _lib()
+    d = _dims()
+    n = ctypes.c_size_t(0)
+    assert lib.mla_prefill_workspace_size(ctypes.byref(d), 1, 4096, ctypes.byref(n)) == 0
+    assert n.value >= 1 * 128 * 4096 * 256 * 2      # expanded k_nope and values
+    need = n.value
+    pf = lib.mla_prefill
+    assert pf(ctypes.byref(d), 1, 0, None, None, None, None, None, 0, None, None, None) == 0
+    assert pf(ctypes.byref(d), 1, -3, FAKE, FAKE, FAKE, FAKE, FAKE, need, FAKE, None, None) == 3
+    assert pf(ctypes.byref(d), 1, 4096, FAKE, None, FAKE, FAKE, FAKE, need, FAKE, None, None) == 1
+    assert pf(ctypes.byref(d), 1, 4096, FAKE, FAKE, MIS, FAKE, FAKE, need, FAKE, None, None) == 4
+    assert pf(ctypes.byref(d), 1, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, need - 256, FAKE, None, None) == 5
+
+
+def test_status_strings():
+    lib = _lib()
+    for s in range(7):
+        assert lib.mla_status_string(s).decode().startswith(binding.STATUS_NAMES[s])
+    assert lib.mla_version().decode().count(".") == 2
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(binding, "_LIB", None)
+    monkeypatch.setattr(binding, "LIB_PATH", "/nonexistent/libmla.so")
+    with pytest.raises(ImportError):
+        binding.lib()
+
+
+def test_product_code_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "head_latent_attention_fp32_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in src and "from oracle" not in src, f
+                assert "mla_oracle" not in src, f

@@ -1,0 +1,220 @@
+"""GPU parity of libmla (through its C ABI) against the CPU oracle on the same seeded inputs.
+
+Bars (tests/gpu_helpers.py): bf16 outputs within 2e-2 x RMS of each oracle output vector, against
+the oracle's staged value before its final bf16 rounding; inv_rms and lse within 1e-4 relative
+(lse relative to the magnitude of its score dot products); -inf lse exactly where the oracle has it;
+cache rows beyond each length are NaN-poisoned, so reading one fails the check. Full-size workloads are checked on sampled sequences,
+rows and heads that the oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import mla_oracle as O
+from synth import inputs as S
+from tests.gpu_helpers import (assert_bf16_parity, assert_f32_parity, bits_of, dev, dev_bf16, host_bits, say)
+
+binding = pytest.importorskip("head_latent_attention_fp32_amd.binding")
+
+pytestmark = pytest.mark.gpu
+SCALE = 192 ** -0.5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm device")
+    binding.lib()   # raises if the HIP library is not built
+
+
+# ----------------------------------------------------------------------------------- query path
+def _query_case(H, n, seed, case_id, positions=None):
+    rng = np.random.default_rng(seed * 1000 + case_id)
+    x = S.normal_bf16_rows(n, S.Q_LORA, 1.0, (seed, case_id, S.T_Q_LATENT))
+    w = S.query_weights(H, seed, case_id)
+    pos = rng.integers(0, 131073, size=n) if positions is None else np.asarray(positions)
+    return x, w["gamma"], w["wq_b"], S.rope_table(pos)
+
+
+def _run_query(x, g, w, cs, H, with_inv=True):
+    n = x.shape[0]
+    inv = torch.empty(n, dtype=torch.float32, device="cuda") if with_inv else None
+    q, _ = binding.query_path(dev_bf16(x), dev(g), dev_bf16(w), dev(cs), H, inv_rms=inv)
+    torch.cuda.synchronize()
+    return host_bits(q), (inv.cpu().numpy() if with_inv else None)
+
+
+@pytest.mark.parametrize("H,n,with_inv", [(16, 1, True), (64, 1, True), (128, 5, False), (128, 64, True),
+                                          (64, 67, True), (32, 130, False), (128, 200, True)])
+def test_query_path_parity(H, n, with_inv):
+    say(f"query_path H={H} n={n} inv={with_inv}")
+    x, g, w, cs = _query_case(H, n, 0, 200 + H + n)
+    qg, inv = _run_query(x, g, w, cs, H, with_inv)
+    qo, invo = O.query_path(x, g, w, cs, H)
+    assert_bf16_parity(qg, qo, "q_out")
+    if with_inv:
+        assert_f32_parity(inv, invo, "inv_rms")
+
+
+# ----------------------------------------------------------------------------------- decode
+def _run_decode(case, q_bits, d, with_lse=True):
+    B, H = case.batch, case.n_heads
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda") if with_lse else None
+    out, _ = binding.decode(dev_bf16(q_bits), dev_bf16(d["wkv_b"]), dev_bf16(d["kv_cache"]),
+                            dev_bf16(d["pe_cache"]), dev(d["lengths"]), int(case.max_seqlen),
+                            cache_row_offset=None if case.layout == "padded" else dev(d["row_offset"]),
+                            lse=lse)
+    torch.cuda.synchronize()
+    return host_bits(out), (lse.cpu().numpy() if with_lse else None)
+
+
+def _decode_magnitude(q_vals, d, lens, ids):
+    mags = []
+    for b in ids:
+        r0, L = int(d["row_offset"][b]), int(lens[b])
+        mags.append(O.decode_score_magnitude(q_vals[b], d["wkv_b"], d["kv_cache"][r0:r0 + L],
+                                             d["pe_cache"][r0:r0 + L], SCALE))
+    return np.stack(mags)
+
+
+def _check_decode(case, q_bits, d, out_bits, lse, batch_ids=None):
+    lens = np.clip(d["lengths"].astype(np.int64), 0, int(case.max_seqlen))
+    ids = list(range(case.batch)) if batch_ids is None else list(batch_ids)
+    qv = O.bf16_decode(q_bits)
+    oo, lo = O.decode_batch(qv, d["wkv_b"], d["kv_cache"], d["pe_cache"], d["row_offset"], lens,
+                            SCALE, staged=True, batch_ids=ids, round_output=False)
+    assert_bf16_parity(out_bits[ids], oo, "out")
+    if lse is not None:
+        assert_f32_parity(lse[ids], lo, "lse", magnitude=_decode_magnitude(qv, d, lens, ids))
+
+
+DECODE_SMALL = [
+    (16, [1], "padded"), (64, [31], "padded"), (64, [32], "padded"), (64, [33], "padded"),
+    (128, [1000], "padded"), (32, [0, 5, 300], "padded"), (128, [257, 1, 0, 64, 512], "padded"),
+    (64, [3, 700, 45, 0, 1, 96], "packed"), (128, [2049, 17], "packed"), (16, [0, 0], "padded"),
+]
+
+
+@pytest.mark.parametrize("H,lens,layout", DECODE_SMALL)
+def test_decode_parity_small(H, lens, layout):
+    say(f"decode H={H} lens={lens} layout={layout}")
+    case = S.DecodeCase("t", 300 + H + len(lens), H, np.array(lens, np.int32), layout=layout,
+                        max_seqlen=max(max(lens), 1))
+    d = S.decode_inputs(case, seed=1, with_q_latent=False)
+    q = S.decode_query(case, seed=1)
+    out, lse = _run_decode(case, q, d)
+    _check_decode(case, q, d, out, lse)
+
+
+def test_decode_lengths_are_clamped():
+    say("decode clamped lengths")
+    case = S.DecodeCase("t", 330, 64, np.array([40, 40, 40], np.int32), max_seqlen=40)
+    d = S.decode_inputs(case, seed=2, with_q_latent=False)
+    d["lengths"] = np.array([-7, 41000, 13], np.int32)     # clamped to [0, max_seqlen]
+    q = S.decode_query(case, seed=2)
+    out, lse = _run_decode(case, q, d)
+    _check_decode(case, q, d, out, lse)
+
+
+def test_decode_is_deterministic():
+    case = S.DecodeCase("t", 331, 128, np.array([3000, 5, 1200], np.int32), layout="packed")
+    d = S.decode_inputs(case, seed=3, with_q_latent=False)
+    q = S.decode_query(case, seed=3)
+    a, la = _run_decode(case, q, d)
+    b, lb = _run_decode(case, q, d)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def _decode_step(cfg, sample):
+    case = S.workload(cfg)
+    say(f"decode step {case.name}: query path + decode on the GPU, oracle on sequences {sample}")
+    d = S.decode_inputs(case, seed=0)
+    H = case.n_heads
+    inv = torch.empty(case.batch, dtype=torch.float32, device="cuda")
+    q, _ = binding.query_path(dev_bf16(d["q_latent"]), dev(d["gamma"]), dev_bf16(d["wq_b"]), dev(d["rope_cs"]), H,
+                              inv_rms=inv)
+    lse = torch.empty((case.batch, H), dtype=torch.float32, device="cuda")
+    out, _ = binding.decode(q, dev_bf16(d["wkv_b"]), dev_bf16(d["kv_cache"]), dev_bf16(d["pe_cache"]),
+                            dev(d["lengths"]), int(case.max_seqlen),
+                            cache_row_offset=None if case.layout == "padded" else dev(d["row_offset"]), lse=lse)
+    torch.cuda.synchronize()
+    qg = host_bits(q)
+    qo, invo = O.query_path(d["q_latent"][sample], d["gamma"], d["wq_b"], d["rope_cs"][sample], H)
+    assert_bf16_parity(qg[sample], qo, "q_out")
+    assert_f32_parity(inv.cpu().numpy()[sample], invo, "inv_rms")
+    # decode checked on the oracle's own query (no GPU value feeds the oracle)
+    qfull = _scatter(qo, sample, case.batch)
+    oo, lo = O.decode_batch(qfull, d["wkv_b"], d["kv_cache"], d["pe_cache"], d["row_offset"], d["lengths"], SCALE,
+                            staged=True, batch_ids=sample, round_output=False)
+    assert_bf16_parity(host_bits(out)[sample], oo, "out")
+    assert_f32_parity(lse.cpu().numpy()[sample], lo, "lse",
+                      magnitude=_decode_magnitude(qfull, d, d["lengths"], sample))
+
+
+def _scatter(vals, ids, n):
+    full = np.zeros((n,) + vals.shape[1:])
+    full[ids] = vals
+    return full
+
+
+def test_decode_step_config0():
+    _decode_step(0, [0])
+
+
+@pytest.mark.slow
+def test_decode_step_config1():
+    _decode_step(1, [0, 13, 31])
+
+
+@pytest.mark.slow
+def test_decode_step_config3_ragged():
+    lens = S.workload(3).lengths
+    _decode_step(3, sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 64, 127}))
+
+
+@pytest.mark.slow
+def test_decode_step_config4_long():
+    _decode_step(4, [0, 7])
+
+
+# ----------------------------------------------------------------------------------- prefill
+def _run_prefill(q_bits, lat, kpe, w, H):
+    B, T = lat.shape[:2]
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    out, _ = binding.prefill(dev_bf16(q_bits), dev_bf16(lat), dev_bf16(kpe), dev_bf16(w), lse=lse)
+    torch.cuda.synchronize()
+    return host_bits(out), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("H,B,T", [(16, 1, 1), (16, 2, 5), (64, 1, 64), (32, 1, 65), (128, 1, 130),
+                                   (64, 3, 200), (16, 1, 257)])
+def test_prefill_parity_small(H, B, T):
+    say(f"prefill H={H} B={B} T={T}")
+    case = S.PrefillCase("t", 400 + H + T + B, H, B, T)
+    d = S.prefill_inputs(case, seed=4, with_q_latent=False)
+    q = S.prefill_query(case, seed=4)
+    out, lse = _run_prefill(q, d["kv_latent"], d["k_pe"], d["wkv_b"], H)
+    for b in range(B):
+        qv = O.bf16_decode(q[b])
+        oo, lo = O.prefill_causal(qv, d["kv_latent"][b], d["k_pe"][b], d["wkv_b"], SCALE, round_output=False)
+        assert_bf16_parity(out[b], oo, f"out[b={b}]")
+        mag = O.prefill_score_magnitude(qv, d["kv_latent"][b], d["k_pe"][b], d["wkv_b"], SCALE)
+        assert_f32_parity(lse[b], lo, f"lse[b={b}]", magnitude=mag)
+
+
+@pytest.mark.slow
+def test_prefill_config2_sampled():
+    case = S.workload(2)
+    say(f"prefill {case.name}: query path + prefill on the GPU, oracle on sampled rows and heads")
+    d = S.prefill_inputs(case, seed=0)
+    H, T = case.n_heads, case.seqlen
+    q, _ = binding.query_path(dev_bf16(d["q_latent"][0]), dev(d["gamma"]), dev_bf16(d["wq_b"]), dev(d["rope_cs"]), H)
+    out, lse = _run_prefill(host_bits(q)[None], d["kv_latent"], d["k_pe"], d["wkv_b"], H)
+    rows = [0, 1, 63, 64, 65, 1000, 2047, 4094, 4095]
+    heads = [0, 77, 127]
+    qo, _ = O.query_path(d["q_latent"][0][: max(rows) + 1], d["gamma"], d["wq_b"], d["rope_cs"][: max(rows) + 1], H)
+    assert_bf16_parity(host_bits(q)[rows], qo[rows], "q_out rows")
+    oo, lo = O.prefill_causal(qo, d["kv_latent"][0], d["k_pe"][0], d["wkv_b"], SCALE, heads=heads, rows=rows,
+                              round_output=False)
+    assert_bf16_parity(out[0][rows][:, heads], oo, "out")
+    mag = O.prefill_score_magnitude(qo, d["kv_latent"][0], d["k_pe"][0], d["wkv_b"], SCALE, heads=heads, rows=rows)
+    assert_f32_parity(lse[0][heads][:, rows], lo, "lse", magnitude=mag)
