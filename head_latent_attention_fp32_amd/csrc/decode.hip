@@ -23,9 +23,6 @@ namespace mla {
 namespace {
 
 constexpr int kTileTok = 32;                     // cached rows per LDS tile
-constexpr int kTileStride = kLat + 8;            // padded LDS row (bf16): conflict-free 16-B reads
-constexpr int kChunksPerRow = kLat / 8;          // 72 sixteen-byte chunks per cached row
-constexpr int kTileChunks = kTileTok * kChunksPerRow;
 
 struct Plan {
   int64_t total_tokens;   // N = sum of clamped lengths
@@ -121,32 +118,125 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// 2. Split-KV attention over runs. NW waves, wave w owns heads 16w .. 16w+15 (H = 16 NW).
+// 2. Split-KV attention over runs.
+//
+//    Block = NW waves, H = 16 NW heads. Cached rows stream through an NSTAGE-deep ring of 32-row
+//    LDS tiles filled by 16-byte direct-to-LDS buffer loads (the descriptor's range check
+//    zero-fills rows past the end of the sequence), so every row is read from HBM once.
+//    Per tile:
+//      scores:  wave w holds the query of heads 16w .. 16w+15 (absorbed latent and rotary part,
+//               576 features) in VGPRs and computes S^T[t][h] = sum_k tile[t][k] q[h][k] on MFMA
+//               (A operand: ds_read_b128 of tile rows), the per-head maximum and P = 2^(s - m),
+//               which it writes to a small LDS buffer;
+//      values:  wave w owns latent columns [512 w / NW, 512 (w+1) / NW) of every head and adds
+//               O^T[c][h] += sum_t tile[t][c] P^T[t][h] (A operand: ds_read_b64_tr_b16, the
+//               transposing LDS read, of tile columns; B operand: ds_read_b128 of P).
+//    So a wave holds 72 registers of query and 128 of accumulators whatever H is.
+//    P^T comes out of the S^T accumulators with lane l holding tokens 4(l/16)+{0..3} and
+//    16+4(l/16)+{0..3} of head l%16 -- its k-group of the P.V product -- and is stored per head
+//    in that order; V^T is read in the same token order.
+//    LDS tile: latent part [32 rows][1024 B] whose 16-byte chunk c of row r sits at c ^ fk(r),
+//    fk(r) = 2(r&7) + ((r>>3)&1); rotary part [32 rows][128 B] with chunk c at c ^ ((r>>1)&7);
+//    P rows of 80 B. Then 16 rows read at one chunk, and 8 consecutive rows read at two adjacent
+//    chunks, touch 16 distinct 16-byte bank groups.
+//    Softmax: per head a reference m (log2 units, scale folded in) that moves only when a tile's
+//    maximum exceeds it by more than 8 -- then every wave rescales its accumulators and l by the
+//    factor each head publishes in LDS -- so p = 2^(s - m) <= 2^8.
 // ---------------------------------------------------------------------------------------------
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void attend_kernel(
+constexpr int kKvBytes = kTileTok * kKvLora * 2;           // 32768
+constexpr int kPeBytes = kTileTok * kRope * 2;             // 4096
+constexpr int kTileBytes = kKvBytes + kPeBytes;            // 36864
+constexpr int kTileLoads = kTileBytes / 1024;              // 36 loads of 64 lanes x 16 B
+constexpr int kPStride = kTileTok * 2 + 16;                // bytes per head row of P
+constexpr uint32_t kRsrcWord3 = 0x00020000u;               // raw buffer, 32-bit data format
+
+__device__ __forceinline__ int fk(int row) { return 2 * (row & 7) + ((row >> 3) & 1); }
+__device__ __forceinline__ int fp(int row) { return (row >> 1) & 7; }
+
+// Workgroup barrier that orders LDS accesses only. __syncthreads() also orders global memory,
+// which waits for every vector-memory load in flight -- here, the next tiles' loads.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  // s_waitcnt vmcnt(N); expcnt and lgkmcnt left unconstrained
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until at most `tiles_after` tiles of loads (of `L` loads each) are still in flight.
+template <int L>
+__device__ __forceinline__ void wait_tiles(int tiles_after) {
+  if (tiles_after >= 3) wait_vm<3 * L>();
+  else if (tiles_after == 2) wait_vm<2 * L>();
+  else if (tiles_after == 1) wait_vm<L>();
+  else wait_vm<0>();
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+
+// Raw buffer descriptor over [base, base + bytes) built from wave-uniform values (so that it
+// lives in SGPRs); loads beyond the range return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
+}
+
+// 16-byte direct-to-LDS buffer load: lane l's 16 bytes at rsrc + voff land at LDS byte offset
+// dst + 16 l. Issued from an asm block: the compiler cannot tell which ring stage such a load
+// writes and would otherwise wait for every load in flight before any LDS read. Completion is
+// tracked with explicit vmcnt waits and barriers. The block writes no registers.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, const uint8_t* dst, uint32_t voff) {
+  const uint32_t d = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)dst));
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "{m0}"(d)
+               : "memory");
+}
+template <int NW, int NSTAGE>
+__global__ __launch_bounds__(NW * 64, 1) void attend_kernel(
     const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const uint16_t* __restrict__ pe, const int64_t* __restrict__ row_offset, int64_t max_seqlen,
-    const Plan* __restrict__ plan, const int64_t* __restrict__ cum, int batch, float scale_log2,
+    const Plan* __restrict__ plan, const int64_t* __restrict__ cum, int batch, int n_heads, float scale_log2,
     float* __restrict__ part_o, float* __restrict__ part_l) {
+  // A block attends H = 16 NW heads: head group hg covers heads [H hg, H hg + H); slots past
+  // n_heads (fewer heads than H) run on a zero query and are never stored. The blocks of the
+  // head groups of one run share blockIdx mod 8 -- the same XCD and its L2 -- and are dispatched
+  // next to each other, so the tiles one of them pulls from HBM are L2 hits for the others.
   constexpr int H = 16 * NW;
-  constexpr int NT = NW * 64;
-  constexpr int CH = (kTileChunks + NT - 1) / NT;
+  constexpr int CB = 32 / NW;                              // 16-column blocks of the latent per wave
+  constexpr int LMAX = (kTileLoads + NW - 1) / NW;         // loads per wave per tile (first waves)
+  constexpr int LMIN = kTileLoads / NW;
+  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "pipeline depth");
 
   const int64_t N = plan->total_tokens;
   const int64_t G = plan->runs;
-  const int64_t g = blockIdx.x;
+  const int n_groups = (n_heads + H - 1) / H;
+  const int hg = (blockIdx.x >> 3) % n_groups;
+  const int64_t g = (blockIdx.x & 7) + 8 * (blockIdx.x / (8 * n_groups));
   if (g >= G) return;
+  const int head0 = hg * H;
 
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kTileTok * kTileStride];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[H * kPStride];
+  __shared__ float alpha_s[H];
+  __shared__ int flag_s[NW];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: lets wave-derived values live in SGPRs
   const int r = lane & 15, grp = lane >> 4;
-  const int head = wave * 16 + r;
+  const int my_loads = (kTileLoads - wave + NW - 1) / NW;  // loads j = wave + NW k of each tile
+  const int c_wave = wave * CB;                            // first 16-column block of this wave
 
   int64_t start = run_start(g, N, G);
   const int64_t end = run_start(g + 1, N, G);
-  // First sequence whose rows reach past `start`.
   int lo = 0, hi = batch - 1;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
@@ -157,120 +247,239 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
   while (start < end) {
     const int64_t seq0 = cum[b];
     const int64_t seg_end = min(end, cum[b + 1]);
-    const int64_t t0 = start - seq0, t1 = seg_end - seq0;
+    const int t0 = static_cast<int>(start - seq0), t1 = static_cast<int>(seg_end - seq0);
     const int64_t base_row = row_offset ? row_offset[b] : static_cast<int64_t>(b) * max_seqlen;
+    const int n_tiles = (t1 - t0 + kTileTok - 1) / kTileTok;
+    // Descriptors over rows [0, t1) of this sequence: loads of later rows return zeros.
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kv + base_row * kKvLora, t1 * (kKvLora * 2));
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(pe + base_row * kRope, t1 * (kRope * 2));
 
-    // Query of (b, head) as MFMA B operand: 16 k-steps of the absorbed latent, 2 of the rotary part.
     bf16x8 qf[18];
     {
-      const uint16_t* ql = q_lat + (static_cast<int64_t>(b) * H + head) * kKvLora + grp * 8;
-      const uint16_t* qp = q + (static_cast<int64_t>(b) * H + head) * kQk + kNope + grp * 8;
+      const int head = head0 + wave * 16 + r;
+      const bool real = head < n_heads;
+      const int hq = real ? head : 0;
+      const uint16_t* ql = q_lat + (static_cast<int64_t>(b) * n_heads + hq) * kKvLora + grp * 8;
+      const uint16_t* qp = q + (static_cast<int64_t>(b) * n_heads + hq) * kQk + kNope + grp * 8;
+      const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) qf[ks] = as_bf16x8(ldg16(ql + ks * 32));
+      for (int ks = 0; ks < 16; ++ks) qf[ks] = as_bf16x8(real ? ldg16(ql + ks * 32) : z);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) qf[16 + ks] = as_bf16x8(ldg16(qp + ks * 32));
+      for (int ks = 0; ks < 2; ++ks) qf[16 + ks] = as_bf16x8(real ? ldg16(qp + ks * 32) : z);
     }
 
-    float m = -INFINITY, lsum = 0.f;
-    f32x4 o[32];
+    // Load j of a tile fills latent row j (j < 32; lane = physical chunk) or rotary rows
+    // 8 (j - 32) .. +7 (lane = 8 rows x 8 physical chunks); this wave issues j = wave + NW k.
+    auto issue = [&](int tile) {
+      const int tt0 = t0 + tile * kTileTok;
+      uint8_t* dst = lds + (tile % NSTAGE) * kTileBytes;
 #pragma unroll
-    for (int cb = 0; cb < 32; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    uint4 pf[CH];
-    auto fetch = [&](int64_t tt0) {
-#pragma unroll
-      for (int k = 0; k < CH; ++k) {
-        const int i = tid + k * NT;
-        if (i < kTileChunks) {
-          const int row = i / kChunksPerRow, ch = i - row * kChunksPerRow;
-          const int64_t t = min(tt0 + row, t1 - 1);   // tail rows re-read the last valid row
-          const int64_t cr = base_row + t;
-          pf[k] = ch < 64 ? ldg16(kv + cr * kKvLora + ch * 8) : ldg16(pe + cr * kRope + (ch - 64) * 8);
-        }
-      }
-    };
-    auto stash = [&]() {
-#pragma unroll
-      for (int k = 0; k < CH; ++k) {
-        const int i = tid + k * NT;
-        if (i < kTileChunks) {
-          const int row = i / kChunksPerRow, ch = i - row * kChunksPerRow;
-          *reinterpret_cast<uint4*>(&tile[row * kTileStride + ch * 8]) = pf[k];
+      for (int k = 0; k < LMAX; ++k) {
+        const int j = wave + NW * k;
+        if (j < kTileLoads) {
+          if (j < kTileTok) {
+            const uint32_t voff = static_cast<uint32_t>(tt0 + j) * (kKvLora * 2) + ((lane ^ fk(j)) << 4);
+            dma16(rk, dst + j * 1024, voff);
+          } else {
+            const int row = 8 * (j - kTileTok) + (lane >> 3);
+            const uint32_t voff =
+                static_cast<uint32_t>(tt0 + row) * (kRope * 2) + (((lane & 7) ^ fp(row)) << 4);
+            dma16(rp, dst + kKvBytes + (j - kTileTok) * 1024, voff);
+          }
         }
       }
     };
 
-    const int n_tiles = static_cast<int>((t1 - t0 + kTileTok - 1) / kTileTok);
-    fetch(t0);
-    for (int it = 0; it < n_tiles; ++it) {
-      __syncthreads();
-      stash();
-      __syncthreads();
-      const int64_t tt0 = t0 + static_cast<int64_t>(it) * kTileTok;
-      if (it + 1 < n_tiles) fetch(tt0 + kTileTok);
+    float m_ref = -INFINITY, lsum = 0.f;       // of head 16 wave + r
+    f32x4 o[CB][NW];                           // O^T[16 (c_wave + cb) + 4 grp + j][16 hb + r]
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int hb = 0; hb < NW; ++hb) o[cb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-      // S^T[token][head] for the 32 tokens of the tile: two 16-token blocks.
-      f32x4 s[2];
+    int issued = 0;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const uint16_t* arow = &tile[(mb * 16 + r) * kTileStride + grp * 8];
+    for (int st = 0; st < NSTAGE - 1; ++st)
+      if (issued < n_tiles) issue(issued++);
+
+    f32x4 s[2];
+    float mx = 0.f;
+    // Wait for tile it, make it visible, start the next loads, S^T and its masked maximum.
+    auto scores = [&](int it) {
+      const int after = issued - 1 - it;
+      if (my_loads == LMAX) wait_tiles<LMAX>(after); else wait_tiles<LMIN>(after);
+      lds_barrier();
+      if (issued < n_tiles) issue(issued++);
+      const uint8_t* tile = lds + (it % NSTAGE) * kTileBytes;
+      // Per-lane operand offsets, recomputed per tile from an opaque copy of the lane id (cheaper
+      // than keeping them live through the loop). S^T latent k-steps: row tb*16 + r, logical chunk
+      // 4 ks + grp; rotary k-steps 16, 17: row tb*16 + r, logical chunk 4 (ks-16) + grp.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int lr = ln & 15, lg = ln >> 4;
+      const int sf = fk(lr);
+      const int s_lane = lr * 1024 + ((lg ^ sf) & 3) * 16;
+      const int s_flip = sf >> 2;
+      const int p_off0 = kKvBytes + lr * 128 + ((lg ^ fp(lr)) * 16);
+      const int p_off1 = kKvBytes + lr * 128 + (((4 + lg) ^ fp(lr)) * 16);
+      s[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      auto rd = [&](int tb, int ks) {
+        const uint8_t* p = ks < 16 ? tile + tb * 16 * 1024 + s_lane + 64 * ((ks & ~3) + ((ks & 3) ^ s_flip))
+                                   : tile + tb * 16 * 128 + (ks == 16 ? p_off0 : p_off1);
+        return *reinterpret_cast<const bf16x8*>(p);
+      };
+      // Operand reads run kAhead k-steps ahead of the MFMAs (both 16-token halves per step).
+      constexpr int kAhead = 4;
+      bf16x8 fa[kAhead][2];
 #pragma unroll
-        for (int ks = 0; ks < 18; ++ks)
-          acc = mfma16x16x32(*reinterpret_cast<const bf16x8*>(arow + ks * 32), qf[ks], acc);
-        s[mb] = acc;
+      for (int ks = 0; ks < kAhead; ++ks) {
+        fa[ks][0] = rd(0, ks);
+        fa[ks][1] = rd(1, ks);
       }
-      const int64_t valid = t1 - tt0;   // tokens of this tile that belong to the run
-      float mx = -INFINITY;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int ks = 0; ks < 18; ++ks) {
+        const bf16x8 a0 = fa[ks % kAhead][0], a1 = fa[ks % kAhead][1];
+        if (ks + kAhead < 18) {
+          fa[ks % kAhead][0] = rd(0, ks + kAhead);
+          fa[ks % kAhead][1] = rd(1, ks + kAhead);
+        }
+        s[0] = mfma16x16x32(a0, qf[ks], s[0]);
+        s[1] = mfma16x16x32(a1, qf[ks], s[1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int valid = t1 - (t0 + it * kTileTok);
+      float m = -INFINITY;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (mb * 16 + grp * 4 + j >= valid) s[mb][j] = -INFINITY;
-          mx = fmaxf(mx, s[mb][j]);
+          if (tb * 16 + grp * 4 + j >= valid) s[tb][j] = -INFINITY;
+          m = fmaxf(m, s[tb][j]);
         }
-      mx = max_over_rows(mx);
-      const float m_new = fmaxf(m, mx);
-      const float alpha = exp2f((m - m_new) * scale_log2);
-      const float mref = m_new * scale_log2;
+      mx = max_over_rows(m) * scale_log2;
+    };
+
+    // P = 2^(s - m) into l and the LDS buffer (tokens in k-group order), then the barrier that
+    // publishes P, the rescale factors and the flags.
+    auto publish = [&]() {
       float p[8];
-      float ps = 0.f;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          p[mb * 4 + j] = exp2f(s[mb][j] * scale_log2 - mref);
-          ps += p[mb * 4 + j];
+          p[tb * 4 + j] = exp2f(s[tb][j] * scale_log2 - m_ref);
+          lsum += p[tb * 4 + j];
         }
-      lsum = lsum * alpha + ps;
-      m = m_new;
-      const bf16x8 pb = bf16x8_from_f32(p);
+      *reinterpret_cast<bf16x8*>(pbuf + (wave * 16 + r) * kPStride + grp * 16) = bf16x8_from_f32(p);
+      lds_barrier();
+    };
 
-      // O^T[c][head] += kv^T[c][token] . P^T[token][head]; k index e of lane group grp is token
-      // (e/4)*16 + 4*grp + e%4, matching where P^T's values sit.
+    // O^T += V^T P^T for this wave's latent columns and all heads.
+    auto values = [&](int it) {
+      const uint8_t* tile = lds + (it % NSTAGE) * kTileBytes;
+      // V^T: source row 4 grp + (r>>2) (+16), logical chunk 2 cb + ((r&3)>>1), byte (r&1)*8.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int lr = ln & 15, lg = ln >> 4;
+      const int vrow = 4 * lg + (lr >> 2);
+      const int vf = fk(vrow);
+      const int v_lane = vrow * 1024 + ((((lr & 3) >> 1) ^ (vf & 1)) * 16) + (lr & 1) * 8;
+      const int v_flip = vf >> 1;
+      auto rdv = [&](int cb) {
+        const int c = c_wave + cb;
+        const uint8_t* v0 = tile + v_lane + 32 * ((c & ~7) + ((c & 7) ^ v_flip));
+        const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(v0));
+        const i16x4 hi4 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(v0 + 16 * 1024));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      auto rdp = [&](int hb) { return *reinterpret_cast<const bf16x8*>(pbuf + (hb * 16 + r) * kPStride + grp * 16); };
+      if constexpr (CB <= 8) {
+        // the wave's V^T fragments and all P fragments are read up front, each once
+        bf16x8 vf[CB], pf[NW];
 #pragma unroll
-      for (int cb = 0; cb < 32; ++cb) {
-        const uint16_t* col = &tile[(grp * 4) * kTileStride + cb * 16 + r];
-        uint4 u;
-        u.x = static_cast<uint32_t>(col[0]) | (static_cast<uint32_t>(col[kTileStride]) << 16);
-        u.y = static_cast<uint32_t>(col[2 * kTileStride]) | (static_cast<uint32_t>(col[3 * kTileStride]) << 16);
-        u.z = static_cast<uint32_t>(col[16 * kTileStride]) | (static_cast<uint32_t>(col[17 * kTileStride]) << 16);
-        u.w = static_cast<uint32_t>(col[18 * kTileStride]) | (static_cast<uint32_t>(col[19 * kTileStride]) << 16);
-        o[cb] = o[cb] * alpha;
-        o[cb] = mfma16x16x32(as_bf16x8(u), pb, o[cb]);
+        for (int cb = 0; cb < CB; ++cb) vf[cb] = rdv(cb);
+#pragma unroll
+        for (int hb = 0; hb < NW; ++hb) pf[hb] = rdp(hb);
+#pragma unroll
+        for (int hb = 0; hb < NW; ++hb) {
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) o[cb][hb] = mfma16x16x32(vf[cb], pf[hb], o[cb][hb]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const bf16x8 a = rdv(cb);
+#pragma unroll
+          for (int hb = 0; hb < NW; ++hb) o[cb][hb] = mfma16x16x32(a, rdp(hb), o[cb][hb]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+
+    // The first tile sets the reference (O and l are still zero).
+    scores(0);
+    m_ref = mx;
+    publish();
+    values(0);
+    int it = 1;
+    while (it < n_tiles) {
+      // Tiles whose maximum stays within 2^8 of the reference of every head: the accumulators are
+      // only ever updated by MFMAs in this loop.
+      bool rescale = false;
+      for (; it < n_tiles; ++it) {
+        scores(it);
+        const bool up = __any(mx > m_ref + 8.f) != 0;
+        if (up) {
+          const float m_new = fmaxf(m_ref, mx);
+          const float alpha = exp2f(m_ref - m_new);
+          m_ref = m_new;
+          lsum *= alpha;
+          if (grp == 0) alpha_s[wave * 16 + r] = alpha;
+        }
+        if (lane == 0) flag_s[wave] = up ? 1 : 0;
+        publish();
+#pragma unroll
+        for (int w = 0; w < NW; ++w) rescale |= flag_s[w] != 0;
+        if (rescale) break;
+        values(it);
+      }
+      if (!rescale) break;
+      // Some head moved its reference: scale every accumulator by its head's factor.
+#pragma unroll
+      for (int hb = 0; hb < NW; ++hb) {
+        const bool moved = flag_s[hb] != 0;
+        const float a = moved ? alpha_s[hb * 16 + r] : 1.f;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) o[cb][hb] *= a;
+      }
+      values(it);
+      ++it;
+    }
+
+    // Final normalisation: every wave needs l of all heads; publish them through alpha_s.
+    const float ltot = sum_over_rows(lsum);
+    lds_barrier();
+    if (grp == 0) alpha_s[wave * 16 + r] = ltot;
+    lds_barrier();
+    const int64_t slot = g + b;
+#pragma unroll
+    for (int hb = 0; hb < NW; ++hb) {
+      if (head0 + hb * 16 < n_heads) {
+        const float inv = 1.f / alpha_s[hb * 16 + r];
+        float* po = part_o + (slot * n_heads + head0 + hb * 16 + r) * kKvLora + c_wave * 16 + grp * 4;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const f32x4 v = o[cb][hb] * inv;
+          *reinterpret_cast<float4*>(po + cb * 16) = make_float4(v[0], v[1], v[2], v[3]);
+        }
       }
     }
-
-    const float ltot = sum_over_rows(lsum);
-    const float inv = 1.f / ltot;
-    const int64_t slot = g + b;
-    float* po = part_o + (slot * H + head) * kKvLora + grp * 4;
-#pragma unroll
-    for (int cb = 0; cb < 32; ++cb) {
-      float4 v = make_float4(o[cb][0] * inv, o[cb][1] * inv, o[cb][2] * inv, o[cb][3] * inv);
-      *reinterpret_cast<float4*>(po + cb * 16) = v;
-    }
-    if (grp == 0) part_l[slot * H + head] = (m * scale_log2 + __log2f(ltot)) * kLn2;
+    if (grp == 0 && head0 + wave * 16 < n_heads)
+      part_l[slot * n_heads + head0 + wave * 16 + r] = (m_ref + __log2f(ltot)) * kLn2;
+    lds_barrier();   // alpha_s / pbuf / ring are reused by the next segment
 
     start = seg_end;
     ++b;
@@ -367,7 +576,9 @@ DecodeLayout decode_layout(int n_heads, int batch, int64_t max_seqlen) {
   L.min_unit_tokens = 256;
   const int64_t upper = static_cast<int64_t>(batch) * max_seqlen;
   int64_t units = (upper + L.min_unit_tokens - 1) / L.min_unit_tokens;
-  units = units < 1 ? 1 : (units > 256 ? 256 : units);
+  // one block per compute unit: 256 CUs, shared by the head groups of a run
+  const int64_t max_units = 256 / ((n_heads + 63) / 64);
+  units = units < 1 ? 1 : (units > max_units ? max_units : units);
   L.units = static_cast<int>(units);
   const size_t B = static_cast<size_t>(batch), H = static_cast<size_t>(n_heads);
   const size_t slots = static_cast<size_t>(L.units) + B;
@@ -400,16 +611,11 @@ hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16
   absorb_plan_kernel<<<dim3(n_heads, kKvLora / 64), 256, 0, stream>>>(
       q, wkv_b, batch, n_heads, q_lat, seqlens, max_seqlen, lay.units, lay.min_unit_tokens, plan, cum);
   mark(ev, 1, stream);
-  switch (n_heads) {
-    case 16: attend_kernel<1><<<lay.units, 64, 0, stream>>>(q_lat, q, kv_cache, pe_cache, row_offset, max_seqlen,
-                                                            plan, cum, batch, scale_log2, part_o, part_l); break;
-    case 32: attend_kernel<2><<<lay.units, 128, 0, stream>>>(q_lat, q, kv_cache, pe_cache, row_offset, max_seqlen,
-                                                             plan, cum, batch, scale_log2, part_o, part_l); break;
-    case 64: attend_kernel<4><<<lay.units, 256, 0, stream>>>(q_lat, q, kv_cache, pe_cache, row_offset, max_seqlen,
-                                                             plan, cum, batch, scale_log2, part_o, part_l); break;
-    case 128: attend_kernel<8><<<lay.units, 512, 0, stream>>>(q_lat, q, kv_cache, pe_cache, row_offset, max_seqlen,
-                                                              plan, cum, batch, scale_log2, part_o, part_l); break;
-    default: return hipErrorInvalidValue;
+  {
+    const int n_groups = (n_heads + 63) / 64;
+    const int blocks = (lay.units + 7) / 8 * 8 * n_groups;
+    attend_kernel<4, 4><<<blocks, 256, 0, stream>>>(q_lat, q, kv_cache, pe_cache, row_offset, max_seqlen, plan, cum,
+                                                    batch, n_heads, scale_log2, part_o, part_l);
   }
   mark(ev, 2, stream);
   combine_kernel<<<dim3(batch, n_heads / 16), 256, 0, stream>>>(plan, cum, n_heads, part_o, part_l, o_lat, lse);

@@ -22,6 +22,9 @@ mla_status_t check_dims(const mla_dims_t* d) {
 
 // The largest decode batch: the combine kernel's grid x and the int32 sequence index.
 constexpr int64_t kMaxBatch = 1 << 24;
+// The longest decode cache: the attention kernel addresses a sequence's rows with 32-bit byte
+// offsets (rows of 1 KiB).
+constexpr int64_t kMaxSeqlen = int64_t(1) << 22;
 // The largest query-path token count (grid y = ceil(n / 64) stays far below 2^31).
 constexpr int64_t kMaxTokens = int64_t(1) << 36;
 
@@ -68,7 +71,7 @@ mla_status_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch, in
   mla_status_t st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (!bytes) return MLA_ERR_INVALID_ARG;
-  if (batch < 0 || batch > kMaxBatch || max_seqlen < 0 || max_seqlen > (int64_t(1) << 40)) return MLA_ERR_SHAPE;
+  if (batch < 0 || batch > kMaxBatch || max_seqlen < 0 || max_seqlen > kMaxSeqlen) return MLA_ERR_SHAPE;
   *bytes = batch == 0 ? 0 : mla::decode_layout(dims->n_heads, batch, max_seqlen).total;
   return MLA_OK;
 }
@@ -80,7 +83,7 @@ mla_status_t mla_decode_ex(const mla_dims_t* dims, int32_t batch, const uint16_t
                            hipEvent_t* stage_events) {
   mla_status_t st = check_dims(dims);
   if (st != MLA_OK) return st;
-  if (batch < 0 || batch > kMaxBatch || max_seqlen < 0 || max_seqlen > (int64_t(1) << 40)) return MLA_ERR_SHAPE;
+  if (batch < 0 || batch > kMaxBatch || max_seqlen < 0 || max_seqlen > kMaxSeqlen) return MLA_ERR_SHAPE;
   if (batch == 0) return MLA_OK;
   if (!q || !wkv_b || !kv_cache || !pe_cache || !cache_seqlens || !workspace || !out) return MLA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(wkv_b) || !aligned16(kv_cache) || !aligned16(pe_cache) ||
