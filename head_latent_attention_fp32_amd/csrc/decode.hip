@@ -120,37 +120,49 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
 // ---------------------------------------------------------------------------------------------
 // 2. Split-KV attention over runs.
 //
-//    Block = NW waves, H = 16 NW heads. Cached rows stream through an NSTAGE-deep ring of 32-row
-//    LDS tiles filled by 16-byte direct-to-LDS buffer loads (the descriptor's range check
-//    zero-fills rows past the end of the sequence), so every row is read from HBM once.
-//    Per tile:
-//      scores:  wave w holds the query of heads 16w .. 16w+15 (absorbed latent and rotary part,
-//               576 features) in VGPRs and computes S^T[t][h] = sum_k tile[t][k] q[h][k] on MFMA
-//               (A operand: ds_read_b128 of tile rows), the per-head maximum and P = 2^(s - m),
-//               which it writes to a small LDS buffer;
-//      values:  wave w owns latent columns [512 w / NW, 512 (w+1) / NW) of every head and adds
-//               O^T[c][h] += sum_t tile[t][c] P^T[t][h] (A operand: ds_read_b64_tr_b16, the
-//               transposing LDS read, of tile columns; B operand: ds_read_b128 of P).
-//    So a wave holds 72 registers of query and 128 of accumulators whatever H is.
+//    Block = 8 waves and 64 heads: head group hg covers heads [64 hg, 64 hg + 64); slots past
+//    n_heads (16 or 32 heads) run on a zero query and are never stored. Cached rows stream through
+//    a 4-deep ring of 32-row LDS tiles filled by 16-byte direct-to-LDS buffer loads. Each tile's
+//    buffer descriptor ends at the segment's last row, so rows past it read as zeros, and every
+//    row is read from HBM once per head group.
+//    The waves split by role, one of each role per SIMD:
+//      score waves 0-3   wave w holds the query of heads 16w .. 16w+15 (absorbed latent and
+//                        rotary part, 576 features) in VGPRs and computes S^T[t][h] =
+//                        sum_k tile[t][k] q[h][k] on MFMA (A operand: ds_read_b128 of tile rows),
+//                        then the softmax: per head a reference m (log2 units, scale folded in)
+//                        that moves only when a tile's maximum exceeds it by more than 8, so
+//                        p = 2^(s - m) <= 2^8, written to LDS as bf16;
+//      value waves 4-7   wave 4+w owns latent columns [128 w, 128 w + 128) of all 64 heads and
+//                        adds O^T[c][h] += sum_t tile[t][c] P^T[t][h] (A operand:
+//                        ds_read_b64_tr_b16, the transposing LDS read, of tile columns; B operand:
+//                        ds_read_b128 of P).
+//    In the iteration of tile t the score waves work on tile t+1 while the value waves work on
+//    tile t, so the softmax arithmetic of one role runs beside the MFMAs of the other; one barrier
+//    per tile hands P(t+1), its rescale factors and flags (double-buffered by tile parity) to the
+//    value waves. A head whose reference moved has its accumulators rescaled before the value
+//    MFMAs of that tile, on a path outside the loop, so that inside it accumulators are only ever
+//    touched by MFMAs.
 //    P^T comes out of the S^T accumulators with lane l holding tokens 4(l/16)+{0..3} and
-//    16+4(l/16)+{0..3} of head l%16 -- its k-group of the P.V product -- and is stored per head
-//    in that order; V^T is read in the same token order.
-//    LDS tile: latent part [32 rows][1024 B] whose 16-byte chunk c of row r sits at c ^ fk(r),
-//    fk(r) = 2(r&7) + ((r>>3)&1); rotary part [32 rows][128 B] with chunk c at c ^ ((r>>1)&7);
-//    P rows of 80 B. Then 16 rows read at one chunk, and 8 consecutive rows read at two adjacent
-//    chunks, touch 16 distinct 16-byte bank groups.
-//    Softmax: per head a reference m (log2 units, scale folded in) that moves only when a tile's
-//    maximum exceeds it by more than 8 -- then every wave rescales its accumulators and l by the
-//    factor each head publishes in LDS -- so p = 2^(s - m) <= 2^8.
+//    16+4(l/16)+{0..3} of head l%16 -- its k-group of the P.V product -- and V^T is read in the
+//    same token order.
+//    LDS layouts: latent part of a tile [32 rows][1024 B] with 16-byte chunk c of row r at
+//    c ^ fk(r), fk(r) = 2(r&7); rotary part [32 rows][128 B] with chunk c at c ^ ((r>>1)&7); P as
+//    [4 token chunks][64 heads][16 B]. A 128-bit LDS read serves each half-wave in two passes, one
+//    for lanes 0-7 and 24-31 and one for lanes 8-23 (as measured with the LDS bank-conflict
+//    counter), over 64 banks that hold one 256-byte line: each pass of the score reads (rows r,
+//    chunks 4k + l/16), of the P reads (heads r, chunk l/16) and of the rotary reads then touches
+//    16 distinct 16-byte bank groups, and the transposing reads of a half-wave (8 rows at two
+//    adjacent chunks each) touch all 32 8-byte bank pairs once.
 // ---------------------------------------------------------------------------------------------
 constexpr int kKvBytes = kTileTok * kKvLora * 2;           // 32768
 constexpr int kPeBytes = kTileTok * kRope * 2;             // 4096
 constexpr int kTileBytes = kKvBytes + kPeBytes;            // 36864
-constexpr int kTileLoads = kTileBytes / 1024;              // 36 loads of 64 lanes x 16 B
-constexpr int kPStride = kTileTok * 2 + 16;                // bytes per head row of P
+constexpr int kStages = 4;                                 // tiles in the LDS ring
+constexpr int kBlockHeads = 64;                            // heads of one workgroup
+constexpr int kPBytes = kTileTok / 8 * kBlockHeads * 16;   // one P buffer
 constexpr uint32_t kRsrcWord3 = 0x00020000u;               // raw buffer, 32-bit data format
 
-__device__ __forceinline__ int fk(int row) { return 2 * (row & 7) + ((row >> 3) & 1); }
+__device__ __forceinline__ int fk(int row) { return 2 * (row & 7); }
 __device__ __forceinline__ int fp(int row) { return (row >> 1) & 7; }
 
 // Workgroup barrier that orders LDS accesses only. __syncthreads() also orders global memory,
@@ -167,7 +179,7 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Wait until at most `tiles_after` tiles of loads (of `L` loads each) are still in flight.
+// Wait until at most `tiles_after` tiles of this wave's loads (L per tile) are still in flight.
 template <int L>
 __device__ __forceinline__ void wait_tiles(int tiles_after) {
   if (tiles_after >= 3) wait_vm<3 * L>();
@@ -181,156 +193,164 @@ typedef __attribute__((ext_vector_type(4))) short i16x4;
 
 // Raw buffer descriptor over [base, base + bytes) built from wave-uniform values (so that it
 // lives in SGPRs); loads beyond the range return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
   const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
   void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)),
+                                           kRsrcWord3);
 }
 
-// 16-byte direct-to-LDS buffer load: lane l's 16 bytes at rsrc + voff land at LDS byte offset
-// dst + 16 l. Issued from an asm block: the compiler cannot tell which ring stage such a load
+// 16-byte direct-to-LDS buffer load: lane l's 16 bytes at rsrc + voff land at LDS byte address
+// lds_addr + 16 l. Issued from an asm block: the compiler cannot tell which ring stage such a load
 // writes and would otherwise wait for every load in flight before any LDS read. Completion is
 // tracked with explicit vmcnt waits and barriers. The block writes no registers.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, const uint8_t* dst, uint32_t voff) {
-  const uint32_t d = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)dst));
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr, uint32_t voff) {
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(rsrc), "{m0}"(d)
+               : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
                : "memory");
 }
-template <int NW, int NSTAGE>
-__global__ __launch_bounds__(NW * 64, 1) void attend_kernel(
-    const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
-    const uint16_t* __restrict__ pe, const int64_t* __restrict__ row_offset, int64_t max_seqlen,
-    const Plan* __restrict__ plan, const int64_t* __restrict__ cum, int batch, int n_heads, float scale_log2,
-    float* __restrict__ part_o, float* __restrict__ part_l) {
-  // A block attends H = 16 NW heads: head group hg covers heads [H hg, H hg + H); slots past
-  // n_heads (fewer heads than H) run on a zero query and are never stored. The blocks of the
-  // head groups of one run share blockIdx mod 8 -- the same XCD and its L2 -- and are dispatched
-  // next to each other, so the tiles one of them pulls from HBM are L2 hits for the others.
-  constexpr int H = 16 * NW;
-  constexpr int CB = 32 / NW;                              // 16-column blocks of the latent per wave
-  constexpr int LMAX = (kTileLoads + NW - 1) / NW;         // loads per wave per tile (first waves)
-  constexpr int LMIN = kTileLoads / NW;
-  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "pipeline depth");
 
-  const int64_t N = plan->total_tokens;
-  const int64_t G = plan->runs;
-  const int n_groups = (n_heads + H - 1) / H;
-  const int hg = (blockIdx.x >> 3) % n_groups;
-  const int64_t g = (blockIdx.x & 7) + 8 * (blockIdx.x / (8 * n_groups));
-  if (g >= G) return;
-  const int head0 = hg * H;
+__device__ __forceinline__ bf16x8 lds_b128(const uint8_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t pbuf[H * kPStride];
-  __shared__ float alpha_s[H];
-  __shared__ int flag_s[NW];
+// Two transposing 8-byte reads (rows +0 and +16 of the tile) -> one A operand of 8 tokens.
+__device__ __forceinline__ bf16x8 lds_vt(const uint8_t* p) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p + 16 * 1024));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: lets wave-derived values live in SGPRs
-  const int r = lane & 15, grp = lane >> 4;
-  const int my_loads = (kTileLoads - wave + NW - 1) / NW;  // loads j = wave + NW k of each tile
-  const int c_wave = wave * CB;                            // first 16-column block of this wave
+// State shared by the two roles of an attention workgroup. Both walk the same segments (the
+// pieces of the run that lie in one sequence) and pass the same barriers: one before the first
+// tile, one per tile, three at the end of a segment.
+struct AttendCtx {
+  const uint16_t* q_lat;
+  const uint16_t* q;
+  const uint16_t* kv;
+  const uint16_t* pe;
+  const int64_t* row_offset;
+  int64_t max_seqlen;
+  const int64_t* cum;
+  int batch, n_heads, head0;
+  int64_t g, start, end;
+  float scale_log2;
+  float* part_o;
+  float* part_l;
+  uint8_t* ring;
+  uint8_t* pbuf;
+  float (*alpha_s)[kBlockHeads];
+  int (*flag_s)[4];
+  int wave, lane;
+};
 
-  int64_t start = run_start(g, N, G);
-  const int64_t end = run_start(g + 1, N, G);
-  int lo = 0, hi = batch - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (cum[mid + 1] > start) hi = mid; else lo = mid + 1;
+struct Segment {
+  int b, n_rows, n_tiles;
+  const uint16_t* kv_seg;   // first row of the segment
+  const uint16_t* pe_seg;
+};
+
+// First sequence of the run; then advance() steps through the sequences the run covers.
+struct SegmentWalk {
+  int64_t start;
+  int b;
+  __device__ SegmentWalk(const AttendCtx& c) : start(c.start) {
+    int lo = 0, hi = c.batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (c.cum[mid + 1] > start) hi = mid; else lo = mid + 1;
+    }
+    b = lo;
   }
-  int b = lo;
+  __device__ bool next(const AttendCtx& c, Segment& sg) {
+    if (start >= c.end) return false;
+    const int64_t seq0 = c.cum[b];
+    const int64_t seg_end = min(c.end, c.cum[b + 1]);
+    const int t0 = static_cast<int>(start - seq0);
+    sg.b = b;
+    sg.n_rows = static_cast<int>(seg_end - start);
+    sg.n_tiles = (sg.n_rows + kTileTok - 1) / kTileTok;
+    const int64_t row0 = (c.row_offset ? c.row_offset[b] : static_cast<int64_t>(b) * c.max_seqlen) + t0;
+    sg.kv_seg = c.kv + row0 * kKvLora;
+    sg.pe_seg = c.pe + row0 * kRope;
+    start = seg_end;
+    ++b;
+    while (b < c.batch && c.cum[b + 1] <= start) ++b;
+    return true;
+  }
+};
 
-  while (start < end) {
-    const int64_t seq0 = cum[b];
-    const int64_t seg_end = min(end, cum[b + 1]);
-    const int t0 = static_cast<int>(start - seq0), t1 = static_cast<int>(seg_end - seq0);
-    const int64_t base_row = row_offset ? row_offset[b] : static_cast<int64_t>(b) * max_seqlen;
-    const int n_tiles = (t1 - t0 + kTileTok - 1) / kTileTok;
-    // Descriptors over rows [0, t1) of this sequence: loads of later rows return zeros.
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kv + base_row * kKvLora, t1 * (kKvLora * 2));
-    const __amdgpu_buffer_rsrc_t rp = make_rsrc(pe + base_row * kRope, t1 * (kRope * 2));
+// Loads of tile t of segment sg into ring stage t % 4: wave w fills latent rows w + 8k (k < 4) --
+// physical chunk `lane` holds logical chunk lane ^ fk(row) = lane ^ 2w -- and a score wave also the
+// rotary rows 8w .. 8w+7 (physical chunk lane%8 of row 8w + lane/8 holds logical chunk
+// (lane%8) ^ fp(row)). The descriptors start at the tile's first row and end at the segment's last
+// row.
+template <bool kScorer>
+__device__ __forceinline__ void issue_tile(const AttendCtx& c, const Segment& sg, int t, uint32_t kv_lane,
+                                           uint32_t pe_voff) {
+  const uint32_t rows_left = static_cast<uint32_t>(sg.n_rows - t * kTileTok);
+  const __amdgpu_buffer_rsrc_t rk =
+      make_rsrc(sg.kv_seg + static_cast<int64_t>(t) * kTileTok * kKvLora, rows_left * 1024u);
+  const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)c.ring)) +
+                       (t % kStages) * kTileBytes;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) dma16(rk, dst + (c.wave + 8 * k) * 1024, kv_lane + (c.wave + 8 * k) * 1024);
+  if (kScorer) {
+    const __amdgpu_buffer_rsrc_t rp =
+        make_rsrc(sg.pe_seg + static_cast<int64_t>(t) * kTileTok * kRope, rows_left * 128u);
+    dma16(rp, dst + kKvBytes + c.wave * 1024, pe_voff);
+  }
+}
 
-    bf16x8 qf[18];
+// Score waves 0-3: S^T of heads 16w .. 16w+15, the softmax, P to LDS.
+__device__ __forceinline__ void score_role(const AttendCtx& c) {
+  constexpr int L = 5;   // loads per tile
+  const int w = c.wave, lane = c.lane, r = lane & 15, grp = lane >> 4;
+  const uint32_t kv_lane = static_cast<uint32_t>((lane ^ (2 * w)) << 4);
+  const int pe_row = 8 * w + (lane >> 3);
+  const uint32_t pe_voff = static_cast<uint32_t>(pe_row * 128 + (((lane & 7) ^ fp(pe_row)) << 4));
+  // LDS byte offsets. Latent k-step ks = 4a + k: row 16 tb + r, logical chunk 4 ks + grp at
+  // physical 16 a + 4 (k ^ (fk>>2)) + (grp ^ (fk&3)); a and tb go into immediates. Rotary k-steps
+  // 16 + k: row 16 tb + r, chunk 4 k + grp at (4 k + grp) ^ fp(r).
+  const int sf = fk(r);
+  int s_off[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) s_off[k] = r * 1024 + 64 * (k ^ (sf >> 2)) + 16 * (grp ^ (sf & 3));
+  const int e_off0 = kKvBytes + r * 128 + 16 * (grp ^ fp(r));
+  const int e_off1 = kKvBytes + r * 128 + 16 * ((4 + grp) ^ fp(r));
+  const int p_wr = (grp * kBlockHeads + w * 16 + r) * 16;
+  const int head = c.head0 + w * 16 + r;
+  const bool real = head < c.n_heads;
+
+  SegmentWalk walk(c);
+  Segment sg;
+  while (walk.next(c, sg)) {
+    const int n_tiles = sg.n_tiles;
+    bf16x8 qf[18];   // B operand: head 16 w + r, k-group grp of each k-step
     {
-      const int head = head0 + wave * 16 + r;
-      const bool real = head < n_heads;
       const int hq = real ? head : 0;
-      const uint16_t* ql = q_lat + (static_cast<int64_t>(b) * n_heads + hq) * kKvLora + grp * 8;
-      const uint16_t* qp = q + (static_cast<int64_t>(b) * n_heads + hq) * kQk + kNope + grp * 8;
+      const uint16_t* ql = c.q_lat + (static_cast<int64_t>(sg.b) * c.n_heads + hq) * kKvLora + grp * 8;
+      const uint16_t* qp = c.q + (static_cast<int64_t>(sg.b) * c.n_heads + hq) * kQk + kNope + grp * 8;
       const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) qf[ks] = as_bf16x8(real ? ldg16(ql + ks * 32) : z);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) qf[16 + ks] = as_bf16x8(real ? ldg16(qp + ks * 32) : z);
     }
-
-    // Load j of a tile fills latent row j (j < 32; lane = physical chunk) or rotary rows
-    // 8 (j - 32) .. +7 (lane = 8 rows x 8 physical chunks); this wave issues j = wave + NW k.
-    auto issue = [&](int tile) {
-      const int tt0 = t0 + tile * kTileTok;
-      uint8_t* dst = lds + (tile % NSTAGE) * kTileBytes;
-#pragma unroll
-      for (int k = 0; k < LMAX; ++k) {
-        const int j = wave + NW * k;
-        if (j < kTileLoads) {
-          if (j < kTileTok) {
-            const uint32_t voff = static_cast<uint32_t>(tt0 + j) * (kKvLora * 2) + ((lane ^ fk(j)) << 4);
-            dma16(rk, dst + j * 1024, voff);
-          } else {
-            const int row = 8 * (j - kTileTok) + (lane >> 3);
-            const uint32_t voff =
-                static_cast<uint32_t>(tt0 + row) * (kRope * 2) + (((lane & 7) ^ fp(row)) << 4);
-            dma16(rp, dst + kKvBytes + (j - kTileTok) * 1024, voff);
-          }
-        }
-      }
-    };
-
-    float m_ref = -INFINITY, lsum = 0.f;       // of head 16 wave + r
-    f32x4 o[CB][NW];                           // O^T[16 (c_wave + cb) + 4 grp + j][16 hb + r]
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int hb = 0; hb < NW; ++hb) o[cb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
     int issued = 0;
-#pragma unroll
-    for (int st = 0; st < NSTAGE - 1; ++st)
-      if (issued < n_tiles) issue(issued++);
+    while (issued < kStages && issued < n_tiles) issue_tile<true>(c, sg, issued++, kv_lane, pe_voff);
 
     f32x4 s[2];
-    float mx = 0.f;
-    // Wait for tile it, make it visible, start the next loads, S^T and its masked maximum.
-    auto scores = [&](int it) {
-      const int after = issued - 1 - it;
-      if (my_loads == LMAX) wait_tiles<LMAX>(after); else wait_tiles<LMIN>(after);
-      lds_barrier();
-      if (issued < n_tiles) issue(issued++);
-      const uint8_t* tile = lds + (it % NSTAGE) * kTileBytes;
-      // Per-lane operand offsets, recomputed per tile from an opaque copy of the lane id (cheaper
-      // than keeping them live through the loop). S^T latent k-steps: row tb*16 + r, logical chunk
-      // 4 ks + grp; rotary k-steps 16, 17: row tb*16 + r, logical chunk 4 (ks-16) + grp.
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int lr = ln & 15, lg = ln >> 4;
-      const int sf = fk(lr);
-      const int s_lane = lr * 1024 + ((lg ^ sf) & 3) * 16;
-      const int s_flip = sf >> 2;
-      const int p_off0 = kKvBytes + lr * 128 + ((lg ^ fp(lr)) * 16);
-      const int p_off1 = kKvBytes + lr * 128 + (((4 + lg) ^ fp(lr)) * 16);
+    auto scores = [&](int t) {
+      const uint8_t* tile = c.ring + (t % kStages) * kTileBytes;
+      auto rd = [&](int tb, int ks) {
+        return ks < 16 ? lds_b128(tile + tb * 16384 + (ks >> 2) * 256 + s_off[ks & 3])
+                       : lds_b128(tile + tb * 2048 + (ks == 16 ? e_off0 : e_off1));
+      };
       s[0] = f32x4{0.f, 0.f, 0.f, 0.f};
       s[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      auto rd = [&](int tb, int ks) {
-        const uint8_t* p = ks < 16 ? tile + tb * 16 * 1024 + s_lane + 64 * ((ks & ~3) + ((ks & 3) ^ s_flip))
-                                   : tile + tb * 16 * 128 + (ks == 16 ? p_off0 : p_off1);
-        return *reinterpret_cast<const bf16x8*>(p);
-      };
-      // Operand reads run kAhead k-steps ahead of the MFMAs (both 16-token halves per step).
-      constexpr int kAhead = 4;
+      constexpr int kAhead = 4;   // operand reads run 4 k-steps ahead of the MFMAs
       bf16x8 fa[kAhead][2];
 #pragma unroll
       for (int ks = 0; ks < kAhead; ++ks) {
@@ -346,145 +366,189 @@ __global__ __launch_bounds__(NW * 64, 1) void attend_kernel(
         }
         s[0] = mfma16x16x32(a0, qf[ks], s[0]);
         s[1] = mfma16x16x32(a1, qf[ks], s[1]);
-        __builtin_amdgcn_sched_barrier(0);
       }
-      const int valid = t1 - (t0 + it * kTileTok);
-      float m = -INFINITY;
+      // rows at or past the segment end score -inf
+      const int valid = sg.n_rows - t * kTileTok - 4 * grp;
+      if (sg.n_rows - t * kTileTok < kTileTok) {
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+        for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (tb * 16 + grp * 4 + j >= valid) s[tb][j] = -INFINITY;
-          m = fmaxf(m, s[tb][j]);
-        }
-      mx = max_over_rows(m) * scale_log2;
+          for (int j = 0; j < 4; ++j)
+            if (tb * 16 + j >= valid) s[tb][j] = -INFINITY;
+      }
     };
-
-    // P = 2^(s - m) into l and the LDS buffer (tokens in k-group order), then the barrier that
-    // publishes P, the rescale factors and the flags.
-    auto publish = [&]() {
+    auto tile_max = [&]() {
+      const float m = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                            fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+      return max_over_rows(m) * c.scale_log2;
+    };
+    float m_ref, lsum = 0.f;   // of head 16 w + r, log2 units; lsum over this lane's tokens
+    auto write_p = [&](int par) {
       float p[8];
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          p[tb * 4 + j] = exp2f(s[tb][j] * scale_log2 - m_ref);
-          lsum += p[tb * 4 + j];
-        }
-      *reinterpret_cast<bf16x8*>(pbuf + (wave * 16 + r) * kPStride + grp * 16) = bf16x8_from_f32(p);
-      lds_barrier();
+        for (int j = 0; j < 4; ++j) p[tb * 4 + j] = fast_exp2(s[tb][j] * c.scale_log2 - m_ref);
+      lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      *reinterpret_cast<bf16x8*>(c.pbuf + par * kPBytes + p_wr) = bf16x8_from_f32(p);
     };
 
-    // O^T += V^T P^T for this wave's latent columns and all heads.
-    auto values = [&](int it) {
-      const uint8_t* tile = lds + (it % NSTAGE) * kTileBytes;
-      // V^T: source row 4 grp + (r>>2) (+16), logical chunk 2 cb + ((r&3)>>1), byte (r&1)*8.
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int lr = ln & 15, lg = ln >> 4;
-      const int vrow = 4 * lg + (lr >> 2);
-      const int vf = fk(vrow);
-      const int v_lane = vrow * 1024 + ((((lr & 3) >> 1) ^ (vf & 1)) * 16) + (lr & 1) * 8;
-      const int v_flip = vf >> 1;
-      auto rdv = [&](int cb) {
-        const int c = c_wave + cb;
-        const uint8_t* v0 = tile + v_lane + 32 * ((c & ~7) + ((c & 7) ^ v_flip));
-        const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(v0));
-        const i16x4 hi4 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(v0 + 16 * 1024));
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
-      auto rdp = [&](int hb) { return *reinterpret_cast<const bf16x8*>(pbuf + (hb * 16 + r) * kPStride + grp * 16); };
-      if constexpr (CB <= 8) {
-        // the wave's V^T fragments and all P fragments are read up front, each once
-        bf16x8 vf[CB], pf[NW];
+    // Tile 0: its maximum is the first reference; no rescale for it.
+    wait_tiles<L>(issued - 1);
+    lds_barrier();
+    scores(0);
+    m_ref = tile_max();
+    write_p(0);
+    c.flag_s[0][w] = 0;
+    for (int it = 0; it < n_tiles; ++it) {
+      // tile it+1 landed, P(it) published, the stage of tile it-1 free for tile it+3
+      if (it + 1 < n_tiles) wait_tiles<L>(issued - 2 - it);
+      lds_barrier();
+      if (issued < n_tiles && issued <= it + 3) issue_tile<true>(c, sg, issued++, kv_lane, pe_voff);
+      if (it + 1 < n_tiles) {
+        scores(it + 1);
+        const float mx = tile_max();
+        const bool up = mx > m_ref + 8.f;
+        const float m_new = up ? mx : m_ref;
+        const float alpha = fast_exp2(m_ref - m_new);
+        m_ref = m_new;
+        lsum *= alpha;
+        write_p((it + 1) & 1);
+        c.alpha_s[(it + 1) & 1][w * 16 + r] = alpha;
+        c.flag_s[(it + 1) & 1][w] = __any(up) ? 1 : 0;
+      }
+    }
+    // Final normalisation: publish l of every head through alpha_s.
+    const float ltot = sum_over_rows(lsum);
+    lds_barrier();
+    c.alpha_s[0][w * 16 + r] = ltot;
+    if (grp == 0 && real) c.part_l[(c.g + sg.b) * c.n_heads + head] = (m_ref + __log2f(ltot)) * kLn2;
+    lds_barrier();
+    lds_barrier();   // alpha_s, P and the ring are reused by the next segment
+  }
+}
+
+// Value waves 4-7: O^T += V^T P^T for latent columns [128 w, 128 w + 128) of all 64 heads.
+__device__ __forceinline__ void value_role(const AttendCtx& c) {
+  constexpr int L = 4;   // loads per tile
+  const int w = c.wave & 3, lane = c.lane, r = lane & 15, grp = lane >> 4;
+  const uint32_t kv_lane = static_cast<uint32_t>((lane ^ (2 * c.wave)) << 4);
+  // V^T: source row 4 grp + (r>>2) (+16), columns 16 (8 w + cb) + 4 (r&3) .. +3 at physical chunk
+  // pair (8 w + cb) ^ (row & 7). P^T: head 16 hb + r, chunk grp.
+  const int vrow = 4 * grp + (r >> 2);
+  int v_off[8];
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) vf[cb] = rdv(cb);
+  for (int cb = 0; cb < 8; ++cb) v_off[cb] = vrow * 1024 + 256 * w + 32 * (cb ^ (vrow & 7)) + 8 * (r & 3);
+  const int p_rd = (grp * kBlockHeads + r) * 16;
+
+  SegmentWalk walk(c);
+  Segment sg;
+  while (walk.next(c, sg)) {
+    const int n_tiles = sg.n_tiles;
+    int issued = 0;
+    while (issued < kStages && issued < n_tiles) issue_tile<false>(c, sg, issued++, kv_lane, 0u);
+
+    f32x4 o[8][4];   // O^T[16 (8 w + cb) + 4 grp + j][16 hb + r]
 #pragma unroll
-        for (int hb = 0; hb < NW; ++hb) pf[hb] = rdp(hb);
+    for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-        for (int hb = 0; hb < NW; ++hb) {
+      for (int hb = 0; hb < 4; ++hb) o[cb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto values = [&](int t) {
+      const uint8_t* tile = c.ring + (t % kStages) * kTileBytes;
+      const uint8_t* pb = c.pbuf + (t & 1) * kPBytes + p_rd;
+      // V^T operands are read two column blocks ahead of their MFMAs
+      bf16x8 pf[4], vf[3];
 #pragma unroll
-          for (int cb = 0; cb < CB; ++cb) o[cb][hb] = mfma16x16x32(vf[cb], pf[hb], o[cb][hb]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else {
+      for (int hb = 0; hb < 4; ++hb) pf[hb] = lds_b128(pb + hb * 256);
+      vf[0] = lds_vt(tile + v_off[0]);
+      vf[1] = lds_vt(tile + v_off[1]);
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const bf16x8 a = rdv(cb);
+      for (int cb = 0; cb < 8; ++cb) {
+        if (cb + 2 < 8) vf[(cb + 2) % 3] = lds_vt(tile + v_off[cb + 2]);
 #pragma unroll
-          for (int hb = 0; hb < NW; ++hb) o[cb][hb] = mfma16x16x32(a, rdp(hb), o[cb][hb]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int hb = 0; hb < 4; ++hb) o[cb][hb] = mfma16x16x32(vf[cb % 3], pf[hb], o[cb][hb]);
       }
     };
+    auto flagged = [&](int par) {
+      return (c.flag_s[par][0] | c.flag_s[par][1] | c.flag_s[par][2] | c.flag_s[par][3]) != 0;
+    };
 
-    // The first tile sets the reference (O and l are still zero).
-    scores(0);
-    m_ref = mx;
-    publish();
-    values(0);
-    int it = 1;
-    while (it < n_tiles) {
-      // Tiles whose maximum stays within 2^8 of the reference of every head: the accumulators are
-      // only ever updated by MFMAs in this loop.
-      bool rescale = false;
+    wait_tiles<L>(issued - 1);
+    lds_barrier();
+    int it = 0;
+    for (;;) {
+      bool moved = false;
       for (; it < n_tiles; ++it) {
-        scores(it);
-        const bool up = __any(mx > m_ref + 8.f) != 0;
-        if (up) {
-          const float m_new = fmaxf(m_ref, mx);
-          const float alpha = exp2f(m_ref - m_new);
-          m_ref = m_new;
-          lsum *= alpha;
-          if (grp == 0) alpha_s[wave * 16 + r] = alpha;
+        if (it + 1 < n_tiles) wait_tiles<L>(issued - 2 - it);
+        lds_barrier();
+        if (issued < n_tiles && issued <= it + 3) issue_tile<false>(c, sg, issued++, kv_lane, 0u);
+        if (flagged(it & 1)) {
+          moved = true;
+          break;
         }
-        if (lane == 0) flag_s[wave] = up ? 1 : 0;
-        publish();
-#pragma unroll
-        for (int w = 0; w < NW; ++w) rescale |= flag_s[w] != 0;
-        if (rescale) break;
         values(it);
       }
-      if (!rescale) break;
-      // Some head moved its reference: scale every accumulator by its head's factor.
+      if (!moved) break;
+      // Some head moved its reference at tile it: scale the accumulators (tiles < it) by each
+      // head's factor, then add the tile.
 #pragma unroll
-      for (int hb = 0; hb < NW; ++hb) {
-        const bool moved = flag_s[hb] != 0;
-        const float a = moved ? alpha_s[hb * 16 + r] : 1.f;
+      for (int hb = 0; hb < 4; ++hb) {
+        const float a = c.alpha_s[it & 1][hb * 16 + r];
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) o[cb][hb] *= a;
+        for (int cb = 0; cb < 8; ++cb) o[cb][hb] *= a;
       }
       values(it);
       ++it;
     }
-
-    // Final normalisation: every wave needs l of all heads; publish them through alpha_s.
-    const float ltot = sum_over_rows(lsum);
     lds_barrier();
-    if (grp == 0) alpha_s[wave * 16 + r] = ltot;
     lds_barrier();
-    const int64_t slot = g + b;
+    const int64_t slot = c.g + sg.b;
 #pragma unroll
-    for (int hb = 0; hb < NW; ++hb) {
-      if (head0 + hb * 16 < n_heads) {
-        const float inv = 1.f / alpha_s[hb * 16 + r];
-        float* po = part_o + (slot * n_heads + head0 + hb * 16 + r) * kKvLora + c_wave * 16 + grp * 4;
+    for (int hb = 0; hb < 4; ++hb) {
+      if (c.head0 + hb * 16 < c.n_heads) {
+        const float inv = 1.f / c.alpha_s[0][hb * 16 + r];
+        float* po = c.part_o + (slot * c.n_heads + c.head0 + hb * 16 + r) * kKvLora + w * 128 + grp * 4;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
+        for (int cb = 0; cb < 8; ++cb) {
           const f32x4 v = o[cb][hb] * inv;
           *reinterpret_cast<float4*>(po + cb * 16) = make_float4(v[0], v[1], v[2], v[3]);
         }
       }
     }
-    if (grp == 0 && head0 + wave * 16 < n_heads)
-      part_l[slot * n_heads + head0 + wave * 16 + r] = (m_ref + __log2f(ltot)) * kLn2;
-    lds_barrier();   // alpha_s / pbuf / ring are reused by the next segment
-
-    start = seg_end;
-    ++b;
-    while (b < batch && cum[b + 1] <= start) ++b;
+    lds_barrier();   // alpha_s, P and the ring are reused by the next segment
   }
+}
+
+__global__ __launch_bounds__(512, 1) void attend_kernel(
+    const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+    const uint16_t* __restrict__ pe, const int64_t* __restrict__ row_offset, int64_t max_seqlen,
+    const Plan* __restrict__ plan, const int64_t* __restrict__ cum, int batch, int n_heads, float scale_log2,
+    float* __restrict__ part_o, float* __restrict__ part_l) {
+  // The blocks of the head groups of one run share blockIdx mod 8 -- the same XCD and its L2 --
+  // and are dispatched next to each other, so the tiles one of them pulls from HBM are L2 hits for
+  // the others.
+  const int64_t N = plan->total_tokens;
+  const int64_t G = plan->runs;
+  const int n_groups = (n_heads + kBlockHeads - 1) / kBlockHeads;
+  const int hg = (blockIdx.x >> 3) % n_groups;
+  const int64_t g = (blockIdx.x & 7) + 8 * (blockIdx.x / (8 * n_groups));
+  if (g >= G) return;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages * kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[2 * kPBytes];
+  __shared__ float alpha_s[2][kBlockHeads];
+  __shared__ int flag_s[2][4];
+
+  AttendCtx c;
+  c.q_lat = q_lat; c.q = q; c.kv = kv; c.pe = pe; c.row_offset = row_offset; c.max_seqlen = max_seqlen;
+  c.cum = cum; c.batch = batch; c.n_heads = n_heads; c.head0 = hg * kBlockHeads;
+  c.g = g; c.start = run_start(g, N, G); c.end = run_start(g + 1, N, G);
+  c.scale_log2 = scale_log2; c.part_o = part_o; c.part_l = part_l;
+  c.ring = ring; c.pbuf = pbuf; c.alpha_s = alpha_s; c.flag_s = flag_s;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: wave-derived values live in SGPRs
+  c.lane = threadIdx.x & 63;
+  if (c.wave < 4) score_role(c);
+  else value_role(c);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -614,8 +678,8 @@ hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16
   {
     const int n_groups = (n_heads + 63) / 64;
     const int blocks = (lay.units + 7) / 8 * 8 * n_groups;
-    attend_kernel<4, 4><<<blocks, 256, 0, stream>>>(q_lat, q, kv_cache, pe_cache, row_offset, max_seqlen, plan, cum,
-                                                    batch, n_heads, scale_log2, part_o, part_l);
+    attend_kernel<<<blocks, 512, 0, stream>>>(q_lat, q, kv_cache, pe_cache, row_offset, max_seqlen, plan, cum, batch,
+                                              n_heads, scale_log2, part_o, part_l);
   }
   mark(ev, 2, stream);
   combine_kernel<<<dim3(batch, n_heads / 16), 256, 0, stream>>>(plan, cum, n_heads, part_o, part_l, o_lat, lse);

@@ -22,9 +22,9 @@ mla_status_t check_dims(const mla_dims_t* d) {
 
 // The largest decode batch: the combine kernel's grid x and the int32 sequence index.
 constexpr int64_t kMaxBatch = 1 << 24;
-// The longest decode cache: the attention kernel addresses a sequence's rows with 32-bit byte
-// offsets (rows of 1 KiB).
-constexpr int64_t kMaxSeqlen = int64_t(1) << 22;
+// The longest decode cache: the attention kernel addresses the rows of a sequence, and one tile
+// past them, through buffer descriptors with 32-bit byte ranges (rows of 1 KiB).
+constexpr int64_t kMaxSeqlen = int64_t(1) << 21;
 // The largest query-path token count (grid y = ceil(n / 64) stays far below 2^31).
 constexpr int64_t kMaxTokens = int64_t(1) << 36;
 

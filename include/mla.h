@@ -109,7 +109,7 @@ mla_status_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch, in
  *   pe_cache          bf16 rows of 64              cached rotated rotary key
  *   cache_row_offset  int64 [batch] or NULL        first cache row of sequence b; NULL = b*max_seqlen
  *   cache_seqlens     int32 [batch]                L_b (device); values are clamped to [0, max_seqlen]
- *   max_seqlen        host upper bound on L_b, 0 .. 4,194,304 (2^22)
+ *   max_seqlen        host upper bound on L_b, 0 .. 2,097,152 (2^21)
  *   workspace         >= mla_decode_workspace_size bytes of device memory (contents need not be
  *                     initialised; overwritten by the call)
  *   out               bf16 [batch, n_heads, 128]

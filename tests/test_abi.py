@@ -84,7 +84,7 @@ def test_decode_validation_and_workspace():
     assert need > 32 * 128 * 512 * 2 * 2          # at least q_lat and o_lat
     assert lib.mla_decode_workspace_size(ctypes.byref(d), -1, 4096, ctypes.byref(n)) == 3
     assert lib.mla_decode_workspace_size(ctypes.byref(d), 1, -5, ctypes.byref(n)) == 3
-    assert lib.mla_decode_workspace_size(ctypes.byref(d), 1, (1 << 22) + 1, ctypes.byref(n)) == 3
+    assert lib.mla_decode_workspace_size(ctypes.byref(d), 1, (1 << 21) + 1, ctypes.byref(n)) == 3
     assert lib.mla_decode_workspace_size(ctypes.byref(d), 0, 10, ctypes.byref(n)) == 0 and n.value == 0
     dec = lib.mla_decode
     args = lambda **kw: [kw.get(k, v) for k, v in [
