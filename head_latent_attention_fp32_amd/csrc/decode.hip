@@ -136,10 +136,11 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
 //                        adds O^T[c][h] += sum_t tile[t][c] P^T[t][h] (A operand:
 //                        ds_read_b64_tr_b16, the transposing LDS read, of tile columns; B operand:
 //                        ds_read_b128 of P).
-//    In the iteration of tile t the score waves work on tile t+1 while the value waves work on
-//    tile t, so the softmax arithmetic of one role runs beside the MFMAs of the other; one barrier
-//    per tile hands P(t+1), its rescale factors and flags (double-buffered by tile parity) to the
-//    value waves. A head whose reference moved has its accumulators rescaled before the value
+//    The iteration of tile t has two phases, each closed by a barrier. Phase A: the score waves
+//    compute S(t+1) with the MFMA pipes to themselves while the value waves issue the loads of tile
+//    t+3 (bound by the load unit). Phase B: the score waves' softmax of tile t+1 runs beside the
+//    value waves' MFMAs of tile t. The barrier that closes phase B hands P(t+1), its rescale factors
+//    and flags (double-buffered by tile parity) to the value waves. A head whose reference moved has its accumulators rescaled before the value
 //    MFMAs of that tile, on a path outside the loop, so that inside it accumulators are only ever
 //    touched by MFMAs.
 //    P^T comes out of the S^T accumulators with lane l holding tokens 4(l/16)+{0..3} and
@@ -179,12 +180,13 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Wait until at most `tiles_after` tiles of this wave's loads (L per tile) are still in flight.
+// Wait until at most `tiles_after` tiles of this wave's loads (L per tile) are still in flight
+// (one tile is the steady state of the loops).
 template <int L>
 __device__ __forceinline__ void wait_tiles(int tiles_after) {
-  if (tiles_after >= 3) wait_vm<3 * L>();
+  if (tiles_after == 1) wait_vm<L>();
+  else if (tiles_after >= 3) wait_vm<3 * L>();
   else if (tiles_after == 2) wait_vm<2 * L>();
-  else if (tiles_after == 1) wait_vm<L>();
   else wait_vm<0>();
 }
 
@@ -223,8 +225,8 @@ __device__ __forceinline__ bf16x8 lds_vt(const uint8_t* p) {
 }
 
 // State shared by the two roles of an attention workgroup. Both walk the same segments (the
-// pieces of the run that lie in one sequence) and pass the same barriers: one before the first
-// tile, one per tile, three at the end of a segment.
+// pieces of the run that lie in one sequence) and pass the same barriers: two before the first
+// tile, two per tile, three at the end of a segment.
 struct AttendCtx {
   const uint16_t* q_lat;
   const uint16_t* q;
@@ -240,6 +242,7 @@ struct AttendCtx {
   float* part_l;
   uint8_t* ring;
   uint8_t* pbuf;
+  uint8_t* xbuf;
   float (*alpha_s)[kBlockHeads];
   int (*flag_s)[4];
   int wave, lane;
@@ -281,45 +284,51 @@ struct SegmentWalk {
   }
 };
 
-// Loads of tile t of segment sg into ring stage t % 4: wave w fills latent rows w + 8k (k < 4) --
-// physical chunk `lane` holds logical chunk lane ^ fk(row) = lane ^ 2w -- and a score wave also the
-// rotary rows 8w .. 8w+7 (physical chunk lane%8 of row 8w + lane/8 holds logical chunk
-// (lane%8) ^ fp(row)). The descriptors start at the tile's first row and end at the segment's last
-// row.
-template <bool kScorer>
-__device__ __forceinline__ void issue_tile(const AttendCtx& c, const Segment& sg, int t, uint32_t kv_lane,
+// Loads of tile t of segment sg into ring stage t % 4, all issued by the value waves (the
+// score waves' critical path -- scores, then softmax -- must not stall behind the load queue):
+// value wave v fills latent rows v + 4k (k < 8) -- physical chunk `lane` holds logical chunk
+// lane ^ fk(row) -- and the rotary rows 8v .. 8v+7 (physical chunk lane%8 of row 8v + lane/8 holds
+// logical chunk (lane%8) ^ fp(row)). The descriptors start at the tile's first row and end at the
+// segment's last row; kv_voff[k] is the byte offset of lane's chunk of row v + 4k.
+__device__ __forceinline__ void issue_tile(const AttendCtx& c, const Segment& sg, int t, const uint32_t* kv_voff,
                                            uint32_t pe_voff) {
+  const int v = c.wave & 3;
   const uint32_t rows_left = static_cast<uint32_t>(sg.n_rows - t * kTileTok);
   const __amdgpu_buffer_rsrc_t rk =
       make_rsrc(sg.kv_seg + static_cast<int64_t>(t) * kTileTok * kKvLora, rows_left * 1024u);
+  const __amdgpu_buffer_rsrc_t rp =
+      make_rsrc(sg.pe_seg + static_cast<int64_t>(t) * kTileTok * kRope, rows_left * 128u);
   const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)c.ring)) +
                        (t % kStages) * kTileBytes;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) dma16(rk, dst + (c.wave + 8 * k) * 1024, kv_lane + (c.wave + 8 * k) * 1024);
-  if (kScorer) {
-    const __amdgpu_buffer_rsrc_t rp =
-        make_rsrc(sg.pe_seg + static_cast<int64_t>(t) * kTileTok * kRope, rows_left * 128u);
-    dma16(rp, dst + kKvBytes + c.wave * 1024, pe_voff);
-  }
+  for (int k = 0; k < 8; ++k) dma16(rk, dst + (v + 4 * k) * 1024, kv_voff[k]);
+  dma16(rp, dst + kKvBytes + v * 1024, pe_voff);
 }
 
-// Score waves 0-3: S^T of heads 16w .. 16w+15, the softmax, P to LDS.
+// Score waves 0-3. Wave w = (kh, hh) = (w & 1, w >> 1) holds the query of the 32 heads of half hh
+// over k half kh -- latent k-steps [8 kh, 8 kh + 8) and rotary k-step 16 + kh -- and computes the
+// partial S^T of those heads for all 32 tokens of a tile (each tile operand it reads feeds two
+// MFMAs). Partners w and w^1 then swap the partials of each other's 16 heads through LDS, so that
+// wave w ends with the full S^T of heads 16w .. 16w+15, runs their softmax and writes P to LDS.
+// They issue no loads: a tile is complete once the value waves, which wait for their own loads of
+// it, reach the next barrier.
 __device__ __forceinline__ void score_role(const AttendCtx& c) {
-  constexpr int L = 5;   // loads per tile
   const int w = c.wave, lane = c.lane, r = lane & 15, grp = lane >> 4;
-  const uint32_t kv_lane = static_cast<uint32_t>((lane ^ (2 * w)) << 4);
-  const int pe_row = 8 * w + (lane >> 3);
-  const uint32_t pe_voff = static_cast<uint32_t>(pe_row * 128 + (((lane & 7) ^ fp(pe_row)) << 4));
+  const int kh = w & 1, hh = w >> 1, partner = w ^ 1;
   // LDS byte offsets. Latent k-step ks = 4a + k: row 16 tb + r, logical chunk 4 ks + grp at
-  // physical 16 a + 4 (k ^ (fk>>2)) + (grp ^ (fk&3)); a and tb go into immediates. Rotary k-steps
-  // 16 + k: row 16 tb + r, chunk 4 k + grp at (4 k + grp) ^ fp(r).
+  // physical 16 a + 4 (k ^ (fk>>2)) + (grp ^ (fk&3)); a and tb go into immediates. Rotary k-step
+  // 16 + kh: row 16 tb + r, chunk 4 kh + grp at (4 kh + grp) ^ fp(r).
   const int sf = fk(r);
   int s_off[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) s_off[k] = r * 1024 + 64 * (k ^ (sf >> 2)) + 16 * (grp ^ (sf & 3));
-  const int e_off0 = kKvBytes + r * 128 + 16 * (grp ^ fp(r));
-  const int e_off1 = kKvBytes + r * 128 + 16 * ((4 + grp) ^ fp(r));
+  const int e_off = kKvBytes + r * 128 + 16 * ((4 * kh + grp) ^ fp(r));
   const int p_wr = (grp * kBlockHeads + w * 16 + r) * 16;
+  // Partial exchange: token half 0 through xbuf[receiver][lane]; token half 1 through the P buffer
+  // of the tile (idle until the softmax), at the receiver's own P slots: only the receiver writes
+  // there afterwards, and only after reading.
+  const int x_send0 = partner * 1024 + lane * 16, x_recv0 = w * 1024 + lane * 16;
+  const int x_send1 = (grp * kBlockHeads + partner * 16 + r) * 16;
   const int head = c.head0 + w * 16 + r;
   const bool real = head < c.n_heads;
 
@@ -327,47 +336,68 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
   Segment sg;
   while (walk.next(c, sg)) {
     const int n_tiles = sg.n_tiles;
-    bf16x8 qf[18];   // B operand: head 16 w + r, k-group grp of each k-step
-    {
-      const int hq = real ? head : 0;
-      const uint16_t* ql = c.q_lat + (static_cast<int64_t>(sg.b) * c.n_heads + hq) * kKvLora + grp * 8;
-      const uint16_t* qp = c.q + (static_cast<int64_t>(sg.b) * c.n_heads + hq) * kQk + kNope + grp * 8;
+    // B operands: qf[hb][j] = head 32 hh + 16 hb + r, k-group grp of k-step 8 kh + j (j < 8) or of
+    // rotary k-step 16 + kh (j = 8).
+    bf16x8 qf[2][9];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int hd = c.head0 + hh * 32 + hb * 16 + r;
+      const bool rl = hd < c.n_heads;
+      const int hq = rl ? hd : 0;
+      const uint16_t* ql = c.q_lat + (static_cast<int64_t>(sg.b) * c.n_heads + hq) * kKvLora + kh * 256 + grp * 8;
+      const uint16_t* qp = c.q + (static_cast<int64_t>(sg.b) * c.n_heads + hq) * kQk + kNope + kh * 32 + grp * 8;
       const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) qf[ks] = as_bf16x8(real ? ldg16(ql + ks * 32) : z);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) qf[16 + ks] = as_bf16x8(real ? ldg16(qp + ks * 32) : z);
+      for (int j = 0; j < 8; ++j) qf[hb][j] = as_bf16x8(rl ? ldg16(ql + j * 32) : z);
+      qf[hb][8] = as_bf16x8(rl ? ldg16(qp) : z);
     }
-    int issued = 0;
-    while (issued < kStages && issued < n_tiles) issue_tile<true>(c, sg, issued++, kv_lane, pe_voff);
 
-    f32x4 s[2];
+    f32x4 acc[2][2];   // partial S^T [token half tb][head block hb]
+    f32x4 s[2];        // full S^T of this wave's heads, token halves 0 and 1
     auto scores = [&](int t) {
       const uint8_t* tile = c.ring + (t % kStages) * kTileBytes;
-      auto rd = [&](int tb, int ks) {
-        return ks < 16 ? lds_b128(tile + tb * 16384 + (ks >> 2) * 256 + s_off[ks & 3])
-                       : lds_b128(tile + tb * 2048 + (ks == 16 ? e_off0 : e_off1));
+      auto rd = [&](int tb, int j) {
+        const int ks = 8 * kh + j;
+        return j < 8 ? lds_b128(tile + tb * 16384 + (ks >> 2) * 256 + s_off[ks & 3])
+                     : lds_b128(tile + tb * 2048 + e_off);
       };
-      s[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      s[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      constexpr int kAhead = 4;   // operand reads run 4 k-steps ahead of the MFMAs
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) acc[tb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      constexpr int kAhead = 9;   // every operand is read up front
       bf16x8 fa[kAhead][2];
 #pragma unroll
-      for (int ks = 0; ks < kAhead; ++ks) {
-        fa[ks][0] = rd(0, ks);
-        fa[ks][1] = rd(1, ks);
+      for (int j = 0; j < kAhead; ++j) {
+        fa[j][0] = rd(0, j);
+        fa[j][1] = rd(1, j);
       }
 #pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        const bf16x8 a0 = fa[ks % kAhead][0], a1 = fa[ks % kAhead][1];
-        if (ks + kAhead < 18) {
-          fa[ks % kAhead][0] = rd(0, ks + kAhead);
-          fa[ks % kAhead][1] = rd(1, ks + kAhead);
+      for (int j = 0; j < 9; ++j) {
+        const bf16x8 a0 = fa[j % kAhead][0], a1 = fa[j % kAhead][1];
+        if (j + kAhead < 9) {
+          fa[j % kAhead][0] = rd(0, j + kAhead);
+          fa[j % kAhead][1] = rd(1, j + kAhead);
         }
-        s[0] = mfma16x16x32(a0, qf[ks], s[0]);
-        s[1] = mfma16x16x32(a1, qf[ks], s[1]);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          acc[0][hb] = mfma16x16x32(a0, qf[hb][j], acc[0][hb]);
+          acc[1][hb] = mfma16x16x32(a1, qf[hb][j], acc[1][hb]);
+        }
       }
-      // rows at or past the segment end score -inf
+    };
+    auto send = [&](int par) {
+      const f32x4 v0 = kh ? acc[0][0] : acc[0][1];
+      const f32x4 v1 = kh ? acc[1][0] : acc[1][1];
+      *reinterpret_cast<f32x4*>(c.xbuf + x_send0) = v0;
+      *reinterpret_cast<f32x4*>(c.pbuf + par * kPBytes + x_send1) = v1;
+    };
+    // Full scores of tile t (after the exchange barrier); rows at or past the segment end -inf.
+    auto receive = [&](int t, int par) {
+      const f32x4 u0 = *reinterpret_cast<const f32x4*>(c.xbuf + x_recv0);
+      const f32x4 u1 = *reinterpret_cast<const f32x4*>(c.pbuf + par * kPBytes + p_wr);
+      s[0] = (kh ? acc[0][1] : acc[0][0]) + u0;
+      s[1] = (kh ? acc[1][1] : acc[1][0]) + u1;
       const int valid = sg.n_rows - t * kTileTok - 4 * grp;
       if (sg.n_rows - t * kTileTok < kTileTok) {
 #pragma unroll
@@ -394,19 +424,25 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
     };
 
     // Tile 0: its maximum is the first reference; no rescale for it.
-    wait_tiles<L>(issued - 1);
-    lds_barrier();
+    lds_barrier();   // tile 0 landed
     scores(0);
+    send(0);
+    lds_barrier();   // partials of tile 0 exchanged
+    receive(0, 0);
     m_ref = tile_max();
     write_p(0);
     c.flag_s[0][w] = 0;
     for (int it = 0; it < n_tiles; ++it) {
-      // tile it+1 landed, P(it) published, the stage of tile it-1 free for tile it+3
-      if (it + 1 < n_tiles) wait_tiles<L>(issued - 2 - it);
-      lds_barrier();
-      if (issued < n_tiles && issued <= it + 3) issue_tile<true>(c, sg, issued++, kv_lane, pe_voff);
+      lds_barrier();   // tile it+1 landed, P(it) published
+      // phase A: the scores of tile it+1 own the MFMA pipes (the value waves issue loads)
       if (it + 1 < n_tiles) {
         scores(it + 1);
+        send((it + 1) & 1);
+      }
+      lds_barrier();
+      // phase B: the softmax of tile it+1 beside the value MFMAs of tile it
+      if (it + 1 < n_tiles) {
+        receive(it + 1, (it + 1) & 1);
         const float mx = tile_max();
         const bool up = mx > m_ref + 8.f;
         const float m_new = up ? mx : m_ref;
@@ -430,9 +466,16 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
 
 // Value waves 4-7: O^T += V^T P^T for latent columns [128 w, 128 w + 128) of all 64 heads.
 __device__ __forceinline__ void value_role(const AttendCtx& c) {
-  constexpr int L = 4;   // loads per tile
+  constexpr int L = 9;   // loads per tile
   const int w = c.wave & 3, lane = c.lane, r = lane & 15, grp = lane >> 4;
-  const uint32_t kv_lane = static_cast<uint32_t>((lane ^ (2 * c.wave)) << 4);
+  uint32_t kv_voff[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int row = w + 4 * k;
+    kv_voff[k] = static_cast<uint32_t>(row * 1024 + ((lane ^ fk(row)) << 4));
+  }
+  const int pe_row = 8 * w + (lane >> 3);
+  const uint32_t pe_voff = static_cast<uint32_t>(pe_row * 128 + (((lane & 7) ^ fp(pe_row)) << 4));
   // V^T: source row 4 grp + (r>>2) (+16), columns 16 (8 w + cb) + 4 (r&3) .. +3 at physical chunk
   // pair (8 w + cb) ^ (row & 7). P^T: head 16 hb + r, chunk grp.
   const int vrow = 4 * grp + (r >> 2);
@@ -446,59 +489,56 @@ __device__ __forceinline__ void value_role(const AttendCtx& c) {
   while (walk.next(c, sg)) {
     const int n_tiles = sg.n_tiles;
     int issued = 0;
-    while (issued < kStages && issued < n_tiles) issue_tile<false>(c, sg, issued++, kv_lane, 0u);
+    while (issued < kStages && issued < n_tiles) issue_tile(c, sg, issued++, kv_voff, pe_voff);
 
     f32x4 o[8][4];   // O^T[16 (8 w + cb) + 4 grp + j][16 hb + r]
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) o[cb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto values = [&](int t) {
+    // O^T += V^T P^T for tile t, in two steps: read_values (phase A: P^T, V^T and the rescale flags
+    // of tile t into registers, beside the score waves' LDS reads) and values (phase B: a head whose
+    // reference moved at tile t has its accumulators -- tiles < t -- scaled, then the MFMAs).
+    bf16x8 pf[4], vf[8];
+    int4 fl;
+    auto read_values = [&](int t) {
       const uint8_t* tile = c.ring + (t % kStages) * kTileBytes;
       const uint8_t* pb = c.pbuf + (t & 1) * kPBytes + p_rd;
-      // V^T operands are read two column blocks ahead of their MFMAs
-      bf16x8 pf[4], vf[3];
+      fl = *reinterpret_cast<const int4*>(&c.flag_s[t & 1][0]);
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) pf[hb] = lds_b128(pb + hb * 256);
-      vf[0] = lds_vt(tile + v_off[0]);
-      vf[1] = lds_vt(tile + v_off[1]);
 #pragma unroll
-      for (int cb = 0; cb < 8; ++cb) {
-        if (cb + 2 < 8) vf[(cb + 2) % 3] = lds_vt(tile + v_off[cb + 2]);
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb) o[cb][hb] = mfma16x16x32(vf[cb % 3], pf[hb], o[cb][hb]);
-      }
+      for (int cb = 0; cb < 8; ++cb) vf[cb] = lds_vt(tile + v_off[cb]);
     };
-    auto flagged = [&](int par) {
-      return (c.flag_s[par][0] | c.flag_s[par][1] | c.flag_s[par][2] | c.flag_s[par][3]) != 0;
+    auto values = [&](int t) {
+      if ((fl.x | fl.y | fl.z | fl.w) != 0) {
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+          const float a = c.alpha_s[t & 1][hb * 16 + r];
+#pragma unroll
+          for (int cb = 0; cb < 8; ++cb) o[cb][hb] *= a;
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) o[cb][hb] = mfma16x16x32(vf[cb], pf[hb], o[cb][hb]);
     };
 
     wait_tiles<L>(issued - 1);
-    lds_barrier();
-    int it = 0;
-    for (;;) {
-      bool moved = false;
-      for (; it < n_tiles; ++it) {
-        if (it + 1 < n_tiles) wait_tiles<L>(issued - 2 - it);
-        lds_barrier();
-        if (issued < n_tiles && issued <= it + 3) issue_tile<false>(c, sg, issued++, kv_lane, 0u);
-        if (flagged(it & 1)) {
-          moved = true;
-          break;
-        }
-        values(it);
-      }
-      if (!moved) break;
-      // Some head moved its reference at tile it: scale the accumulators (tiles < it) by each
-      // head's factor, then add the tile.
-#pragma unroll
-      for (int hb = 0; hb < 4; ++hb) {
-        const float a = c.alpha_s[it & 1][hb * 16 + r];
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) o[cb][hb] *= a;
-      }
+    lds_barrier();   // tile 0 landed
+    lds_barrier();   // partials of tile 0 exchanged
+    for (int it = 0; it < n_tiles; ++it) {
+      // tile it+1 landed, P(it) published, the stage of tile it-1 free for tile it+3
+      if (it + 1 < n_tiles) wait_tiles<L>(issued - 2 - it);
+      lds_barrier();
+      // phase A: operand reads, then loads (bound by the load unit), while the score waves'
+      // MFMAs own the pipes
+      read_values(it);
+      if (issued < n_tiles && issued <= it + 3) issue_tile(c, sg, issued++, kv_voff, pe_voff);
+      lds_barrier();
+      // phase B: the value MFMAs of tile it beside the softmax of tile it+1
       values(it);
-      ++it;
     }
     lds_barrier();
     lds_barrier();
@@ -536,15 +576,16 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(
 
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages * kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t pbuf[2 * kPBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t xbuf[4 * 1024];
   __shared__ float alpha_s[2][kBlockHeads];
-  __shared__ int flag_s[2][4];
+  __shared__ __attribute__((aligned(16))) int flag_s[2][4];
 
   AttendCtx c;
   c.q_lat = q_lat; c.q = q; c.kv = kv; c.pe = pe; c.row_offset = row_offset; c.max_seqlen = max_seqlen;
   c.cum = cum; c.batch = batch; c.n_heads = n_heads; c.head0 = hg * kBlockHeads;
   c.g = g; c.start = run_start(g, N, G); c.end = run_start(g + 1, N, G);
   c.scale_log2 = scale_log2; c.part_o = part_o; c.part_l = part_l;
-  c.ring = ring; c.pbuf = pbuf; c.alpha_s = alpha_s; c.flag_s = flag_s;
+  c.ring = ring; c.pbuf = pbuf; c.xbuf = xbuf; c.alpha_s = alpha_s; c.flag_s = flag_s;
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: wave-derived values live in SGPRs
   c.lane = threadIdx.x & 63;
   if (c.wave < 4) score_role(c);
