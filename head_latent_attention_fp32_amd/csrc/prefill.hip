@@ -8,8 +8,10 @@
 // Two kernels:
 //   1. expand   [k_nope | v] = latent . wkv_b^T per head (MFMA GEMM, bf16 outputs as the bf16
 //               Linear of the excerpt). k_nope is written [b][h][t][128] and v transposed,
-//               [b][h][128][t], so that the attention kernel's P.V operand reads runs of keys.
-//   2. attend   flash-style causal attention: block = (b, h, 64 queries), wave = 16 queries;
+//               [b][h][128][t], so that the attention kernel's P.V operand reads runs of keys;
+//               within every 32 keys the order is permuted (key 16a + 4g + j at 8g + 4a + j) to
+//               match the key order in which P^T leaves the score accumulators.
+//   2. attend   flash-style causal attention: block = (b, h, 128 queries), wave = 32 queries;
 //               S^T = K . Q^T and O^T += V^T . P^T on MFMA with an fp32 online softmax; the
 //               score matrix never leaves registers.
 #include "mla_common.hpp"
@@ -19,16 +21,19 @@ namespace mla {
 
 namespace {
 
-constexpr int kQBlk = 64;     // queries per block
-constexpr int kKBlk = 64;     // keys per LDS tile
-constexpr int kKStride = kQk + 8;       // K tile row: 128 k_nope + 64 k_pe (+ pad)
-constexpr int kVStride = kKBlk + 8;     // V^T tile row: 64 keys (+ pad)
+constexpr int kKBlk = 64;     // key padding granule of the expanded k_nope / V^T
 
 // ---------------------------------------------------------------------------------------------
 // 1. Expansion: rows = B*T tokens, columns = H*256 (k_nope then v per head), K = 512.
 //    Block tile 64 tokens x 64 columns; wave (wt, wc) owns 32 x 32.
 // ---------------------------------------------------------------------------------------------
 constexpr int EX_BT = 64, EX_BC = 64, EX_BK = 64, EX_LD = EX_BK + 8;
+
+// Position of key t in its V^T row: within each group of 32, key 16a + 4g + j sits at 8g + 4a + j.
+__device__ __forceinline__ int64_t vt_pos(int64_t t) {
+  const int64_t w = t & 31;
+  return (t - w) + ((w >> 2) & 3) * 8 + (w >> 4) * 4 + (w & 3);
+}
 
 __global__ __launch_bounds__(256) void expand_kernel(const uint16_t* __restrict__ lat, const uint16_t* __restrict__ wkv_b,
                                                      int n_heads, int seqlen, int64_t t_pad, int64_t n_rows,
@@ -97,6 +102,7 @@ __global__ __launch_bounds__(256) void expand_kernel(const uint16_t* __restrict_
       if (tok0 >= n_rows) continue;
       const int64_t b = tok0 / seqlen;
       const int64_t t = tok0 - b * seqlen;   // 4 consecutive tokens stay in one sequence when seqlen % 4 == 0
+      const int64_t tp = vt_pos(t);          // and at 4 consecutive permuted positions
       const int64_t bh = b * n_heads + h;
       if (jj < kNope) {
 #pragma unroll
@@ -110,180 +116,268 @@ __global__ __launch_bounds__(256) void expand_kernel(const uint16_t* __restrict_
         uint2 u;
         u.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
         u.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-        *reinterpret_cast<uint2*>(&vt[(bh * kVDim + (jj - kNope)) * t_pad + t]) = u;
+        *reinterpret_cast<uint2*>(&vt[(bh * kVDim + (jj - kNope)) * t_pad + tp]) = u;
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int64_t tk = tok0 + e;
           if (tk >= n_rows) break;
           const int64_t bb = tk / seqlen, tt = tk - bb * seqlen;
-          vt[((bb * n_heads + h) * kVDim + (jj - kNope)) * t_pad + tt] = f32_to_bf16_bits(acc[i][j][e]);
+          vt[((bb * n_heads + h) * kVDim + (jj - kNope)) * t_pad + vt_pos(tt)] = f32_to_bf16_bits(acc[i][j][e]);
         }
       }
     }
   }
 }
 
-// Zero V^T columns seqlen .. t_pad-1: they sit inside the last key tile, where P is exactly 0, and
-// must hold finite values (0 * NaN would poison the product).
+// Zero the V^T entries of keys seqlen .. t_pad-1: they sit inside the last key tile, where P is
+// exactly 0, and must hold finite values (0 * NaN would poison the product).
 __global__ __launch_bounds__(256) void zero_vt_tail_kernel(uint16_t* __restrict__ vt, int64_t rows, int seqlen,
                                                            int64_t t_pad) {
   const int64_t w = t_pad - seqlen;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= rows * w) return;
   const int64_t row = i / w;
-  vt[row * t_pad + seqlen + (i - row * w)] = 0;
+  vt[row * t_pad + vt_pos(seqlen + (i - row * w))] = 0;
 }
 
 // ---------------------------------------------------------------------------------------------
-// 2. Causal flash attention for one (b, h, 64-query block); 4 waves x 16 queries.
+// 2. Causal flash attention for one (b, h, 128-query block); 4 waves x 32 queries.
+//
+//    Keys stream through two LDS stages of 64 keys, filled by 16-byte direct-to-LDS buffer loads
+//    (k_nope rows of 256 B, rotary key rows of 128 B, V^T rows of 64 keys); one barrier per tile.
+//    Per tile and wave: S^T (64 keys x 32 queries) = K . Q^T, 48 MFMAs with each K operand read
+//    once for both 16-query halves; the online softmax in fp32 (log2 units, scale folded in; the
+//    accumulators are rescaled only when a query's maximum grows by more than 8); O^T (128 dims x
+//    32 queries) += V^T . P^T, 32 MFMAs, with P^T taken from the score accumulators in registers.
+//    LDS layouts (16-byte chunks): k_nope chunk c of key row r at c ^ 2(r&7); rotary key and V^T
+//    rows (128 B) chunk c of row r at c ^ ((r>>1)&7) -- every 128-bit operand read is free of bank
+//    conflicts under the two-pass service of a half-wave (lanes 0-7 with 24-31, lanes 8-23).
+//    Blocks of one (b, h) share an XCD (blockIdx mod 8), so its K and V^T stay in that L2; within
+//    it the longest query blocks go first.
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void attend_kernel(
+constexpr int kPQ = 128;                    // queries per block
+constexpr int kPK = 64;                     // keys per tile
+constexpr int kKnBytes = kPK * kNope * 2;   // 16384
+constexpr int kKpBytes = kPK * kRope * 2;   // 8192
+constexpr int kVtBytes = kVDim * kPK * 2;   // 16384
+constexpr int kStage = kKnBytes + kKpBytes + kVtBytes;   // 40960
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)),
+                                           kRsrcWord3);
+}
+
+// 16-byte direct-to-LDS buffer load (lane l's bytes land at lds_addr + 16 l; loads outside the
+// descriptor's range return zeros); completion is tracked with explicit vmcnt waits.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ bf16x8 lds_b128(const uint8_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ int swz_kn(int row) { return 2 * (row & 7); }
+__device__ __forceinline__ int swz_128(int row) { return (row >> 1) & 7; }
+
+__global__ __launch_bounds__(256, 2) void attend_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ knope, const uint16_t* __restrict__ vt,
-    const uint16_t* __restrict__ k_pe, int n_heads, int seqlen, int64_t t_pad, float scale_log2,
+    const uint16_t* __restrict__ k_pe, int batch, int n_heads, int seqlen, int64_t t_pad, float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks_[kKBlk * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vs_[kVDim * kVStride];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage[2][kStage];
 
-  const int n_qb = gridDim.x;
-  const int qb = n_qb - 1 - blockIdx.x;          // longest rows first
-  const int h = blockIdx.y;
-  const int64_t b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_qb = (seqlen + kPQ - 1) / kPQ;
+  const int n_bh = batch * n_heads;
+  const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3;
+  const int bh = xcd + 8 * (i / n_qb);
+  if (bh >= n_bh) return;
+  const int qb = n_qb - 1 - i % n_qb;                    // longest query blocks first
+  const int64_t b = bh / n_heads;
+  const int h = bh % n_heads;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, grp = lane >> 4;
-  const int q0 = qb * kQBlk;
-  const int tq = q0 + wave * 16 + r;             // this lane's query (B-operand column)
-  const int tq_c = min(tq, seqlen - 1);
+  const int q0 = qb * kPQ + wave * 32;                   // this wave's first query
 
-  bf16x8 qf[6];
-  {
-    const uint16_t* qp = q + ((b * seqlen + tq_c) * n_heads + h) * kQk + grp * 8;
+  // Query fragments (B operand): query q0 + 16 qh + r, k-group grp of each of the 6 k-steps.
+  bf16x8 qf[2][6];
 #pragma unroll
-    for (int ks = 0; ks < 6; ++ks) qf[ks] = as_bf16x8(ldg16(qp + ks * 32));
+  for (int qh = 0; qh < 2; ++qh) {
+    const int tq = min(q0 + 16 * qh + r, seqlen - 1);
+    const uint16_t* qp = q + ((b * seqlen + tq) * n_heads + h) * kQk + grp * 8;
+#pragma unroll
+    for (int ks = 0; ks < 6; ++ks) qf[qh][ks] = as_bf16x8(ldg16(qp + ks * 32));
   }
-  const uint16_t* kn = knope + (b * n_heads + h) * t_pad * kNope;
-  const uint16_t* vh = vt + (b * n_heads + h) * kVDim * t_pad;
+
+  const uint16_t* kn = knope + static_cast<int64_t>(bh) * t_pad * kNope;
+  const uint16_t* vh = vt + static_cast<int64_t>(bh) * kVDim * t_pad;
   const uint16_t* pe = k_pe + b * static_cast<int64_t>(seqlen) * kRope;
+  const uint32_t st_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)&stage[0][0]));
 
-  // Per tile: 64 rows x 16 chunks of k_nope, 64 x 8 of k_pe, 128 x 8 of V^T = 2560 chunks.
-  constexpr int kChunks = kKBlk * 16 + kKBlk * 8 + kVDim * 8;
-  constexpr int CH = kChunks / 256;
-  uint4 pf[CH];
-  auto fetch = [&](int k0) {
+  // Loads of a tile, 10 per wave: k_nope instructions d = wave + 4e (4 keys x 256 B each), rotary
+  // d = wave + 4e (8 keys x 128 B), V^T d = wave + 4e (8 dims x 128 B).
+  uint32_t kn_off[4], kp_off[2], vt_off[4];
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int i = tid + 256 * c;
-      if (i < kKBlk * 16) {
-        const int row = i >> 4, ch = i & 15;
-        const int t = min(k0 + row, seqlen - 1);
-        pf[c] = ldg16(kn + static_cast<int64_t>(t) * kNope + ch * 8);
-      } else if (i < kKBlk * 24) {
-        const int j = i - kKBlk * 16;
-        const int row = j >> 3, ch = j & 7;
-        const int t = min(k0 + row, seqlen - 1);
-        pf[c] = ldg16(pe + static_cast<int64_t>(t) * kRope + ch * 8);
-      } else {
-        const int j = i - kKBlk * 24;
-        const int d = j >> 3, ch = j & 7;
-        pf[c] = ldg16(vh + static_cast<int64_t>(d) * t_pad + k0 + ch * 8);   // t_pad covers the tile
-      }
-    }
-  };
-  auto stash = [&]() {
+  for (int e = 0; e < 4; ++e) {
+    const int d = wave + 4 * e;
+    const int key = 4 * d + (lane >> 4);
+    kn_off[e] = static_cast<uint32_t>(key * 256 + (((lane & 15) ^ swz_kn(key)) << 4));
+    const int dim = 8 * d + (lane >> 3);
+    vt_off[e] = static_cast<uint32_t>(dim * t_pad * 2 + (((lane & 7) ^ swz_128(dim)) << 4));
+  }
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int i = tid + 256 * c;
-      if (i < kKBlk * 16) {
-        const int row = i >> 4, ch = i & 15;
-        *reinterpret_cast<uint4*>(&ks_[row * kKStride + ch * 8]) = pf[c];
-      } else if (i < kKBlk * 24) {
-        const int j = i - kKBlk * 16;
-        const int row = j >> 3, ch = j & 7;
-        *reinterpret_cast<uint4*>(&ks_[row * kKStride + kNope + ch * 8]) = pf[c];
-      } else {
-        const int j = i - kKBlk * 24;
-        const int d = j >> 3, ch = j & 7;
-        *reinterpret_cast<uint4*>(&vs_[d * kVStride + ch * 8]) = pf[c];
-      }
-    }
+  for (int e = 0; e < 2; ++e) {
+    const int d = wave + 4 * e;
+    const int key = 8 * d + (lane >> 3);
+    kp_off[e] = static_cast<uint32_t>(key * 128 + (((lane & 7) ^ swz_128(key)) << 4));
+  }
+  auto issue = [&](int kt) {
+    const int k0 = kt * kPK;
+    const uint32_t dst = st_lds + (kt & 1) * kStage;
+    const auto rk = make_rsrc(kn + static_cast<int64_t>(k0) * kNope, static_cast<uint32_t>(t_pad - k0) * 256u);
+    const int rows_pe = seqlen - k0;
+    const auto rp = make_rsrc(pe + static_cast<int64_t>(k0) * kRope, static_cast<uint32_t>(rows_pe) * 128u);
+    const auto rv = make_rsrc(vh + k0, static_cast<uint32_t>(kVDim * t_pad - k0) * 2u);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dma16(rk, dst + (wave + 4 * e) * 1024, kn_off[e]);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) dma16(rp, dst + kKnBytes + (wave + 4 * e) * 1024, kp_off[e]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dma16(rv, dst + kKnBytes + kKpBytes + (wave + 4 * e) * 1024, vt_off[e]);
   };
 
-  float m = -INFINITY, lsum = 0.f;
-  f32x4 o[8];
+  // Operand offsets within a stage. Scores: key row 16 kb + r, k-step ks < 4: k_nope chunk
+  // 4 ks + grp; ks = 4, 5: rotary chunk 4 (ks - 4) + grp. Values: V^T row 16 db + r, chunk 4 ks + grp
+  // (keys 4 grp + j and 16 + 4 grp + j of the 32-key group ks, in the permuted order).
+  int kn_rd[4], kp_rd[2], v_rd[2];
 #pragma unroll
-  for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int n_kt = min(qb + 1, (seqlen + kKBlk - 1) / kKBlk);
-  fetch(0);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    __syncthreads();
-    stash();
-    __syncthreads();
-    if (kt + 1 < n_kt) fetch((kt + 1) * kKBlk);
-    const int k0 = kt * kKBlk;
-
-    f32x4 s[4];
+  for (int ks = 0; ks < 4; ++ks) kn_rd[ks] = r * 256 + (((4 * ks + grp) ^ swz_kn(r)) << 4);
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t* arow = &ks_[(mb * 16 + r) * kKStride + grp * 8];
-#pragma unroll
-      for (int ks = 0; ks < 6; ++ks) acc = mfma16x16x32(*reinterpret_cast<const bf16x8*>(arow + ks * 32), qf[ks], acc);
-      s[mb] = acc;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = k0 + mb * 16 + grp * 4 + j;
-        if (key > tq || key >= seqlen) s[mb][j] = -INFINITY;
-        mx = fmaxf(mx, s[mb][j]);
-      }
-    mx = max_over_rows(mx);
-    const float m_new = fmaxf(m, mx);
-    const float alpha = exp2f((m - m_new) * scale_log2);
-    const float mref = m_new * scale_log2;
-    float p[16];
-    float ps = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        p[mb * 4 + j] = exp2f(s[mb][j] * scale_log2 - mref);
-        ps += p[mb * 4 + j];
-      }
-    lsum = lsum * alpha + ps;
-    m = m_new;
-    const bf16x8 pb0 = bf16x8_from_f32(p), pb1 = bf16x8_from_f32(p + 8);
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const uint16_t* vrow = &vs_[(db * 16 + r) * kVStride + grp * 4];
-      uint4 u0, u1;
-      const uint2 a0 = *reinterpret_cast<const uint2*>(vrow);
-      const uint2 a1 = *reinterpret_cast<const uint2*>(vrow + 16);
-      const uint2 a2 = *reinterpret_cast<const uint2*>(vrow + 32);
-      const uint2 a3 = *reinterpret_cast<const uint2*>(vrow + 48);
-      u0 = make_uint4(a0.x, a0.y, a1.x, a1.y);
-      u1 = make_uint4(a2.x, a2.y, a3.x, a3.y);
-      o[db] = o[db] * alpha;
-      o[db] = mfma16x16x32(as_bf16x8(u0), pb0, o[db]);
-      o[db] = mfma16x16x32(as_bf16x8(u1), pb1, o[db]);
-    }
+  for (int ks = 0; ks < 2; ++ks) {
+    kp_rd[ks] = kKnBytes + r * 128 + (((4 * ks + grp) ^ swz_128(r)) << 4);
+    v_rd[ks] = kKnBytes + kKpBytes + r * 128 + (((4 * ks + grp) ^ swz_128(r)) << 4);
   }
 
-  const float ltot = sum_over_rows(lsum);
-  if (tq < seqlen) {
-    const float inv = 1.f / ltot;
-    uint16_t* dst = out + ((b * seqlen + tq) * n_heads + h) * kVDim + grp * 4;
+  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};   // per query (log2 units)
+  f32x4 o[2][8];
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      uint2 u;
-      u.x = pack_bf16x2(o[db][0] * inv, o[db][1] * inv);
-      u.y = pack_bf16x2(o[db][2] * inv, o[db][3] * inv);
-      *reinterpret_cast<uint2*>(dst + db * 16) = u;
+  for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[qh][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // keys 0 .. min(seqlen, last query of the block + 1)
+  const int k_end = min(seqlen, (qb + 1) * kPQ);
+  const int n_kt = (k_end + kPK - 1) / kPK;
+  issue(0);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));   // vmcnt(0): this wave's loads of tile kt
+    lds_barrier();                                               // everyone's; stage kt-1 free
+    if (kt + 1 < n_kt) issue(kt + 1);
+    const uint8_t* st = &stage[kt & 1][0];
+    const int k0 = kt * kPK;
+
+    f32x4 s[2][4];   // [query half][key block]
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      s[0][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s[1][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 6; ++ks) {
+        const bf16x8 a = ks < 4 ? lds_b128(st + kb * 16 * 256 + kn_rd[ks]) : lds_b128(st + kb * 16 * 128 + kp_rd[ks - 4]);
+        s[0][kb] = mfma16x16x32(a, qf[0][ks], s[0][kb]);
+        s[1][kb] = mfma16x16x32(a, qf[1][ks], s[1][kb]);
+      }
     }
-    if (lse && grp == 0) lse[(b * n_heads + h) * seqlen + tq] = (m * scale_log2 + __log2f(ltot)) * kLn2;
+    // causal and length mask on the tiles that reach past this wave's first query
+    if (k0 + kPK - 1 > q0 || k0 + kPK > seqlen) {
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh) {
+        const int tq = q0 + 16 * qh + r;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int key = k0 + 16 * kb + 4 * grp + j;
+            if (key > tq || key >= seqlen) s[qh][kb][j] = -INFINITY;
+          }
+      }
+    }
+    bf16x8 pb[2][2];   // [query half][key group of 32]
+    bool any_up = false;
+    float alpha[2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      float mx = fmaxf(fmaxf(fmaxf(s[qh][0][0], s[qh][0][1]), fmaxf(s[qh][0][2], s[qh][0][3])),
+                       fmaxf(fmaxf(s[qh][1][0], s[qh][1][1]), fmaxf(s[qh][1][2], s[qh][1][3])));
+      mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[qh][2][0], s[qh][2][1]), fmaxf(s[qh][2][2], s[qh][2][3])),
+                           fmaxf(fmaxf(s[qh][3][0], s[qh][3][1]), fmaxf(s[qh][3][2], s[qh][3][3]))));
+      mx = max_over_rows(mx) * scale_log2;
+      // the reference moves only when the maximum grows by more than 8 (p <= 2^8 otherwise)
+      const bool up = mx > m[qh] + 8.f;
+      const float m_new = up ? mx : m[qh];
+      alpha[qh] = fast_exp2(m[qh] - m_new);   // 1 when the reference stays; 0 from -inf
+      any_up |= up;
+      m[qh] = m_new;
+      float p[16];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[kb * 4 + j] = fast_exp2(s[qh][kb][j] * scale_log2 - m_new);
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; e += 4) ps += (p[e] + p[e + 1]) + (p[e + 2] + p[e + 3]);
+      lsum[qh] = lsum[qh] * alpha[qh] + ps;
+      // k-group order of the 32-key groups: keys 4 grp + j (block 2g) then 16 + 4 grp + j (block 2g+1)
+      pb[qh][0] = bf16x8_from_f32(p);
+      pb[qh][1] = bf16x8_from_f32(p + 8);
+    }
+    if (__any(any_up)) {
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[qh][db] *= alpha[qh];
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 a = lds_b128(st + db * 16 * 128 + v_rd[ks]);
+        o[0][db] = mfma16x16x32(a, pb[0][ks], o[0][db]);
+        o[1][db] = mfma16x16x32(a, pb[1][ks], o[1][db]);
+      }
+  }
+
+#pragma unroll
+  for (int qh = 0; qh < 2; ++qh) {
+    const float ltot = sum_over_rows(lsum[qh]);
+    const int tq = q0 + 16 * qh + r;
+    if (tq < seqlen) {
+      const float inv = 1.f / ltot;
+      uint16_t* dst = out + ((b * seqlen + tq) * n_heads + h) * kVDim + grp * 4;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        uint2 u;
+        u.x = pack_bf16x2(o[qh][db][0] * inv, o[qh][db][1] * inv);
+        u.y = pack_bf16x2(o[qh][db][2] * inv, o[qh][db][3] * inv);
+        *reinterpret_cast<uint2*>(dst + db * 16) = u;
+      }
+      if (lse && grp == 0) lse[(b * n_heads + h) * seqlen + tq] = (m[qh] + __log2f(ltot)) * kLn2;
+    }
   }
 }
 
@@ -316,8 +410,13 @@ hipError_t launch_prefill(int n_heads, int batch, int seqlen, const uint16_t* q,
   const dim3 g1(static_cast<unsigned>((n_rows + EX_BT - 1) / EX_BT), n_heads * kKvRows / EX_BC);
   expand_kernel<<<g1, 256, 0, stream>>>(kv_latent, wkv_b, n_heads, seqlen, lay.t_pad, n_rows, knope, vt);
   mark(ev, 1, stream);
-  const dim3 g2(static_cast<unsigned>((seqlen + kQBlk - 1) / kQBlk), n_heads, batch);
-  attend_kernel<<<g2, 256, 0, stream>>>(q, knope, vt, k_pe, n_heads, seqlen, lay.t_pad, scale * kLog2e, out, lse);
+  {
+    // blocks of one (b, h) on one XCD: grid = 8 x ceil(B H / 8) x query blocks
+    const int64_t n_qb = (seqlen + kPQ - 1) / kPQ;
+    const int64_t n_bh8 = (static_cast<int64_t>(batch) * n_heads + 7) / 8;
+    attend_kernel<<<static_cast<unsigned>(8 * n_bh8 * n_qb), 256, 0, stream>>>(
+        q, knope, vt, k_pe, batch, n_heads, seqlen, lay.t_pad, scale * kLog2e, out, lse);
+  }
   mark(ev, 2, stream);
   return hipGetLastError();
 }
