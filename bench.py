@@ -12,10 +12,17 @@ The printed JSON line carries:
   value       whole-job decode throughput, cache-token.heads/s = H * sum(L_b) / step time
   roofline    the split-KV attention kernel (the dominant kernel): algorithmic bytes per launch
               (1152 B per cached token: 512 latent + 64 rotary bf16) / its mean duration, timed with
-              HIP events recorded on its own stream around that kernel, against 8 TB/s
+              HIP events recorded on its own stream around that kernel, against 8 TB/s; `traffic`
+              is the HBM bytes per launch measured by rocprofv3 (FETCH_SIZE + WRITE_SIZE, scaled by a
+              copy-kernel calibration) as committed under profiles/, or null when the kernel source
+              has changed since (checked by hash) or for another workload
   prefill     the DeepSeek-V3.2-shaped prefill (T = 4096, 128 heads): query path + expansion +
               causal attention, TFLOP/s of algorithmic flops against 2.5 PFLOP/s bf16
-  cpu_baseline the CPU oracle on a bounded sample of the same workload (whole batch, one pass)
+  cpu_baseline the CPU oracle on a bounded sample of the same workload (whole sequences, one at a
+              time, for about half of --cpu-budget seconds)
+
+    python bench.py --copy-calibration MIB   only runs a plain device copy of MIB MiB (for scaling
+                                             the rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
 """
 from __future__ import annotations
 
@@ -41,15 +48,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_kernel_hbm_traffic_dsv32_b32_l4096.txt")
+DECODE_SRC = os.path.join(ROOT, "head_latent_attention_fp32_amd", "csrc", "decode.hip")
+
+
 class HipEvents:
-    """Raw hipEvent_t handles (created up front, so the library can record them)."""
+    """Raw hipEvent_t handles (created up front, so the library can record them). They are created
+    without the system-scope fence on record, which otherwise adds microseconds to every stage."""
 
     def __init__(self, n):
         self.hip = ctypes.CDLL("libamdhip64.so")
         self.ev = (ctypes.c_void_p * n)()
         for i in range(n):
             h = ctypes.c_void_p()
-            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
+            assert self.hip.hipEventCreateWithFlags(ctypes.byref(h), ctypes.c_uint(HIP_EVENT_DISABLE_SYSTEM_FENCE)) == 0
             self.ev[i] = h.value
 
     def ptr(self, i):
@@ -202,6 +215,32 @@ def prefill_bench(args, torch, binding, S):
     }
 
 
+def measured_traffic():
+    """HBM bytes per launch of the attention kernel on this workload, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary -- None when decode.hip changed since it was taken."""
+    import hashlib
+    try:
+        fields = dict(l.split(":", 1) for l in open(TRAFFIC_FILE).read().splitlines() if ":" in l)
+        src = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+        if fields.get("decode_hip_sha256", "").strip() != src:
+            return None
+        return float(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch, mib):
+    """A plain device copy of known size (bytes read = bytes written = mib MiB), for scaling the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    n = mib << 20
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
 def cpu_baseline(case, d, budget_s):
     """The oracle (untuned) on the whole batch of the decode step: query path + decode."""
     from oracle import mla_oracle as O
@@ -214,23 +253,32 @@ def cpu_baseline(case, d, budget_s):
     except Exception:  # pragma: no cover
         ctl, used = None, os.cpu_count()
     H = case.n_heads
+    # passes over the batch, one sequence at a time, until about half the budget is spent (at least
+    # one sequence, at most the budget)
     t0 = time.perf_counter()
     n_seq = 0
     tokens = 0
-    for b in range(case.batch):
-        qo, _ = O.query_path(d["q_latent"][b:b + 1], d["gamma"], d["wq_b"], d["rope_cs"][b:b + 1], H)
-        r0, Lb = int(d["row_offset"][b]), int(d["lengths"][b])
-        O.decode_absorbed(qo[0], d["wkv_b"], d["kv_cache"][r0:r0 + Lb], d["pe_cache"][r0:r0 + Lb], 192 ** -0.5)
-        n_seq += 1
-        tokens += Lb
-        if time.perf_counter() - t0 > budget_s:
-            break
+    passes = 0
+    done = False
+    while not done:
+        for b in range(case.batch):
+            qo, _ = O.query_path(d["q_latent"][b:b + 1], d["gamma"], d["wq_b"], d["rope_cs"][b:b + 1], H)
+            r0, Lb = int(d["row_offset"][b]), int(d["lengths"][b])
+            O.decode_absorbed(qo[0], d["wkv_b"], d["kv_cache"][r0:r0 + Lb], d["pe_cache"][r0:r0 + Lb],
+                              192 ** -0.5)
+            n_seq += 1
+            tokens += Lb
+            if time.perf_counter() - t0 > budget_s:
+                done = True
+                break
+        passes += 1
+        done = done or time.perf_counter() - t0 > budget_s / 2
     dt = time.perf_counter() - t0
     if ctl is not None:
         ctl.unregister() if hasattr(ctl, "unregister") else None
     return {"value": H * tokens / dt, "unit": "cache-token·heads/s", "cores": int(used), "kind": "oracle",
-            "sample": f"{n_seq} of {case.batch} sequences of {case.name} (query path + absorbed decode, fp64 NumPy), "
-                      f"{dt:.1f} s"}
+            "sample": f"{n_seq} sequences ({passes} pass(es) over the {case.batch} of {case.name}; query path + "
+                      f"absorbed decode, fp64 NumPy, one sequence at a time), {dt:.1f} s"}
 
 
 def main():
@@ -243,6 +291,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -256,6 +306,9 @@ def main():
     from synth import inputs as S
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration)
+        return
     binding.lib()
 
     res, d = decode_bench(args, torch, binding, S)
@@ -285,8 +338,9 @@ def main():
         "stages_ms": res["stages_ms"],
         "roofline": {"bound": "hbm", "kernel": "split-KV attention (mla_decode stage 2)",
                      "achieved": res["attn_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": res["attn_gbps"] / HBM_PEAK_GBPS, "traffic": None,
-                     "bytes_per_launch": res["alg_cache"]},
+                     "frac": res["attn_gbps"] / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic() if case.name == "dsv32_decode_b32_l4096_h128" else None,
+                     "bytes_per_launch": res["alg_cache"], "attn_us": res["stages_ms"]["split_kv_attention"] * 1e3},
         "prefill": None if pre is None else {
             "workload": pre["workload"], "ms": pre["ms"], "tflops": pre["tflops"],
             "frac_of_bf16_peak": pre["tflops"] / BF16_PEAK_TFLOPS, "stages": pre["stages"]},
