@@ -102,6 +102,9 @@ def decode_bench(args, torch, binding, S):
     inv = torch.empty(B, dtype=torch.float32, device="cuda")
     out = torch.empty((B, H, 128), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    qws_bytes = binding.query_path_workspace_size(H, B)
+    qws = torch.empty(max(qws_bytes, 1), dtype=torch.uint8, device="cuda")
+    qws_ptr = qws.data_ptr() if qws_bytes else None
     stream = torch.cuda.current_stream().cuda_stream
     packed = case.layout == "packed"
     K, W = args.steps, args.warmup
@@ -114,7 +117,7 @@ def decode_bench(args, torch, binding, S):
         ed = evd.ptr(5 * (i - W)) if timed else None
         st = L.mla_query_path_ex(ctypes.byref(dims), B, s["q_latent"].data_ptr(), s["gamma"].data_ptr(),
                                  s["wq_b"].data_ptr(), s["rope_cs"].data_ptr(), q.data_ptr(), inv.data_ptr(),
-                                 stream, eq)
+                                 qws_ptr, qws_bytes, stream, eq)
         assert st == 0, st
         st = L.mla_decode_ex(ctypes.byref(dims), B, q.data_ptr(), s["wkv_b"].data_ptr(), s["kv"].data_ptr(),
                              s["pe"].data_ptr(), s["off"].data_ptr() if packed else None, s["lens"].data_ptr(),
@@ -175,6 +178,8 @@ def prefill_bench(args, torch, binding, S):
     q = torch.empty((B, T, H, 192), dtype=torch.bfloat16, device="cuda")
     inv = torch.empty(B * T, dtype=torch.float32, device="cuda")
     out = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device="cuda")
+    qws_bytes = binding.query_path_workspace_size(H, B * T)
+    qws = torch.empty(qws_bytes, dtype=torch.uint8, device="cuda")
     ws_bytes = binding.prefill_workspace_size(H, B, T)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
@@ -187,7 +192,8 @@ def prefill_bench(args, torch, binding, S):
         eq = evq.ptr(3 * (i - W)) if timed else None
         ep = evp.ptr(3 * (i - W)) if timed else None
         assert L.mla_query_path_ex(ctypes.byref(dims), B * T, xs.data_ptr(), g.data_ptr(), wq.data_ptr(),
-                                   cs.data_ptr(), q.data_ptr(), inv.data_ptr(), stream, eq) == 0
+                                   cs.data_ptr(), q.data_ptr(), inv.data_ptr(), qws.data_ptr(), qws_bytes,
+                                   stream, eq) == 0
         assert L.mla_prefill_ex(ctypes.byref(dims), B, T, q.data_ptr(), lat.data_ptr(), kpe.data_ptr(),
                                 wkv.data_ptr(), ws.data_ptr(), ws_bytes, out.data_ptr(), None, stream, ep) == 0
 

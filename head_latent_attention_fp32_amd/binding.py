@@ -51,12 +51,14 @@ def _lib():
         lib = ctypes.CDLL(LIB_PATH)
         dp = ctypes.POINTER(MlaDims)
         lib.mla_dims_default.argtypes = [_I32, dp]
-        lib.mla_query_path.argtypes = [dp, _I64, _P, _P, _P, _P, _P, _P, _P]
+        lib.mla_query_path_workspace_size.argtypes = [dp, _I64, ctypes.POINTER(_SZ)]
+        lib.mla_query_path.argtypes = [dp, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
         lib.mla_decode_workspace_size.argtypes = [dp, _I32, _I64, ctypes.POINTER(_SZ)]
         lib.mla_decode.argtypes = [dp, _I32, _P, _P, _P, _P, _P, _P, _I64, _P, _SZ, _P, _P, _P]
         lib.mla_prefill_workspace_size.argtypes = [dp, _I32, _I32, ctypes.POINTER(_SZ)]
         lib.mla_prefill.argtypes = [dp, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]
-        for f in ("mla_dims_default", "mla_query_path", "mla_decode_workspace_size", "mla_decode",
+        for f in ("mla_dims_default", "mla_query_path_workspace_size", "mla_query_path", "mla_decode_workspace_size",
+                  "mla_decode",
                   "mla_prefill_workspace_size", "mla_prefill"):
             getattr(lib, f).restype = ctypes.c_int
         lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -109,11 +111,21 @@ def _check(status: int, what: str) -> None:
         raise MlaError(status, what)
 
 
+def query_path_workspace_size(n_heads: int, n_tokens: int, d: Optional[MlaDims] = None) -> int:
+    d = d or dims(n_heads)
+    n = _SZ(0)
+    _check(_lib().mla_query_path_workspace_size(ctypes.byref(d), n_tokens, ctypes.byref(n)),
+           "mla_query_path_workspace_size")
+    return n.value
+
+
 def query_path(q_latent: torch.Tensor, q_norm_w: torch.Tensor, wq_b: torch.Tensor, rope_cs: torch.Tensor,
                n_heads: int, q_out: Optional[torch.Tensor] = None, inv_rms: Optional[torch.Tensor] = None,
-               d: Optional[MlaDims] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+               workspace: Optional[torch.Tensor] = None, d: Optional[MlaDims] = None
+               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """q_latent bf16 [n, 1536] (or [..., 1536]), q_norm_w fp32 [1536], wq_b bf16 [1536, H*192],
-    rope_cs fp32 [n, 32, 2] -> q_out bf16 [n, H, 192] (and inv_rms fp32 [n] if given)."""
+    rope_cs fp32 [n, 32, 2] -> q_out bf16 [n, H, 192] (and inv_rms fp32 [n] if given). The workspace
+    (uint8, needed above 32 tokens) is allocated when not given."""
     d = d or dims(n_heads)
     lead = tuple(q_latent.shape[:-1])
     n = 1
@@ -134,8 +146,14 @@ def query_path(q_latent: torch.Tensor, q_norm_w: torch.Tensor, wq_b: torch.Tenso
         _need(inv_rms, "inv_rms", torch.float32)
         if inv_rms.numel() != n:
             raise ValueError("inv_rms must hold one value per token")
+    ws_bytes = query_path_workspace_size(n_heads, n, d)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q_latent.device)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
     _check(_lib().mla_query_path(ctypes.byref(d), n, _ptr(q_latent), _ptr(q_norm_w), _ptr(wq_b), _ptr(rope_cs),
-                                 _ptr(q_out), _ptr(inv_rms), _stream()), "mla_query_path")
+                                 _ptr(q_out), _ptr(inv_rms), _ptr(workspace),
+                                 0 if workspace is None else workspace.numel(), _stream()), "mla_query_path")
     return q_out, inv_rms
 
 

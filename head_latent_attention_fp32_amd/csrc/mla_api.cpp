@@ -25,8 +25,9 @@ constexpr int64_t kMaxBatch = 1 << 24;
 // The longest decode cache: the attention kernel addresses the rows of a sequence, and one tile
 // past them, through buffer descriptors with 32-bit byte ranges (rows of 1 KiB).
 constexpr int64_t kMaxSeqlen = int64_t(1) << 21;
-// The largest query-path token count (grid y = ceil(n / 64) stays far below 2^31).
-constexpr int64_t kMaxTokens = int64_t(1) << 36;
+// The largest query-path token count: the product's grid has ceil(n / 128) blocks in y (at most
+// 65535).
+constexpr int64_t kMaxTokens = int64_t(65535) * 128;
 
 }  // namespace
 
@@ -45,26 +46,40 @@ mla_status_t mla_dims_default(int32_t n_heads, mla_dims_t* dims) {
   return check_dims(dims);
 }
 
+mla_status_t mla_query_path_workspace_size(const mla_dims_t* dims, int64_t n_tokens, size_t* bytes) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!bytes) return MLA_ERR_INVALID_ARG;
+  if (n_tokens < 0 || n_tokens > kMaxTokens) return MLA_ERR_SHAPE;
+  *bytes = mla::query_layout(n_tokens).total;
+  return MLA_OK;
+}
+
 mla_status_t mla_query_path_ex(const mla_dims_t* dims, int64_t n_tokens, const uint16_t* q_latent,
                                const float* q_norm_w, const uint16_t* wq_b, const float* rope_cs, uint16_t* q_out,
-                               float* inv_rms, hipStream_t stream, hipEvent_t* stage_events) {
+                               float* inv_rms, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                               hipEvent_t* stage_events) {
   mla_status_t st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (n_tokens < 0 || n_tokens > kMaxTokens) return MLA_ERR_SHAPE;
   if (n_tokens == 0) return MLA_OK;
   if (!q_latent || !q_norm_w || !wq_b || !rope_cs || !q_out) return MLA_ERR_INVALID_ARG;
+  const mla::QueryLayout lay = mla::query_layout(n_tokens);
+  if (lay.total > 0 && !workspace) return MLA_ERR_INVALID_ARG;
   if (!aligned16(q_latent) || !aligned16(q_norm_w) || !aligned16(wq_b) || !aligned16(rope_cs) ||
-      !aligned16(q_out) || (inv_rms && !aligned16(inv_rms)))
+      !aligned16(q_out) || (inv_rms && !aligned16(inv_rms)) || (workspace && !aligned16(workspace)))
     return MLA_ERR_ALIGNMENT;
+  if (workspace_bytes < lay.total) return MLA_ERR_WORKSPACE;
   hipError_t e = mla::launch_query_path(dims->n_heads, n_tokens, q_latent, q_norm_w, wq_b, rope_cs, q_out, inv_rms,
-                                        dims->rms_eps, stream, stage_events);
+                                        workspace, lay, dims->rms_eps, stream, stage_events);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 mla_status_t mla_query_path(const mla_dims_t* dims, int64_t n_tokens, const uint16_t* q_latent,
                             const float* q_norm_w, const uint16_t* wq_b, const float* rope_cs, uint16_t* q_out,
-                            float* inv_rms, hipStream_t stream) {
-  return mla_query_path_ex(dims, n_tokens, q_latent, q_norm_w, wq_b, rope_cs, q_out, inv_rms, stream, nullptr);
+                            float* inv_rms, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return mla_query_path_ex(dims, n_tokens, q_latent, q_norm_w, wq_b, rope_cs, q_out, inv_rms, workspace,
+                           workspace_bytes, stream, nullptr);
 }
 
 mla_status_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch, int64_t max_seqlen, size_t* bytes) {

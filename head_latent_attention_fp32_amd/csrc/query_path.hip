@@ -18,166 +18,65 @@ namespace mla {
 
 namespace {
 
-constexpr int BN = 64;    // weight columns per block
-constexpr int BM = 64;    // tokens per block
-constexpr int BK = 64;    // reduction slice per LDS stage
-constexpr int LDK = BK + 8;
+// ---------------------------------------------------------------------------------------------
+// Many tokens: the RMSNorm runs once per token, ahead of the product.
+// One wave per token: inv_rms = 1/sqrt(mean x^2 + eps) in fp32, then y = bf16(gain * (x * inv_rms))
+// (the rounding point of the RMSNorm excerpt) into the workspace, laid out as the LDS image of the
+// product's activation stages: [24 k-stages of 64][tiles of 128 tokens][128 rows][128 B], 16-byte
+// chunk c of row r at c ^ ((r >> 1) & 7). A stage of a block is then one contiguous run, loaded
+// 1 KB per instruction. Rows past the last token are written as zeros.
+// ---------------------------------------------------------------------------------------------
+constexpr int kYTile = 128;   // tokens per activation tile
 
-// inv_rms[m] = 1/sqrt(mean_k x[m,k]^2 + eps); one wave per token.
-__global__ __launch_bounds__(256) void row_stats_kernel(const uint16_t* __restrict__ x, int64_t n_tokens,
-                                                        float eps, float* __restrict__ inv_rms) {
+// Activation tiles: an even count, so that a block of 256 tokens never reads past the last one.
+__host__ __device__ inline int64_t y_tiles(int64_t n_tokens) { return (n_tokens + 2 * kYTile - 1) / (2 * kYTile) * 2; }
+
+__device__ __forceinline__ int64_t y_chunk_offset(int64_t m, int k, int64_t n_tiles) {
+  // element offset of the 8 activations k .. k+7 (k a multiple of 8) of token m
+  const int ks = k >> 6, c = (k >> 3) & 7;
+  const int r = static_cast<int>(m & (kYTile - 1));
+  return (((static_cast<int64_t>(ks) * n_tiles + (m >> 7)) * kYTile + r) * 64) + ((c ^ ((r >> 1) & 7)) << 3);
+}
+
+__global__ __launch_bounds__(256) void normalize_kernel(const uint16_t* __restrict__ x, const float* __restrict__ gamma,
+                                                        int64_t n_tokens, int64_t n_tiles, float eps,
+                                                        float* __restrict__ inv_rms, uint16_t* __restrict__ y) {
   const int64_t m = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (m >= n_tokens) return;
+  if (m >= n_tiles * kYTile) return;
+  constexpr int kPer = kQLora / (64 * 8);   // 3 chunks of 8 per lane
+  if (m >= n_tokens) {
+    const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) *reinterpret_cast<uint4*>(y + y_chunk_offset(m, (i * 64 + lane) * 8, n_tiles)) = z;
+    return;
+  }
   const uint16_t* row = x + m * kQLora;
+  bf16x8 v[kPer];
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < kQLora / (64 * 8); ++i) {
-    const uint4 v = ldg16(row + (i * 64 + lane) * 8);
+  for (int i = 0; i < kPer; ++i) {
+    v[i] = as_bf16x8(ldg16(row + (i * 64 + lane) * 8));
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float f = bf16_bits_to_f32(u4_elem(v, e));
+      const float f = static_cast<float>(v[i][e]);
       s += f * f;
     }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  if (lane == 0) inv_rms[m] = 1.f / sqrtf(s * (1.f / kQLora) + eps);
-}
-
-// FUSED: the block computes the statistics of its own BM tokens first (used when the tokens fit
-// one block column, i.e. decode); otherwise inv_rms was written by row_stats_kernel.
-template <bool FUSED>
-__global__ __launch_bounds__(256) void query_gemm_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ gamma, const uint16_t* __restrict__ wq_b,
-    const float* __restrict__ rope_cs, int64_t n_tokens, int n_cols, float eps,
-    float* __restrict__ inv_rms, uint16_t* __restrict__ q_out) {
-  __shared__ __attribute__((aligned(16))) uint16_t ws[BN * LDK];   // [n][k]
-  __shared__ __attribute__((aligned(16))) uint16_t ys[BM * LDK];   // [m][k]
-  __shared__ float rinv[BM];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = lane & 15, grp = lane >> 4;
-  const int n0 = blockIdx.x * BN;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
-
-  if (FUSED) {
-    // wave w: tokens m0 + w, m0 + w + 4, ...
-    for (int mi = wave; mi < BM; mi += 4) {
-      if (m0 + mi >= n_tokens) {
-        if (lane == 0) rinv[mi] = 0.f;
-        continue;
-      }
-      const int64_t m = m0 + mi;
-      const uint16_t* row = x + m * kQLora;
-      float s = 0.f;
+  const float iv = 1.f / sqrtf(s * (1.f / kQLora) + eps);
+  if (lane == 0) inv_rms[m] = iv;
 #pragma unroll
-      for (int i = 0; i < kQLora / 512; ++i) {
-        const uint4 v = ldg16(row + (i * 64 + lane) * 8);
+  for (int i = 0; i < kPer; ++i) {
+    const int k = (i * 64 + lane) * 8;
+    const float4 g0 = *reinterpret_cast<const float4*>(gamma + k);
+    const float4 g1 = *reinterpret_cast<const float4*>(gamma + k + 4);
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    float o[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float f = bf16_bits_to_f32(u4_elem(v, e));
-          s += f * f;
-        }
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-      const float iv = 1.f / sqrtf(s * (1.f / kQLora) + eps);
-      if (lane == 0) {
-        rinv[mi] = iv;
-        if (inv_rms && blockIdx.x == 0 && m0 + mi < n_tokens) inv_rms[m0 + mi] = iv;
-      }
-    }
-  } else {
-    if (tid < BM) rinv[tid] = inv_rms[min(m0 + tid, n_tokens - 1)];
-  }
-
-  // Per-thread load assignment: 2 weight chunks (8 n of one k) and 2 activation chunks (8 k of one m).
-  uint4 wreg[2], xreg[2];
-  auto fetch = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + 256 * i;
-      const int kk = idx >> 3, nch = idx & 7;
-      wreg[i] = ldg16(wq_b + static_cast<int64_t>(k0 + kk) * n_cols + n0 + nch * 8);
-      const int mm = idx >> 3, kch = idx & 7;
-      xreg[i] = ldg16(x + min(m0 + mm, n_tokens - 1) * kQLora + k0 + kch * 8);
-    }
-  };
-  auto stash = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + 256 * i;
-      const int kk = idx >> 3, nch = idx & 7;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ws[(nch * 8 + e) * LDK + kk] = u4_elem(wreg[i], e);
-      const int mm = idx >> 3, kch = idx & 7;
-      const float sc = rinv[mm];
-      float y[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        y[e] = gamma[k0 + kch * 8 + e] * (bf16_bits_to_f32(u4_elem(xreg[i], e)) * sc);
-      *reinterpret_cast<bf16x8*>(&ys[mm * LDK + kch * 8]) = bf16x8_from_f32(y);
-    }
-  };
-
-  // wave (wn, wm) computes weight columns wn*32 .. +32 x tokens wm*32 .. +32.
-  const int wn = wave >> 1, wm = wave & 1;
-  f32x4 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  fetch(0);
-  __syncthreads();   // rinv visible
-  for (int k0 = 0; k0 < kQLora; k0 += BK) {
-    __syncthreads();
-    stash(k0);
-    __syncthreads();
-    if (k0 + BK < kQLora) fetch(k0 + BK);
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      bf16x8 a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(&ws[(wn * 32 + i * 16 + r) * LDK + kk + grp * 8]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(&ys[(wm * 32 + j * 16 + r) * LDK + kk + grp * 8]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
-    }
-  }
-
-  // Epilogue: lane holds q[m][n .. n+3], m = m0 + wm*32 + j*16 + r, n = n0 + wn*32 + i*16 + 4*grp.
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int64_t m = m0 + wm * 32 + j * 16 + r;
-    if (m >= n_tokens) continue;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int n = n0 + wn * 32 + i * 16 + grp * 4;
-      const int hd = n % kQk;
-      float v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = round_bf16(acc[i][j][e]);   // bf16 Linear output
-      if (hd >= kNope) {
-        const int pair = (hd - kNope) >> 1;
-        const float4 cs = *reinterpret_cast<const float4*>(rope_cs + (m * (kRope / 2) + pair) * 2);
-        const float a0 = v[0], b0 = v[1], a1 = v[2], b1 = v[3];
-        v[0] = a0 * cs.x - b0 * cs.y;
-        v[1] = a0 * cs.y + b0 * cs.x;
-        v[2] = a1 * cs.z - b1 * cs.w;
-        v[3] = a1 * cs.w + b1 * cs.z;
-      }
-      uint2 u;
-      u.x = pack_bf16x2(v[0], v[1]);
-      u.y = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<uint2*>(q_out + m * n_cols + n) = u;
-    }
+    for (int e = 0; e < 8; ++e) o[e] = g[e] * (static_cast<float>(v[i][e]) * iv);
+    *reinterpret_cast<bf16x8*>(y + y_chunk_offset(m, k, n_tiles)) = bf16x8_from_f32(o);
   }
 }
 
@@ -429,14 +328,179 @@ __global__ __launch_bounds__(256, 1) void query_gemm_small_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Many tokens (prefill): large-tile MFMA GEMM on the normalised activation y (normalize_kernel),
+// q^T = W^T . y^T per block tile of BN output columns x BM tokens, 4 waves as 2 x 2, each wave
+// (BN/2) x (BM/2). The W operand (the transposing read, half the LDS rate of a plain read) is reused
+// across the wave's BM/32 token blocks. K advances 64 at a time through three LDS stages (two in flight), filled
+// by direct-to-LDS loads, so the main loop holds no conversion work:
+//   W stage [64 k][BN] bf16: 32-byte column group g of row k at g ^ f(k), f(k) = (k & 3) |
+//     ((k >> 1) & 4), so the 8 rows of a half-wave's transposing read (ds_read_b64_tr_b16: 16
+//     columns x 8 consecutive k, the A operand) hit 8 distinct 32-byte bank groups;
+//   Y stage [BM tokens][64 k] bf16: 16-byte chunk c of row m at c ^ ((m >> 1) & 7).
+// The epilogue rounds the Linear output to bf16 and rotates the rotary pairs in registers.
+// ---------------------------------------------------------------------------------------------
+constexpr int kBigStages = 3;   // LDS stages of 64 k; two in flight ahead of the one in use
+
+template <int BN, int BM>
+struct BigTile {
+  static constexpr int kWN = BN / 2 / 16;            // n-blocks per wave
+  static constexpr int kWM = BM / 2 / 16;            // m-blocks per wave
+  static constexpr int kWBytes = 64 * BN * 2;        // W stage
+  static constexpr int kYBytes = BM * 64 * 2;        // Y stage
+  static constexpr int kWLoads = kWBytes / 1024 / 4; // direct-to-LDS loads per wave per stage
+  static constexpr int kYLoads = kYBytes / 1024 / 4;
+};
+
+__device__ __forceinline__ int wswz(int k) { return (k & 3) | ((k >> 1) & 4); }
+
+template <int BN, int BM>
+__global__ __launch_bounds__(256, 1) void query_gemm_big_kernel(
+    const uint16_t* __restrict__ y, const uint16_t* __restrict__ wq_b, const float* __restrict__ rope_cs,
+    int64_t n_tokens, int n_cols, uint16_t* __restrict__ q_out) {
+  using T = BigTile<BN, BM>;
+  __shared__ __attribute__((aligned(1024))) uint8_t wst[kBigStages][T::kWBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t yst[kBigStages][T::kYBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, grp = lane >> 4;
+  const int wn = wave >> 1, wm = wave & 1;
+  const int n0 = blockIdx.x * BN;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
+
+  // W loads: stage rows k0 .. k0+63, columns n0 .. n0+BN-1 of wq_b (row pitch n_cols); load li
+  // covers 1 KB = 1024 / (2 BN) rows; lane l -> row, physical 16-byte chunk.
+  constexpr int kRowChunks = BN * 2 / 16;
+  constexpr int kRowsPerLoad = 1024 / (BN * 2);
+  uint32_t w_voff[T::kWLoads];
+#pragma unroll
+  for (int e = 0; e < T::kWLoads; ++e) {
+    const int li = wave + 4 * e;
+    const int row = li * kRowsPerLoad + lane / kRowChunks;
+    const int pc = lane % kRowChunks;
+    const int lc = (((pc >> 1) ^ wswz(row)) << 1) | (pc & 1);
+    w_voff[e] = static_cast<uint32_t>(row * n_cols * 2 + lc * 16);
+  }
+  // Y loads: the block's BM tokens of a stage are BM / 128 consecutive tiles of the workspace
+  // (already in LDS order): contiguous 1 KB loads.
+  const int64_t n_tiles = y_tiles(n_tokens);
+  const uint16_t* y_blk = y + (m0 / kYTile) * kYTile * 64;   // stage 0 of this block's first tile
+  const uint32_t y_stage_pitch = static_cast<uint32_t>(n_tiles * kYTile * 128);   // bytes per k-stage
+  const uint32_t y_bytes = y_stage_pitch * (kQLora / 64) - static_cast<uint32_t>(m0 / kYTile) * kYTile * 128;
+  const uint32_t w_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)&wst[0][0]));
+  const uint32_t y_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)&yst[0][0]));
+  auto issue = [&](int kt) {
+    // descriptors rebuilt per stage (scalar work): kept short-lived, they stay in SGPRs
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(wq_b + n0, static_cast<uint32_t>(kQLora) * n_cols * 2u);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(y_blk, y_bytes);
+    const uint32_t wk = static_cast<uint32_t>(kt) * 64u * n_cols * 2u;
+    const uint32_t yk = static_cast<uint32_t>(kt) * y_stage_pitch;
+#pragma unroll
+    for (int e = 0; e < T::kWLoads; ++e)
+      dma16(rw, w_lds + (kt % kBigStages) * T::kWBytes + (wave + 4 * e) * 1024, w_voff[e] + wk);
+#pragma unroll
+    for (int e = 0; e < T::kYLoads; ++e)
+      dma16(ry, y_lds + (kt % kBigStages) * T::kYBytes + (wave + 4 * e) * 1024, yk + (wave + 4 * e) * 1024 + lane * 16);
+  };
+
+  // Operand offsets. A (W^T, n-block nb of the wave, k rows 8 grp + 4 h .. +3 of k-step ks):
+  // source lane j of a 16-lane group reads row 32 ks + 8 grp + 4 h + j/4 at columns
+  // 16 (wn kWN + nb) + 4 (j%4) .. +3. B (y, m-block mb): row 16 (wm kWM + mb) + r, chunk 4 ks + grp.
+  int b_off[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int row = wm * (BM / 2) + r;                  // + 16 mb leaves (row >> 1) & 7 unchanged
+    b_off[ks] = row * 128 + (((4 * ks + grp) ^ ((row >> 1) & 7)) << 4);
+  }
+
+  f32x4 acc[T::kWN][T::kWM];
+#pragma unroll
+  for (int i = 0; i < T::kWN; ++i)
+#pragma unroll
+    for (int j = 0; j < T::kWM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int n_kt = kQLora / 64;   // 24
+  constexpr int kLoads = T::kWLoads + T::kYLoads;
+  issue(0);
+  issue(1);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    // this wave's loads of stage kt (those of kt+1 may stay in flight)
+    if (kt + 1 < n_kt) wait_vm<kLoads>();
+    else wait_vm<0>();
+    __syncthreads();         // everyone's; the stage of kt-1 is free
+    if (kt + 2 < n_kt) issue(kt + 2);
+    const uint8_t* wb = &wst[kt % kBigStages][0];
+    const uint8_t* yb = &yst[kt % kBigStages][0];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 af[T::kWN], bfm[T::kWM];
+#pragma unroll
+      for (int nb = 0; nb < T::kWN; ++nb) {
+        const int g = wn * T::kWN + nb;                   // 32-byte column group
+        i16x4 half[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int row = 32 * ks + 8 * grp + 4 * h + (r >> 2);
+          const int byte = row * (BN * 2) + ((g ^ wswz(row)) << 5) + 8 * (r & 3);
+          half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(wb + byte));
+        }
+        af[nb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int mb = 0; mb < T::kWM; ++mb) bfm[mb] = *reinterpret_cast<const bf16x8*>(yb + b_off[ks] + mb * 16 * 128);
+#pragma unroll
+      for (int nb = 0; nb < T::kWN; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < T::kWM; ++mb) acc[nb][mb] = mfma16x16x32(af[nb], bfm[mb], acc[nb][mb]);
+    }
+  }
+
+  // lane holds q[m][n .. n+3], m = m0 + wm BM/2 + 16 mb + r, n = n0 + wn BN/2 + 16 nb + 4 grp
+#pragma unroll
+  for (int mb = 0; mb < T::kWM; ++mb) {
+    const int64_t m = m0 + wm * (BM / 2) + 16 * mb + r;
+    if (m >= n_tokens) continue;
+#pragma unroll
+    for (int nb = 0; nb < T::kWN; ++nb) {
+      const int n = n0 + wn * (BN / 2) + 16 * nb + 4 * grp;
+      const int hd = n % kQk;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = round_bf16(acc[nb][mb][e]);   // bf16 Linear output
+      if (hd >= kNope) {
+        const int pair = (hd - kNope) >> 1;
+        const float4 cs = *reinterpret_cast<const float4*>(rope_cs + (m * (kRope / 2) + pair) * 2);
+        const float a0 = v[0], b0 = v[1], a1 = v[2], b1 = v[3];
+        v[0] = a0 * cs.x - b0 * cs.y;
+        v[1] = a0 * cs.y + b0 * cs.x;
+        v[2] = a1 * cs.z - b1 * cs.w;
+        v[3] = a1 * cs.w + b1 * cs.z;
+      }
+      uint2 u;
+      u.x = pack_bf16x2(v[0], v[1]);
+      u.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(q_out + m * n_cols + n) = u;
+    }
+  }
+}
+
 }  // namespace
+
+QueryLayout query_layout(int64_t n_tokens) {
+  QueryLayout L{};
+  if (n_tokens <= kSmallM) return L;
+  const int64_t n_pad = y_tiles(n_tokens) * kYTile;
+  L.y_off = 0;
+  L.inv_off = align_up(static_cast<size_t>(n_pad) * kQLora * sizeof(uint16_t));
+  L.total = align_up(L.inv_off + static_cast<size_t>(n_tokens) * sizeof(float));
+  return L;
+}
 
 hipError_t launch_query_path(int n_heads, int64_t n_tokens, const uint16_t* q_latent, const float* gamma,
                              const uint16_t* wq_b, const float* rope_cs, uint16_t* q_out, float* inv_rms,
-                             float eps, hipStream_t stream, hipEvent_t* ev) {
+                             void* workspace, const QueryLayout& lay, float eps, hipStream_t stream, hipEvent_t* ev) {
   const int n_cols = n_heads * kQk;
-  const int64_t m_blocks = (n_tokens + BM - 1) / BM;
-  const dim3 grid(n_cols / BN, static_cast<unsigned>(m_blocks));
   mark(ev, 0, stream);
   if (n_tokens <= kSmallM) {
     // one block per CU (at most one per slice); a multiple of 8 so that every XCD has blocks
@@ -445,15 +509,21 @@ hipError_t launch_query_path(int n_heads, int64_t n_tokens, const uint16_t* q_la
     mark(ev, 1, stream);
     query_gemm_small_kernel<<<grid, 256, 0, stream>>>(q_latent, gamma, wq_b, rope_cs, static_cast<int>(n_tokens),
                                                       n_cols, eps, inv_rms, q_out);
-  } else if (m_blocks == 1 || inv_rms == nullptr) {
-    mark(ev, 1, stream);
-    query_gemm_kernel<true><<<grid, 256, 0, stream>>>(q_latent, gamma, wq_b, rope_cs, n_tokens, n_cols, eps,
-                                                      inv_rms, q_out);
   } else {
-    row_stats_kernel<<<static_cast<unsigned>((n_tokens + 3) / 4), 256, 0, stream>>>(q_latent, n_tokens, eps, inv_rms);
+    char* ws = static_cast<char*>(workspace);
+    uint16_t* y = reinterpret_cast<uint16_t*>(ws + lay.y_off);
+    float* inv = inv_rms ? inv_rms : reinterpret_cast<float*>(ws + lay.inv_off);
+    const int64_t n_tiles = y_tiles(n_tokens);
+    normalize_kernel<<<static_cast<unsigned>(n_tiles * kYTile / 4), 256, 0, stream>>>(q_latent, gamma, n_tokens, n_tiles,
+                                                                                     eps, inv, y);
     mark(ev, 1, stream);
-    query_gemm_kernel<false><<<grid, 256, 0, stream>>>(q_latent, gamma, wq_b, rope_cs, n_tokens, n_cols, eps,
-                                                       inv_rms, q_out);
+    if (n_tokens >= 1024) {
+      const dim3 grid(n_cols / 128, static_cast<unsigned>((n_tokens + 255) / 256));
+      query_gemm_big_kernel<128, 256><<<grid, 256, 0, stream>>>(y, wq_b, rope_cs, n_tokens, n_cols, q_out);
+    } else {
+      const dim3 grid(n_cols / 128, static_cast<unsigned>((n_tokens + 127) / 128));
+      query_gemm_big_kernel<128, 128><<<grid, 256, 0, stream>>>(y, wq_b, rope_cs, n_tokens, n_cols, q_out);
+    }
   }
   mark(ev, 2, stream);
   return hipGetLastError();

@@ -73,8 +73,14 @@ typedef struct {
 /* Fill *dims with the pages' widths for n_heads heads, scale 192^-0.5 and eps 1e-6. */
 mla_status_t mla_dims_default(int32_t n_heads, mla_dims_t* dims);
 
+/* Bytes of device workspace mla_query_path needs for n_tokens tokens: 0 for n_tokens <= 32 (the
+ * decode sizes), n_tokens * (1536 * 2 + 4) rounded up to 256-byte pieces otherwise (the normalised
+ * activation and the row statistics). Host-only; no HIP call. */
+mla_status_t mla_query_path_workspace_size(const mla_dims_t* dims, int64_t n_tokens, size_t* bytes);
+
 /* Query path ("DeepSeek-V3.2-Exp · Query heads": q^C = c^Q W_UQ, q^pe = c^Q W_QR,
  * Q^R = RoPE(Q^pe, R), Q = [Q^C; Q^R]; c^Q = RMSNorm(q latent) per "DeepSeek V4.1 · Query RMSNorm").
+ *   n_tokens  0 .. 8,388,480
  *   q_latent  bf16 [n_tokens, q_lora_rank]           query latent (output of wq_a)
  *   q_norm_w  fp32 [q_lora_rank]                      RMSNorm gain
  *   wq_b      bf16 [q_lora_rank, n_heads*192]         input x output; head h owns columns
@@ -82,14 +88,17 @@ mla_status_t mla_dims_default(int32_t n_heads, mla_dims_t* dims);
  *   rope_cs   fp32 [n_tokens, 32, 2]                  R row of each token: (cos, sin) of each pair
  *   q_out     bf16 [n_tokens, n_heads, 192]           token-major query heads
  *   inv_rms   fp32 [n_tokens] or NULL                 1/sqrt(mean(x^2) + eps) of each token
+ *   workspace >= mla_query_path_workspace_size bytes; may be NULL when that size is 0
  * Arithmetic: inv_rms in fp32; y = bf16(gain * x * inv_rms) (rounded before the product, as the
  * RMSNorm excerpt casts back to the input dtype); q = bf16(y @ wq_b) with fp32 accumulation; rotary
  * pairs (2i, 2i+1) of each head rotate as (a,b) -> (a cos - b sin, a sin + b cos) from the bf16
- * product and are rounded to bf16 again. */
+ * product and are rounded to bf16 again.
+ * Errors: MLA_ERR_WORKSPACE when workspace_bytes is below the size query; MLA_ERR_INVALID_ARG for a
+ * NULL workspace when one is needed. */
 mla_status_t mla_query_path(const mla_dims_t* dims, int64_t n_tokens,
                             const uint16_t* q_latent, const float* q_norm_w, const uint16_t* wq_b,
                             const float* rope_cs, uint16_t* q_out, float* inv_rms,
-                            hipStream_t stream);
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of device workspace mla_decode needs for `batch` sequences of at most max_seqlen cached
  * rows each. Host-only; no HIP call. */
@@ -145,12 +154,14 @@ mla_status_t mla_prefill(const mla_dims_t* dims, int32_t batch, int32_t seqlen, 
  * at the boundaries of the library's kernel stages, so a caller can time each stage on the stream
  * it runs on. stage_events is NULL or an array of (number of stages + 1) events, any of which may be
  * NULL: event i is recorded before stage i and the last after the final stage.
- *   mla_query_path_ex: 2 stages (row statistics -- empty when fused into the product --, product + RoPE)
+ *   mla_query_path_ex: 2 stages (RMSNorm pass -- empty when fused into the product, 32 tokens or
+ *                      fewer --, product + RoPE)
  *   mla_decode_ex:     4 stages (absorb + run plan, split-KV attention, log-sum-exp combine, value projection)
  *   mla_prefill_ex:    2 stages (latent expansion, causal attention) */
 mla_status_t mla_query_path_ex(const mla_dims_t* dims, int64_t n_tokens,
                                const uint16_t* q_latent, const float* q_norm_w, const uint16_t* wq_b,
                                const float* rope_cs, uint16_t* q_out, float* inv_rms,
+                               void* workspace, size_t workspace_bytes,
                                hipStream_t stream, hipEvent_t* stage_events);
 mla_status_t mla_decode_ex(const mla_dims_t* dims, int32_t batch, const uint16_t* q, const uint16_t* wkv_b,
                            const uint16_t* kv_cache, const uint16_t* pe_cache,

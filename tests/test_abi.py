@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_three_entry_points():
     names = declared_functions()
-    for f in ("mla_query_path", "mla_decode", "mla_prefill", "mla_decode_workspace_size",
+    for f in ("mla_query_path", "mla_query_path_workspace_size", "mla_decode", "mla_prefill",
+              "mla_decode_workspace_size",
               "mla_prefill_workspace_size", "mla_status_string"):
         assert f in names
 
@@ -57,22 +58,40 @@ FAKE = 0x10000          # 16-byte aligned, never dereferenced
 MIS = 0x10002           # misaligned
 
 
+def test_query_path_workspace_size():
+    lib = _lib()
+    d = _dims()
+    n = ctypes.c_size_t(7)
+    assert lib.mla_query_path_workspace_size(ctypes.byref(d), 32, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.mla_query_path_workspace_size(ctypes.byref(d), 33, ctypes.byref(n)) == 0
+    assert n.value >= 33 * (1536 * 2 + 4) and n.value % 256 == 0
+    assert lib.mla_query_path_workspace_size(ctypes.byref(d), -1, ctypes.byref(n)) == 3
+    assert lib.mla_query_path_workspace_size(ctypes.byref(d), 65535 * 128 + 1, ctypes.byref(n)) == 3
+    assert lib.mla_query_path_workspace_size(ctypes.byref(d), 4, None) == 1
+
+
 def test_query_path_validation():
     lib = _lib()
     d = _dims()
     q = lib.mla_query_path
-    assert q(None, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 1
-    assert q(ctypes.byref(d), -1, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 3
-    assert q(ctypes.byref(d), 0, None, None, None, None, None, None, None) == 0       # nothing to do
-    assert q(ctypes.byref(d), 4, None, FAKE, FAKE, FAKE, FAKE, None, None) == 1
-    assert q(ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, MIS, None, None) == 4
-    assert q(ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, FAKE, MIS, None) == 4
+    assert q(None, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 1
+    assert q(ctypes.byref(d), -1, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 3
+    assert q(ctypes.byref(d), 0, None, None, None, None, None, None, None, 0, None) == 0       # nothing to do
+    assert q(ctypes.byref(d), 4, None, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 1
+    assert q(ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, MIS, None, None, 0, None) == 4
+    assert q(ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, FAKE, MIS, None, 0, None) == 4
     d2 = _dims()
     d2.q_lora_rank = 1024
-    assert q(ctypes.byref(d2), 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 2
+    assert q(ctypes.byref(d2), 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 2
     d3 = _dims()
     d3.softmax_scale = float("nan")
-    assert q(ctypes.byref(d3), 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 1
+    assert q(ctypes.byref(d3), 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 1
+    # above 32 tokens a workspace is required and checked
+    n = ctypes.c_size_t(0)
+    assert lib.mla_query_path_workspace_size(ctypes.byref(d), 100, ctypes.byref(n)) == 0
+    assert q(ctypes.byref(d), 100, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 1
+    assert q(ctypes.byref(d), 100, FAKE, FAKE, FAKE, FAKE, FAKE, None, MIS, n.value, None) == 4
+    assert q(ctypes.byref(d), 100, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, n.value - 1, None) == 5
 
 
 def test_decode_validation_and_workspace():
