@@ -24,6 +24,10 @@ Sources (page title -- section):
         MLA __init__ and query code excerpts
   [AU]  "DeepSeek-V3.2-Exp · Attention update" -- RMSNorm excerpt, mla-decode (MQA decode) excerpt
   [VS]  "Kimi-K2 · value_states" -- shapes, Parameters, mla-init and mla-prefill excerpts
+  The same pages also fix the steps next to the path: the key/value side of new tokens (wkv_a
+  split, kv_norm, rotary key) and the cache rows they fill ([QH], [VS], [AU]); the top-k index mask
+  of V3.2 decode ([AU] mla-decode); prefill of new queries over cached keys ([VS] mla-prefill);
+  the output projection wo ([AU] mla-output, attention-update shape).
 
 Readings taken where the pages are silent (each also listed in the design notes):
   * RoPE pairs are adjacent, interleaved features (2i, 2i+1) of the 64 rotary features: the V3.2
@@ -34,7 +38,12 @@ Readings taken where the pages are silent (each also listed in the design notes)
   * softmax scale = 192^-0.5 ([QH], MLA __init__), without the long-context mscale correction.
   * decode attends exactly the L_b cached rows it is given; L_b = 0 gives out = 0, lse = -inf.
   * lse is the natural log of the sum over attended positions of exp(scaled score).
-  * prefill starts at position 0 and keeps key t' for query t iff t' <= t.
+  * prefill keeps key t' for query t iff t' <= t; with a cached prefix of S - Tq keys, query i is
+    position S - Tq + i.
+  * wkv_a's 576 outputs are [latent 512 | rotary key 64] in that order (the order of the sum in its
+    width); the rotary key is rotated like q_pe.
+  * a top-k entry outside [0, L) names no position; an empty selection gives out = 0, lse = -inf.
+  * wo is stored [dim, H*128] (torch Linear orientation) and y = x W^T.
 
 Parity unpinned: the RoPE pairing/sign convention itself (the pages never show the rotation's body);
 the oracle's rotation is pinned only to its own reading (identity at position 0, norm preservation,
@@ -333,19 +342,22 @@ def expand_latent(kv_latent_bits, wkv_b_bits, n_heads: int, staged: bool = True,
     return _maybe_round(k, staged), _maybe_round(v, staged)
 
 
-def prefill_head(q_h, k_nope_h, v_h, k_pe, scale: float, rows: Optional[Sequence[int]] = None
-                 ) -> Tuple[np.ndarray, np.ndarray]:
+def prefill_head(q_h, k_nope_h, v_h, k_pe, scale: float, rows: Optional[Sequence[int]] = None,
+                 q_offset: int = 0) -> Tuple[np.ndarray, np.ndarray]:
     """[VS] mla-prefill for one head: key_states = [k_nope ; k_pe] (k_pe shared by all heads),
     S = scale Q K^T, add the causal mask (0 where t' <= t, -inf after), softmax in float64,
-    O = P V. q_h [T, 192], k_nope_h [T, 128], v_h [T, 128], k_pe [T, 64] (fp64 values).
+    O = P V. Query row i sits at position t = q_offset + i (q_offset > 0: the queries are the
+    last rows of a longer sequence whose earlier keys are cached). q_h [Tq, 192],
+    k_nope_h / v_h [>= t+1, 128], k_pe [>= t+1, 64] (fp64 values).
     Returns (O [n, 128], lse [n]) for the listed query rows (all rows by default)."""
-    T = q_h.shape[0]
-    rows = list(range(T)) if rows is None else list(rows)
-    k = np.concatenate([k_nope_h, k_pe], axis=1)                      # [T, 192]
+    Tq = q_h.shape[0]
+    rows = list(range(Tq)) if rows is None else list(rows)
+    k = np.concatenate([k_nope_h, k_pe], axis=1)                      # [S, 192]
     O = np.empty((len(rows), V_DIM))
     lse = np.empty(len(rows))
-    for i, t in enumerate(rows):
-        s = scale * (k[: t + 1] @ q_h[t])                              # keys 0..t only
+    for i, r in enumerate(rows):
+        t = q_offset + r
+        s = scale * (k[: t + 1] @ q_h[r])                              # keys 0..t only
         m = s.max()
         p = np.exp(s - m)
         O[i] = (p @ v_h[: t + 1]) / p.sum()
@@ -356,23 +368,133 @@ def prefill_head(q_h, k_nope_h, v_h, k_pe, scale: float, rows: Optional[Sequence
 def prefill_causal(q, kv_latent_bits, k_pe_bits, wkv_b_bits, scale: float, staged: bool = True,
                    heads: Optional[Sequence[int]] = None, rows: Optional[Sequence[int]] = None,
                    round_output: bool = True) -> Tuple[np.ndarray, np.ndarray]:
-    """Causal non-absorbed prefill of one sequence. q [T, H, 192] fp64 values.
+    """Causal non-absorbed prefill of one sequence. q [Tq, H, 192] fp64 values; the latent and
+    rotary key cover S >= Tq positions (S = Tq: the plain prefill from position 0; S > Tq: the
+    queries are the last Tq positions, the first S - Tq keys a cached prefix -- [VS] mla-prefill,
+    whose weights and mask are sized (q_len, kv_seq_len) once past keys join the new ones).
     Returns (out [n_rows, n_heads_sel, 128] -- bf16-valued when staged and round_output,
     lse [n_heads_sel, n_rows])."""
     q = np.asarray(q, np.float64)
-    T, H, _ = q.shape
+    Tq, H, _ = q.shape
+    S = np.asarray(kv_latent_bits).shape[0]
+    if S < Tq:
+        raise ValueError("fewer key positions than queries")
+    off = S - Tq
     heads = list(range(H)) if heads is None else list(heads)
-    rows = list(range(T)) if rows is None else list(rows)
-    need = max(rows) + 1 if rows else 0
+    rows = list(range(Tq)) if rows is None else list(rows)
+    need = off + max(rows) + 1 if rows else 0
     pe = bf16_decode(k_pe_bits[:need])
     out = np.empty((len(rows), len(heads), V_DIM))
     lse = np.empty((len(heads), len(rows)))
     for j, h in enumerate(heads):
         k_h, v_h = expand_latent(kv_latent_bits[:need], wkv_b_bits, H, staged, heads=[h])
-        o, l = prefill_head(q[:need, h, :], k_h[:, 0, :], v_h[:, 0, :], pe, scale, rows)
+        o, l = prefill_head(q[:, h, :], k_h[:, 0, :], v_h[:, 0, :], pe, scale, rows, q_offset=off)
         out[:, j, :] = o
         lse[j] = l
     return _maybe_round(out, staged and round_output), lse
+
+
+# ---------------------------------------------------------------------------------------------
+# Key/value side of new tokens and the cache write
+# ---------------------------------------------------------------------------------------------
+def kv_side(kv_a_bits, kv_gamma, rope_cs, eps: float = 1e-6, staged: bool = True) -> Tuple[np.ndarray, np.ndarray]:
+    """[QH] MLA __init__ / [VS] mla-init: the joint down-projection wkv_a gives each token
+    kv_lora + rope = 576 features. The first 512 are the latent, normalised by kv_norm (an RMSNorm
+    of width 512 with its own gain, [QN] equation); the last 64 are the rotary key shared by every
+    head, rotated at the token's position with the same pairing as q_pe ([VS] mla-prefill rotates
+    q_pe and k_pe together).
+    kv_a_bits bf16 [n, 576]; kv_gamma fp32 [512]; rope_cs fp32 [n, 32, 2].
+    Returns (latent [n, 512], k_pe [n, 64]) -- bf16-valued when staged: what the caches hold."""
+    a = bf16_decode(kv_a_bits)
+    lat, _ = rms_norm(a[:, :KV_LORA], kv_gamma, eps)
+    pe = rope_rotate(a[:, KV_LORA:], np.asarray(rope_cs, np.float64))
+    return _maybe_round(lat, staged), _maybe_round(pe, staged)
+
+
+def cache_append(kv_cache_bits, pe_cache_bits, row_offset, start_pos, latent_bits, k_pe_bits,
+                 max_seqlen: int) -> Tuple[np.ndarray, np.ndarray]:
+    """[AU] mla-decode reads kv_cache[:bsz, :end_pos] and pe_cache[:bsz, :end_pos]: the cache rows
+    of a sequence are its positions in order. New token t of sequence b (latent_bits [B, T, 512],
+    k_pe_bits [B, T, 64]) is position start_pos[b] + t, stored at cache row
+    row_offset[b] + start_pos[b] + t; positions outside [0, max_seqlen) are not stored.
+    Returns updated copies of both caches (rows of 512 and of 64 bf16 bit patterns)."""
+    kv = np.array(kv_cache_bits, copy=True)
+    pe = np.array(pe_cache_bits, copy=True)
+    lat = np.asarray(latent_bits)
+    kpe = np.asarray(k_pe_bits)
+    B, T = lat.shape[:2]
+    for b in range(B):
+        for t in range(T):
+            pos = int(start_pos[b]) + t
+            if 0 <= pos < max_seqlen:
+                row = int(row_offset[b]) + pos
+                kv[row] = lat[b, t]
+                pe[row] = kpe[b, t]
+    return kv, pe
+
+
+# ---------------------------------------------------------------------------------------------
+# Decode restricted to the indexer's top-k positions
+# ---------------------------------------------------------------------------------------------
+def decode_topk(q, wkv_b_bits, kv_bits, pe_bits, topk, scale: float, staged: bool = True,
+                round_output: bool = True) -> Tuple[np.ndarray, np.ndarray]:
+    """[AU] mla-decode with its index mask: a mask of -inf over the L cached positions gets 0 at
+    every position the top-k list names (a scatter, so a position named twice is still one
+    position) and is added to the scores before the softmax. Entries outside [0, L) name no
+    position (reading: padding of a list longer than the sequence). No named position gives
+    out = 0, lse = -inf. q [H, 192] fp64 values; topk int [K].
+    Returns (out [H, 128] -- bf16-valued when staged and round_output, lse [H])."""
+    q = np.asarray(q, np.float64)
+    H = q.shape[0]
+    c = bf16_decode(kv_bits)
+    pe = bf16_decode(pe_bits)
+    L = c.shape[0]
+    idx = np.asarray(topk, np.int64)
+    mask = np.full(L, -np.inf)
+    mask[idx[(idx >= 0) & (idx < L)]] = 0.0
+    if not np.isfinite(mask).any():
+        return np.zeros((H, V_DIM)), np.full(H, -np.inf)
+    _, uv = wkv_b_heads(bf16_decode(wkv_b_bits), H)
+    q_lat = absorb_query(q, wkv_b_bits, staged)
+    s = scale * (q_lat @ c.T + q[:, NOPE:] @ pe.T) + mask[None, :]
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True)
+    o_lat = (p @ c) / l
+    out = np.einsum("hc,hdc->hd", o_lat, uv)
+    return _maybe_round(out, staged and round_output), (m + np.log(l))[:, 0]
+
+
+def decode_topk_batch(q, wkv_b_bits, kv_cache_bits, pe_cache_bits, row_offset, lengths, topk, scale: float,
+                      staged: bool = True, batch_ids: Optional[Sequence[int]] = None, round_output: bool = True
+                      ) -> Tuple[np.ndarray, np.ndarray]:
+    """decode_topk of every (or each listed) sequence b over its rows [row_offset[b],
+    row_offset[b] + lengths[b]) with top-k list topk[b]. Returns (out [n, H, 128], lse [n, H])."""
+    q = np.asarray(q, np.float64)
+    ids = range(q.shape[0]) if batch_ids is None else list(batch_ids)
+    outs, lses = [], []
+    for b in ids:
+        r0, L = int(row_offset[b]), int(lengths[b])
+        o, l = decode_topk(q[b], wkv_b_bits, kv_cache_bits[r0:r0 + L], pe_cache_bits[r0:r0 + L], topk[b],
+                           scale, staged, round_output)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)
+
+
+# ---------------------------------------------------------------------------------------------
+# Output projection
+# ---------------------------------------------------------------------------------------------
+def output_proj(x_bits, wo_bits, staged: bool = True) -> np.ndarray:
+    """[AU] mla-output: the head outputs [.., H, 128] are flattened (head-major, feature h*128 + d)
+    and projected by wo, a Linear from H*128 features to the model width ([QH] MLA __init__;
+    [AU] shape of the attention update: 7168 for DeepSeek-V3.2). The weight is stored as a torch
+    Linear stores it, [out = dim, in = H*128], and y = x W^T, a bf16 Linear output.
+    x_bits bf16 [n, H, 128]; wo_bits bf16 [dim, H*128]. Returns y [n, dim]."""
+    x = bf16_decode(x_bits)
+    x = x.reshape(x.shape[0], -1)
+    w = bf16_decode(wo_bits)
+    return _maybe_round(x @ w.T, staged)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -395,15 +517,16 @@ def prefill_score_magnitude(q, kv_latent_bits, k_pe_bits, wkv_b_bits, scale: flo
                             ) -> np.ndarray:
     """For each listed head and query row t, max_{t' <= t} scale * sum_i |q_t,i k_t',i|. [n_heads_sel, n_rows]."""
     q = np.asarray(q, np.float64)
-    T, H, _ = q.shape
+    Tq, H, _ = q.shape
+    off = np.asarray(kv_latent_bits).shape[0] - Tq
     heads = list(range(H)) if heads is None else list(heads)
-    rows = list(range(T)) if rows is None else list(rows)
-    need = max(rows) + 1 if rows else 0
+    rows = list(range(Tq)) if rows is None else list(rows)
+    need = off + max(rows) + 1 if rows else 0
     pe = np.abs(bf16_decode(k_pe_bits[:need]))
     mag = np.empty((len(heads), len(rows)))
     for j, h in enumerate(heads):
         k_h, _ = expand_latent(kv_latent_bits[:need], wkv_b_bits, H, staged, heads=[h])
         k = np.concatenate([np.abs(k_h[:, 0, :]), pe], axis=1)
-        for i, t in enumerate(rows):
-            mag[j, i] = scale * np.max(k[: t + 1] @ np.abs(q[t, h]))
+        for i, r in enumerate(rows):
+            mag[j, i] = scale * np.max(k[: off + r + 1] @ np.abs(q[r, h]))
     return mag

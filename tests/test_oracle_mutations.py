@@ -9,6 +9,7 @@ import pytest
 from oracle import mla_oracle as O
 import tests.test_oracle_attention as TA
 import tests.test_oracle_codec_norms as TC
+import tests.test_oracle_next as TN
 
 MUTANTS = {
     "rope_sign": ("ra = a * c - b * s", "ra = a * c + b * s",
@@ -27,7 +28,7 @@ MUTANTS = {
     "absorb_through_value_half": ("uk, _ = wkv_b_heads(bf16_decode(wkv_b_bits), q.shape[0])",
                                   "_, uk = wkv_b_heads(bf16_decode(wkv_b_bits), q.shape[0])",
                                   [(TA, "test_absorbed_equals_expanded")]),
-    "causal_diagonal_dropped": ("s = scale * (k[: t + 1] @ q_h[t])", "s = scale * (k[: max(t, 1)] @ q_h[t])",
+    "causal_diagonal_dropped": ("s = scale * (k[: t + 1] @ q_h[r])", "s = scale * (k[: max(t, 1)] @ q_h[r])",
                                 [(TA, "test_prefill_first_row_future_rows_and_sdpa")]),
     "rms_sum_not_mean": ("m2 = np.mean(x * x, axis=-1, keepdims=True)", "m2 = np.sum(x * x, axis=-1, keepdims=True)",
                          [(TC, "test_rmsnorm_hand_case"), (TC, "test_rmsnorm_unit_rms_and_eps_shrink")]),
@@ -40,6 +41,18 @@ MUTANTS = {
     "bf16_truncates": ("r = np.rint(flat[fin] * np.exp2(-q)) * np.exp2(q)",
                        "r = np.trunc(flat[fin] * np.exp2(-q)) * np.exp2(q)",
                        [(TC, "test_bf16_encode_matches_torch_on_fp32_values")]),
+    "kv_split_rotary_first": ("lat, _ = rms_norm(a[:, :KV_LORA], kv_gamma, eps)",
+                              "lat, _ = rms_norm(a[:, ROPE:], kv_gamma, eps)",
+                              [(TN, "test_kv_side_split_order")]),
+    "cache_position_shifted": ("pos = int(start_pos[b]) + t", "pos = int(start_pos[b]) + t + 1",
+                               [(TN, "test_cache_append_rows_and_decode_roundtrip")]),
+    "topk_mask_ignored": ("mask[idx[(idx >= 0) & (idx < L)]] = 0.0", "mask[:] = 0.0",
+                          [(TN, "test_topk_equals_dense_decode_over_gathered_rows")]),
+    "prefix_offset_dropped": ("t = q_offset + r", "t = r",
+                              [(TN, "test_prefix_prefill_equals_tail_of_whole_prefill")]),
+    "wo_flatten_value_major": ("x = x.reshape(x.shape[0], -1)",
+                               "x = x.transpose(0, 2, 1).reshape(x.shape[0], -1)",
+                               [(TN, "test_output_proj_width_flatten_order_and_library")]),
     "gain_ignored": ("y = np.asarray(gamma, dtype=np.float64) * (x * inv)", "y = (x * inv) + 0 * np.asarray(gamma)",
                      [(TA, "test_query_path_matches_torch_complex_route")]),
 }
