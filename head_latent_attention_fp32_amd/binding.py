@@ -57,9 +57,11 @@ def _lib():
         lib.mla_decode.argtypes = [dp, _I32, _P, _P, _P, _P, _P, _P, _I64, _P, _SZ, _P, _P, _P]
         lib.mla_prefill_workspace_size.argtypes = [dp, _I32, _I32, ctypes.POINTER(_SZ)]
         lib.mla_prefill.argtypes = [dp, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]
+        lib.mla_prefill_with_prefix.argtypes = [dp, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]
+        lib.mla_kv_append.argtypes = [dp, _I32, _I32, _P, _P, _P, _P, _P, _I64, _P, _P, _P]
         for f in ("mla_dims_default", "mla_query_path_workspace_size", "mla_query_path", "mla_decode_workspace_size",
-                  "mla_decode",
-                  "mla_prefill_workspace_size", "mla_prefill"):
+                  "mla_decode", "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_with_prefix",
+                  "mla_kv_append"):
             getattr(lib, f).restype = ctypes.c_int
         lib.mla_status_string.argtypes = [ctypes.c_int]
         lib.mla_status_string.restype = ctypes.c_char_p
@@ -238,3 +240,65 @@ def prefill(q: torch.Tensor, kv_latent: torch.Tensor, k_pe: torch.Tensor, wkv_b:
     _check(_lib().mla_prefill(ctypes.byref(d), B, T, _ptr(q), _ptr(kv_latent), _ptr(k_pe), _ptr(wkv_b),
                               _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _stream()), "mla_prefill")
     return out, lse
+
+
+def prefill_with_prefix(q: torch.Tensor, kv_latent: torch.Tensor, k_pe: torch.Tensor, wkv_b: torch.Tensor,
+                        workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None, d: Optional[MlaDims] = None
+                        ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """q bf16 [B, Tq, H, 192] for the last Tq of S positions; kv_latent bf16 [B, S, 512]; k_pe bf16
+    [B, S, 64]; wkv_b bf16 [H*256, 512] -> out bf16 [B, Tq, H, 128] (and lse fp32 [B, H, Tq] if given)."""
+    _need(q, "q", torch.bfloat16)
+    if q.dim() != 4 or q.shape[3] != QK:
+        raise ValueError("q must be [B, Tq, H, 192]")
+    B, Tq, H = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
+    d = d or dims(H)
+    _need(kv_latent, "kv_latent", torch.bfloat16)
+    if kv_latent.dim() != 3 or kv_latent.shape[0] != B or kv_latent.shape[2] != KV_LORA:
+        raise ValueError("kv_latent must be [B, S, 512]")
+    S = int(kv_latent.shape[1])
+    _need(k_pe, "k_pe", torch.bfloat16, (B, S, ROPE))
+    _need(wkv_b, "wkv_b", torch.bfloat16, (H * (NOPE + V_DIM), KV_LORA))
+    need = prefill_workspace_size(H, B, S, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    if out is None:
+        out = torch.empty((B, Tq, H, V_DIM), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (B, Tq, H, V_DIM))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, H, Tq))
+    _check(_lib().mla_prefill_with_prefix(ctypes.byref(d), B, Tq, S, _ptr(q), _ptr(kv_latent), _ptr(k_pe),
+                                          _ptr(wkv_b), _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse),
+                                          _stream()), "mla_prefill_with_prefix")
+    return out, lse
+
+
+def kv_append(kv_a: torch.Tensor, kv_norm_w: torch.Tensor, rope_cs: torch.Tensor, start_pos: torch.Tensor,
+              kv_cache: torch.Tensor, pe_cache: torch.Tensor, max_seqlen: int,
+              cache_row_offset: Optional[torch.Tensor] = None, d: Optional[MlaDims] = None,
+              n_heads: int = 128) -> None:
+    """kv_a bf16 [B, T, 576]; kv_norm_w fp32 [512]; rope_cs fp32 [B, T, 32, 2]; start_pos int32 [B];
+    kv_cache bf16 [rows, 512] and pe_cache bf16 [rows, 64], written in place at rows
+    cache_row_offset[b] (or b*max_seqlen) + start_pos[b] + t."""
+    d = d or dims(n_heads)
+    _need(kv_a, "kv_a", torch.bfloat16)
+    if kv_a.dim() != 3 or kv_a.shape[2] != KV_LORA + ROPE:
+        raise ValueError("kv_a must be [B, T, 576]")
+    B, T = int(kv_a.shape[0]), int(kv_a.shape[1])
+    _need(kv_norm_w, "kv_norm_w", torch.float32, (KV_LORA,))
+    _need(rope_cs, "rope_cs", torch.float32, (B, T, ROPE // 2, 2))
+    _need(start_pos, "start_pos", torch.int32, (B,))
+    _need(kv_cache, "kv_cache", torch.bfloat16)
+    _need(pe_cache, "pe_cache", torch.bfloat16)
+    if kv_cache.shape[-1] != KV_LORA or pe_cache.shape[-1] != ROPE:
+        raise ValueError("kv_cache rows must be 512 wide and pe_cache rows 64 wide")
+    if kv_cache.numel() // KV_LORA != pe_cache.numel() // ROPE:
+        raise ValueError("kv_cache and pe_cache must hold the same number of rows")
+    if cache_row_offset is not None:
+        _need(cache_row_offset, "cache_row_offset", torch.int64, (B,))
+    elif kv_cache.numel() // KV_LORA < B * max_seqlen:
+        raise ValueError("padded caches (no row offsets) need batch * max_seqlen rows")
+    _check(_lib().mla_kv_append(ctypes.byref(d), B, T, _ptr(kv_a), _ptr(kv_norm_w), _ptr(rope_cs), _ptr(start_pos),
+                                _ptr(cache_row_offset), int(max_seqlen), _ptr(kv_cache), _ptr(pe_cache), _stream()),
+           "mla_kv_append")

@@ -144,8 +144,54 @@ mla_status_t mla_prefill_ex(const mla_dims_t* dims, int32_t batch, int32_t seqle
     return MLA_ERR_ALIGNMENT;
   const mla::PrefillLayout lay = mla::prefill_layout(dims->n_heads, batch, seqlen);
   if (workspace_bytes < lay.total) return MLA_ERR_WORKSPACE;
-  hipError_t e = mla::launch_prefill(dims->n_heads, batch, seqlen, q, kv_latent, k_pe, wkv_b, workspace, lay, out,
-                                     lse, dims->softmax_scale, stream, stage_events);
+  hipError_t e = mla::launch_prefill(dims->n_heads, batch, seqlen, seqlen, q, kv_latent, k_pe, wkv_b, workspace, lay,
+                                     out, lse, dims->softmax_scale, stream, stage_events);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_prefill_with_prefix_ex(const mla_dims_t* dims, int32_t batch, int32_t q_len, int32_t kv_len,
+                                        const uint16_t* q, const uint16_t* kv_latent, const uint16_t* k_pe,
+                                        const uint16_t* wkv_b, void* workspace, size_t workspace_bytes, uint16_t* out,
+                                        float* lse, hipStream_t stream, hipEvent_t* stage_events) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || batch > 65535 || q_len < 0 || kv_len < q_len) return MLA_ERR_SHAPE;
+  if (batch == 0 || q_len == 0) return MLA_OK;
+  if (!q || !kv_latent || !k_pe || !wkv_b || !workspace || !out) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kv_latent) || !aligned16(k_pe) || !aligned16(wkv_b) || !aligned16(workspace) ||
+      !aligned16(out) || (lse && !aligned16(lse)))
+    return MLA_ERR_ALIGNMENT;
+  const mla::PrefillLayout lay = mla::prefill_layout(dims->n_heads, batch, kv_len);
+  if (workspace_bytes < lay.total) return MLA_ERR_WORKSPACE;
+  hipError_t e = mla::launch_prefill(dims->n_heads, batch, q_len, kv_len, q, kv_latent, k_pe, wkv_b, workspace, lay,
+                                     out, lse, dims->softmax_scale, stream, stage_events);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_prefill_with_prefix(const mla_dims_t* dims, int32_t batch, int32_t q_len, int32_t kv_len,
+                                     const uint16_t* q, const uint16_t* kv_latent, const uint16_t* k_pe,
+                                     const uint16_t* wkv_b, void* workspace, size_t workspace_bytes, uint16_t* out,
+                                     float* lse, hipStream_t stream) {
+  return mla_prefill_with_prefix_ex(dims, batch, q_len, kv_len, q, kv_latent, k_pe, wkv_b, workspace,
+                                    workspace_bytes, out, lse, stream, nullptr);
+}
+
+mla_status_t mla_kv_append(const mla_dims_t* dims, int32_t batch, int32_t seqlen, const uint16_t* kv_a,
+                           const float* kv_norm_w, const float* rope_cs, const int32_t* start_pos,
+                           const int64_t* cache_row_offset, int64_t max_seqlen, uint16_t* kv_cache,
+                           uint16_t* pe_cache, hipStream_t stream) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || batch > kMaxBatch || seqlen < 0 || max_seqlen < 0 || max_seqlen > kMaxSeqlen ||
+      static_cast<int64_t>(batch) * seqlen > kMaxTokens)
+    return MLA_ERR_SHAPE;
+  if (batch == 0 || seqlen == 0) return MLA_OK;
+  if (!kv_a || !kv_norm_w || !rope_cs || !start_pos || !kv_cache || !pe_cache) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(kv_a) || !aligned16(kv_norm_w) || !aligned16(rope_cs) || !aligned16(start_pos) ||
+      !aligned16(kv_cache) || !aligned16(pe_cache) || (cache_row_offset && !aligned16(cache_row_offset)))
+    return MLA_ERR_ALIGNMENT;
+  hipError_t e = mla::launch_kv_append(batch, seqlen, kv_a, kv_norm_w, rope_cs, start_pos, cache_row_offset,
+                                       max_seqlen, dims->rms_eps, kv_cache, pe_cache, stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -49,9 +49,16 @@ hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16
                          const DecodeLayout& lay, uint16_t* out, float* lse, float scale,
                          hipStream_t stream, hipEvent_t* ev);
 
-hipError_t launch_prefill(int n_heads, int batch, int seqlen, const uint16_t* q, const uint16_t* kv_latent,
-                          const uint16_t* k_pe, const uint16_t* wkv_b, void* workspace,
+// Causal prefill of the last q_len of kv_len positions (q_len <= kv_len); the workspace layout is
+// prefill_layout(n_heads, batch, kv_len).
+hipError_t launch_prefill(int n_heads, int batch, int q_len, int kv_len, const uint16_t* q,
+                          const uint16_t* kv_latent, const uint16_t* k_pe, const uint16_t* wkv_b, void* workspace,
                           const PrefillLayout& lay, uint16_t* out, float* lse, float scale,
                           hipStream_t stream, hipEvent_t* ev);
+
+hipError_t launch_kv_append(int batch, int seqlen, const uint16_t* kv_a, const float* kv_norm_w,
+                            const float* rope_cs, const int32_t* start_pos, const int64_t* row_offset,
+                            int64_t max_seqlen, float eps, uint16_t* kv_cache, uint16_t* pe_cache,
+                            hipStream_t stream);
 
 }  // namespace mla

@@ -3,10 +3,13 @@
 // Follows "Kimi-K2 · value_states", mla-prefill excerpt: the cached latent is expanded through
 // kv_b_proj (wkv_b) into per-head k_nope and value states; each head's key joins its k_nope with
 // the rotary key shared by every head; scores are scaled, causally masked, softmaxed in fp32 and
-// used to mix the values. Start position 0: query t sees keys 0..t.
+// used to mix the values. The queries are the last q_len of kv_len positions (q_len = kv_len: a
+// prefill from position 0; q_len < kv_len: new tokens over a cached prefix, the mask then being
+// (q_len, kv_seq_len) as in the excerpt): query i, at position kv_len - q_len + i, sees keys
+// 0 .. kv_len - q_len + i.
 //
 // Two kernels:
-//   1. expand   [k_nope | v] = latent . wkv_b^T per head (MFMA GEMM, bf16 outputs as the bf16
+//   1. expand   [k_nope | v] = latent . wkv_b^T per head for all kv_len positions (MFMA GEMM, bf16 outputs as the bf16
 //               Linear of the excerpt). k_nope is written [b][h][t][128] and v transposed,
 //               [b][h][128][t], so that the attention kernel's P.V operand reads runs of keys;
 //               within every 32 keys the order is permuted (key 16a + 4g + j at 8g + 4a + j) to
@@ -196,11 +199,12 @@ __device__ __forceinline__ int swz_128(int row) { return (row >> 1) & 7; }
 
 __global__ __launch_bounds__(256, 2) void attend_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ knope, const uint16_t* __restrict__ vt,
-    const uint16_t* __restrict__ k_pe, int batch, int n_heads, int seqlen, int64_t t_pad, float scale_log2,
-    uint16_t* __restrict__ out, float* __restrict__ lse) {
+    const uint16_t* __restrict__ k_pe, int batch, int n_heads, int q_len, int kv_len, int64_t t_pad,
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) uint8_t stage[2][kStage];
 
-  const int n_qb = (seqlen + kPQ - 1) / kPQ;
+  const int n_qb = (q_len + kPQ - 1) / kPQ;
+  const int q_pos0 = kv_len - q_len;                     // position of query 0
   const int n_bh = batch * n_heads;
   const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3;
   const int bh = xcd + 8 * (i / n_qb);
@@ -212,21 +216,22 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, grp = lane >> 4;
-  const int q0 = qb * kPQ + wave * 32;                   // this wave's first query
+  const int q0 = qb * kPQ + wave * 32;                   // this wave's first query (index)
+  const int p0 = q_pos0 + q0;                            // and its position
 
   // Query fragments (B operand): query q0 + 16 qh + r, k-group grp of each of the 6 k-steps.
   bf16x8 qf[2][6];
 #pragma unroll
   for (int qh = 0; qh < 2; ++qh) {
-    const int tq = min(q0 + 16 * qh + r, seqlen - 1);
-    const uint16_t* qp = q + ((b * seqlen + tq) * n_heads + h) * kQk + grp * 8;
+    const int tq = min(q0 + 16 * qh + r, q_len - 1);
+    const uint16_t* qp = q + ((b * q_len + tq) * n_heads + h) * kQk + grp * 8;
 #pragma unroll
     for (int ks = 0; ks < 6; ++ks) qf[qh][ks] = as_bf16x8(ldg16(qp + ks * 32));
   }
 
   const uint16_t* kn = knope + static_cast<int64_t>(bh) * t_pad * kNope;
   const uint16_t* vh = vt + static_cast<int64_t>(bh) * kVDim * t_pad;
-  const uint16_t* pe = k_pe + b * static_cast<int64_t>(seqlen) * kRope;
+  const uint16_t* pe = k_pe + b * static_cast<int64_t>(kv_len) * kRope;
   const uint32_t st_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)&stage[0][0]));
 
   // Loads of a tile, 10 per wave: k_nope instructions d = wave + 4e (4 keys x 256 B each), rotary
@@ -250,7 +255,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
     const int k0 = kt * kPK;
     const uint32_t dst = st_lds + (kt & 1) * kStage;
     const auto rk = make_rsrc(kn + static_cast<int64_t>(k0) * kNope, static_cast<uint32_t>(t_pad - k0) * 256u);
-    const int rows_pe = seqlen - k0;
+    const int rows_pe = kv_len - k0;
     const auto rp = make_rsrc(pe + static_cast<int64_t>(k0) * kRope, static_cast<uint32_t>(rows_pe) * 128u);
     const auto rv = make_rsrc(vh + k0, static_cast<uint32_t>(kVDim * t_pad - k0) * 2u);
 #pragma unroll
@@ -280,8 +285,8 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
 #pragma unroll
     for (int db = 0; db < 8; ++db) o[qh][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // keys 0 .. min(seqlen, last query of the block + 1)
-  const int k_end = min(seqlen, (qb + 1) * kPQ);
+  // keys 0 .. position of the block's last query
+  const int k_end = min(kv_len, q_pos0 + (qb + 1) * kPQ);
   const int n_kt = (k_end + kPK - 1) / kPK;
   issue(0);
   for (int kt = 0; kt < n_kt; ++kt) {
@@ -303,17 +308,17 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
         s[1][kb] = mfma16x16x32(a, qf[1][ks], s[1][kb]);
       }
     }
-    // causal and length mask on the tiles that reach past this wave's first query
-    if (k0 + kPK - 1 > q0 || k0 + kPK > seqlen) {
+    // causal and length mask on the tiles that reach past this wave's first query position
+    if (k0 + kPK - 1 > p0 || k0 + kPK > kv_len) {
 #pragma unroll
       for (int qh = 0; qh < 2; ++qh) {
-        const int tq = q0 + 16 * qh + r;
+        const int pq = p0 + 16 * qh + r;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int key = k0 + 16 * kb + 4 * grp + j;
-            if (key > tq || key >= seqlen) s[qh][kb][j] = -INFINITY;
+            if (key > pq || key >= kv_len) s[qh][kb][j] = -INFINITY;
           }
       }
     }
@@ -366,9 +371,9 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
   for (int qh = 0; qh < 2; ++qh) {
     const float ltot = sum_over_rows(lsum[qh]);
     const int tq = q0 + 16 * qh + r;
-    if (tq < seqlen) {
+    if (tq < q_len) {
       const float inv = 1.f / ltot;
-      uint16_t* dst = out + ((b * seqlen + tq) * n_heads + h) * kVDim + grp * 4;
+      uint16_t* dst = out + ((b * q_len + tq) * n_heads + h) * kVDim + grp * 4;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         uint2 u;
@@ -376,7 +381,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
         u.y = pack_bf16x2(o[qh][db][2] * inv, o[qh][db][3] * inv);
         *reinterpret_cast<uint2*>(dst + db * 16) = u;
       }
-      if (lse && grp == 0) lse[(b * n_heads + h) * seqlen + tq] = (m[qh] + __log2f(ltot)) * kLn2;
+      if (lse && grp == 0) lse[(b * n_heads + h) * q_len + tq] = (m[qh] + __log2f(ltot)) * kLn2;
     }
   }
 }
@@ -393,13 +398,14 @@ PrefillLayout prefill_layout(int n_heads, int batch, int seqlen) {
   return L;
 }
 
-hipError_t launch_prefill(int n_heads, int batch, int seqlen, const uint16_t* q, const uint16_t* kv_latent,
-                          const uint16_t* k_pe, const uint16_t* wkv_b, void* workspace,
+hipError_t launch_prefill(int n_heads, int batch, int q_len, int kv_len, const uint16_t* q,
+                          const uint16_t* kv_latent, const uint16_t* k_pe, const uint16_t* wkv_b, void* workspace,
                           const PrefillLayout& lay, uint16_t* out, float* lse, float scale,
                           hipStream_t stream, hipEvent_t* ev) {
   char* ws = static_cast<char*>(workspace);
   uint16_t* knope = reinterpret_cast<uint16_t*>(ws + lay.knope_off);
   uint16_t* vt = reinterpret_cast<uint16_t*>(ws + lay.vt_off);
+  const int seqlen = kv_len;   // the expansion covers every key position
   const int64_t n_rows = static_cast<int64_t>(batch) * seqlen;
   mark(ev, 0, stream);
   if (lay.t_pad != seqlen) {
@@ -412,10 +418,10 @@ hipError_t launch_prefill(int n_heads, int batch, int seqlen, const uint16_t* q,
   mark(ev, 1, stream);
   {
     // blocks of one (b, h) on one XCD: grid = 8 x ceil(B H / 8) x query blocks
-    const int64_t n_qb = (seqlen + kPQ - 1) / kPQ;
+    const int64_t n_qb = (q_len + kPQ - 1) / kPQ;
     const int64_t n_bh8 = (static_cast<int64_t>(batch) * n_heads + 7) / 8;
     attend_kernel<<<static_cast<unsigned>(8 * n_bh8 * n_qb), 256, 0, stream>>>(
-        q, knope, vt, k_pe, batch, n_heads, seqlen, lay.t_pad, scale * kLog2e, out, lse);
+        q, knope, vt, k_pe, batch, n_heads, q_len, kv_len, lay.t_pad, scale * kLog2e, out, lse);
   }
   mark(ev, 2, stream);
   return hipGetLastError();

@@ -150,6 +150,47 @@ mla_status_t mla_prefill(const mla_dims_t* dims, int32_t batch, int32_t seqlen, 
                          void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
                          hipStream_t stream);
 
+/* Causal prefill of new tokens over a cached prefix ("Kimi-K2 · value_states", mla-prefill excerpt:
+ * once past keys join the new ones the weights and mask are (q_len, kv_seq_len)). The sequence has
+ * kv_len positions; the queries are its last q_len (q_len <= kv_len), query i at position
+ * kv_len - q_len + i, and see keys 0 .. kv_len - q_len + i. q_len = kv_len is mla_prefill.
+ *   q          bf16 [batch, q_len, n_heads, 192]
+ *   kv_latent  bf16 [batch, kv_len, 512]    normalised latent of every position (cached prefix, then
+ *                                           the new tokens' own rows, e.g. as mla_kv_append wrote them)
+ *   k_pe       bf16 [batch, kv_len, 64]     rotated rotary key of every position
+ *   wkv_b      bf16 [n_heads*256, 512]
+ *   workspace  >= mla_prefill_workspace_size(dims, batch, kv_len) bytes
+ *   out        bf16 [batch, q_len, n_heads, 128]
+ *   lse        fp32 [batch, n_heads, q_len] or NULL
+ * kv_len < q_len -> MLA_ERR_SHAPE; q_len = 0 enqueues nothing. */
+mla_status_t mla_prefill_with_prefix(const mla_dims_t* dims, int32_t batch, int32_t q_len, int32_t kv_len,
+                                     const uint16_t* q, const uint16_t* kv_latent, const uint16_t* k_pe,
+                                     const uint16_t* wkv_b, void* workspace, size_t workspace_bytes,
+                                     uint16_t* out, float* lse, hipStream_t stream);
+
+/* Key/value side of new tokens and their cache rows ("DeepSeek-V3.2-Exp · Query heads", MLA __init__:
+ * wkv_a gives kv_lora_rank + qk_rope_dim = 576 features per token and kv_norm normalises the latent;
+ * "Kimi-K2 · value_states", mla-init and mla-prefill excerpts: the rotary key is rotated like q_pe;
+ * "DeepSeek-V3.2-Exp · Attention update", mla-decode excerpt: cache rows are positions). For new
+ * token t of sequence b, at position p = start_pos[b] + t:
+ *   latent = bf16(kv_norm_w * x / sqrt(mean(x^2) + rms_eps)),  x = kv_a[b,t,0:512]  (fp32 math)
+ *   rotary = bf16(RoPE(kv_a[b,t,512:576], rope_cs[b,t]))  interleaved pairs (2i, 2i+1),
+ *            (a, b) -> (a cos - b sin, a sin + b cos)
+ *   kv_cache[row] = latent, pe_cache[row] = rotary,  row = cache_row_offset[b] + p
+ *   kv_a              bf16 [batch, seqlen, 576]   wkv_a output: latent (512) then rotary key (64)
+ *   kv_norm_w         fp32 [512]                  kv_norm gain
+ *   rope_cs           fp32 [batch, seqlen, 32, 2] (cos, sin) of each token's own position
+ *   start_pos         int32 [batch], device       position of each sequence's first new token
+ *   cache_row_offset  int64 [batch], device, or NULL for b * max_seqlen (a padded [batch, max_seqlen]
+ *                     cache)
+ *   kv_cache, pe_cache bf16 rows of 512 / 64, written in place (the caches mla_decode reads)
+ * Positions outside [0, max_seqlen) are not written (a caller error that never writes out of
+ * bounds). No other row is touched. Tokens must not map to the same row. */
+mla_status_t mla_kv_append(const mla_dims_t* dims, int32_t batch, int32_t seqlen, const uint16_t* kv_a,
+                           const float* kv_norm_w, const float* rope_cs, const int32_t* start_pos,
+                           const int64_t* cache_row_offset, int64_t max_seqlen, uint16_t* kv_cache,
+                           uint16_t* pe_cache, hipStream_t stream);
+
 /* Instrumented variants: identical work, plus hipEventRecord of caller-created events on `stream`
  * at the boundaries of the library's kernel stages, so a caller can time each stage on the stream
  * it runs on. stage_events is NULL or an array of (number of stages + 1) events, any of which may be
@@ -157,7 +198,7 @@ mla_status_t mla_prefill(const mla_dims_t* dims, int32_t batch, int32_t seqlen, 
  *   mla_query_path_ex: 2 stages (RMSNorm pass -- empty when fused into the product, 32 tokens or
  *                      fewer --, product + RoPE)
  *   mla_decode_ex:     4 stages (absorb + run plan, split-KV attention, log-sum-exp combine, value projection)
- *   mla_prefill_ex:    2 stages (latent expansion, causal attention) */
+ *   mla_prefill_ex, mla_prefill_with_prefix_ex: 2 stages (latent expansion, causal attention) */
 mla_status_t mla_query_path_ex(const mla_dims_t* dims, int64_t n_tokens,
                                const uint16_t* q_latent, const float* q_norm_w, const uint16_t* wq_b,
                                const float* rope_cs, uint16_t* q_out, float* inv_rms,
@@ -172,6 +213,10 @@ mla_status_t mla_prefill_ex(const mla_dims_t* dims, int32_t batch, int32_t seqle
                             const uint16_t* kv_latent, const uint16_t* k_pe, const uint16_t* wkv_b,
                             void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
                             hipStream_t stream, hipEvent_t* stage_events);
+mla_status_t mla_prefill_with_prefix_ex(const mla_dims_t* dims, int32_t batch, int32_t q_len, int32_t kv_len,
+                                        const uint16_t* q, const uint16_t* kv_latent, const uint16_t* k_pe,
+                                        const uint16_t* wkv_b, void* workspace, size_t workspace_bytes,
+                                        uint16_t* out, float* lse, hipStream_t stream, hipEvent_t* stage_events);
 
 /* Static description of a status code. */
 const char* mla_status_string(mla_status_t status);

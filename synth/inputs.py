@@ -14,6 +14,10 @@ Recipe (identical for the GPU path, the oracle, the tests and the benchmark):
     512 for wkv_b; the RMSNorm gain is 1 + 0.1 N(0, 1) in fp32;
   * draws are made in fp32 and rounded to bf16 with round-to-nearest-even;
   * rotary frequencies follow theta = 10000 over 64 rotary features (32 pairs).
+Steps next to the path draw in the same way: the joint down-projection output kv_a [n, 576] is
+N(0, 1) (an N(0,1) token through N(0, 1/fan_in) weights), the kv_norm gain 1 + 0.1 N(0, 1), wo
+[7168, H*128] N(0, 1/(H*128)), head outputs N(0, 1); a top-k list of sequence b holds
+min(k, L_b) distinct positions drawn uniformly from [0, L_b) in random order, padded with -1.
 """
 from __future__ import annotations
 
@@ -38,6 +42,9 @@ SOFTMAX_SCALE = QK_DIM ** -0.5
 
 # Tensor ids of the PCG64 key.
 T_Q_LATENT, T_GAMMA, T_WQ_B, T_WKV_B, T_KV, T_PE, T_LENGTHS, T_SPIKES, T_KV_LAT, T_K_PE, T_Q = range(11)
+T_KV_A, T_KV_GAMMA, T_WO, T_TOPK, T_HEAD_OUT = range(11, 16)
+
+MODEL_DIM = 7168               # DeepSeek-V3.2 model width (the attention update is [B, 1, 7168])
 
 _ROWS_PER_CHUNK = 16384
 
@@ -288,3 +295,37 @@ def prefill_query(case: PrefillCase, seed: int = 0, workers: Optional[int] = Non
     return normal_bf16_rows(case.batch * case.seqlen, case.n_heads * QK_DIM, 1.0,
                             (seed, case.case_id, T_Q), workers).reshape(
         case.batch, case.seqlen, case.n_heads, QK_DIM)
+
+
+# --------------------------------------------------------------------------------------------
+# Inputs of the steps next to the path
+# --------------------------------------------------------------------------------------------
+def kv_side_inputs(n_tokens: int, seed: int, case_id: int, workers: int = 1) -> Dict[str, np.ndarray]:
+    """kv_a bf16 [n, 576] (the joint down-projection output) and the kv_norm gain fp32 [512]."""
+    g = _rng(seed, case_id, T_KV_GAMMA).standard_normal(KV_LORA, dtype=np.float32)
+    return {"kv_a": normal_bf16_rows(n_tokens, KV_LORA + ROPE, 1.0, (seed, case_id, T_KV_A), workers),
+            "kv_gamma": (np.float32(1.0) + np.float32(0.1) * g).astype(np.float32)}
+
+
+def wo_weights(n_heads: int, seed: int, case_id: int, dim: int = MODEL_DIM, workers: int = 1) -> np.ndarray:
+    """wo bf16 [dim, H*128] (output x input) ~ N(0, 1/(H*128))."""
+    return normal_bf16_rows(dim, n_heads * V_DIM, (n_heads * V_DIM) ** -0.5, (seed, case_id, T_WO), workers)
+
+
+def head_outputs(n_tokens: int, n_heads: int, seed: int, case_id: int, workers: int = 1) -> np.ndarray:
+    """Attention head outputs bf16 [n, H, 128] ~ N(0, 1) (input of wo for wo-only tests)."""
+    return normal_bf16_rows(n_tokens, n_heads * V_DIM, 1.0, (seed, case_id, T_HEAD_OUT), workers).reshape(
+        n_tokens, n_heads, V_DIM)
+
+
+def topk_indices(lengths: np.ndarray, k: int, seed: int, case_id: int) -> np.ndarray:
+    """int32 [B, k]: for sequence b, min(k, L_b) distinct positions of [0, L_b) in random order,
+    then -1 padding."""
+    lengths = np.asarray(lengths)
+    out = np.full((lengths.shape[0], k), -1, dtype=np.int32)
+    for b, L in enumerate(lengths):
+        L = int(L)
+        n = min(k, L)
+        if n > 0:
+            out[b, :n] = _rng(seed, case_id, T_TOPK, b).choice(L, size=n, replace=False)
+    return out

@@ -29,7 +29,7 @@ def test_header_declares_the_three_entry_points():
     names = declared_functions()
     for f in ("mla_query_path", "mla_query_path_workspace_size", "mla_decode", "mla_prefill",
               "mla_decode_workspace_size",
-              "mla_prefill_workspace_size", "mla_status_string"):
+              "mla_prefill_workspace_size", "mla_status_string", "mla_prefill_with_prefix", "mla_kv_append"):
         assert f in names
 
 
@@ -138,6 +138,43 @@ def test_prefill_validation_and_workspace():
     assert pf(ctypes.byref(d), 1, 4096, FAKE, None, FAKE, FAKE, FAKE, need, FAKE, None, None) == 1
     assert pf(ctypes.byref(d), 1, 4096, FAKE, FAKE, MIS, FAKE, FAKE, need, FAKE, None, None) == 4
     assert pf(ctypes.byref(d), 1, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, need - 256, FAKE, None, None) == 5
+
+
+def test_prefill_with_prefix_validation():
+    lib = _lib()
+    d = _dims()
+    n = ctypes.c_size_t(0)
+    assert lib.mla_prefill_workspace_size(ctypes.byref(d), 1, 4096, ctypes.byref(n)) == 0
+    need = n.value
+    pf = lib.mla_prefill_with_prefix
+    args = lambda **kw: [kw.get(k, v) for k, v in [
+        ("dims", ctypes.byref(d)), ("batch", 1), ("q_len", 1024), ("kv_len", 4096), ("q", FAKE), ("lat", FAKE),
+        ("pe", FAKE), ("w", FAKE), ("ws", FAKE), ("wsb", need), ("out", FAKE), ("lse", None), ("stream", None)]]
+    assert pf(*args(q_len=0, q=None)) == 0
+    assert pf(*args(kv_len=1023)) == 3                 # fewer keys than queries
+    assert pf(*args(q_len=-1)) == 3
+    assert pf(*args(lat=None)) == 1
+    assert pf(*args(lse=MIS)) == 4
+    assert pf(*args(wsb=need - 1)) == 5
+
+
+def test_kv_append_validation():
+    lib = _lib()
+    d = _dims()
+    ap = lib.mla_kv_append
+    args = lambda **kw: [kw.get(k, v) for k, v in [
+        ("dims", ctypes.byref(d)), ("batch", 4), ("seqlen", 1), ("kv_a", FAKE), ("g", FAKE), ("cs", FAKE),
+        ("start", FAKE), ("off", None), ("maxl", 4096), ("kv", FAKE), ("pe", FAKE), ("stream", None)]]
+    assert ap(*args(batch=0, kv_a=None)) == 0
+    assert ap(*args(seqlen=-1)) == 3
+    assert ap(*args(maxl=(1 << 21) + 1)) == 3
+    assert ap(*args(start=None)) == 1
+    assert ap(*args(pe=None)) == 1
+    assert ap(*args(off=MIS)) == 4
+    assert ap(*args(kv_a=MIS)) == 4
+    d2 = _dims()
+    d2.kv_lora_rank = 256
+    assert ap(*args(dims=ctypes.byref(d2))) == 2
 
 
 def test_status_strings():

@@ -1,0 +1,175 @@
+"""GPU parity of the steps next to the hot path (through the C ABI) against the CPU oracle:
+the key/value side with its cache write, prefill over a cached prefix, and their composition with
+decode and prefill on caches the library wrote itself.
+
+Bars as in tests/gpu_helpers.py. Cache rows that no new token owns are compared bit for bit
+(they must be untouched); written rows within 2e-2 x RMS of each row."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import mla_oracle as O
+from synth import inputs as S
+from tests.gpu_helpers import (assert_bf16_parity, assert_f32_parity, dev, dev_bf16, host_bits, say)
+
+binding = pytest.importorskip("head_latent_attention_fp32_amd.binding")
+
+pytestmark = pytest.mark.gpu
+SCALE = 192 ** -0.5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm device")
+    binding.lib()
+
+
+# ----------------------------------------------------------------------------------- kv side
+def _kv_append_case(B, T, max_seqlen, start, packed, seed):
+    rng = np.random.default_rng(seed)
+    n = B * T
+    inp = S.kv_side_inputs(n, seed, 500 + B + T)
+    pos = (np.asarray(start)[:, None] + np.arange(T)[None]).reshape(-1)
+    cs = S.rope_table(np.maximum(pos, 0)).reshape(B, T, 32, 2)
+    if packed:
+        offs = np.concatenate([[0], np.cumsum(np.full(B, max_seqlen + 3))[:-1]]).astype(np.int64)
+        rows = int(offs[-1]) + max_seqlen + 3
+    else:
+        offs = np.arange(B, dtype=np.int64) * max_seqlen
+        rows = B * max_seqlen
+    kv = S.f32_to_bf16_bits(rng.standard_normal((rows, 512)).astype(np.float32))
+    pe = S.f32_to_bf16_bits(rng.standard_normal((rows, 64)).astype(np.float32))
+    return inp, cs, offs, kv, pe
+
+
+@pytest.mark.parametrize("B,T,max_seqlen,start,packed", [
+    (3, 5, 16, [0, 7, 13], False),          # the last sequence's tokens 3, 4 fall past the cache
+    (2, 1, 9, [8, 0], True),
+    (32, 1, 4096, list(range(4064, 4096)), False),
+    (1, 300, 512, [100], True),
+])
+def test_kv_append_parity(B, T, max_seqlen, start, packed):
+    say(f"kv_append B={B} T={T} max_seqlen={max_seqlen} packed={packed}")
+    inp, cs, offs, kv, pe = _kv_append_case(B, T, max_seqlen, start, packed, seed=B * 100 + T)
+    kv_d, pe_d = dev_bf16(kv), dev_bf16(pe)
+    binding.kv_append(dev_bf16(inp["kv_a"].reshape(B, T, 576)), dev(inp["kv_gamma"]), dev(cs),
+                      dev(np.asarray(start, np.int32)), kv_d, pe_d, max_seqlen,
+                      cache_row_offset=dev(offs) if packed else None)
+    torch.cuda.synchronize()
+    kv_g, pe_g = host_bits(kv_d), host_bits(pe_d)
+    lat, kpe = O.kv_side(inp["kv_a"], inp["kv_gamma"], cs.reshape(-1, 32, 2), staged=False)
+    written = np.zeros(kv.shape[0], bool)
+    rows, src = [], []
+    for b in range(B):
+        for t in range(T):
+            p = start[b] + t
+            if 0 <= p < max_seqlen:
+                rows.append(int(offs[b]) + p)
+                src.append(b * T + t)
+    written[rows] = True
+    np.testing.assert_array_equal(kv_g[~written], kv[~written])
+    np.testing.assert_array_equal(pe_g[~written], pe[~written])
+    assert_bf16_parity(kv_g[rows], lat[src], "latent rows")
+    assert_bf16_parity(pe_g[rows], kpe[src], "rotary key rows")
+
+
+def test_append_then_decode_on_own_caches():
+    """One decode step after appending each sequence's newest token: the library writes the row
+    and then attends over it; the oracle does the same with its own rows."""
+    B, H, Lmax = 4, 64, 300
+    lens_before = np.array([0, 1, 150, 299], np.int32)
+    seed = 7
+    rng = np.random.default_rng(seed)
+    kv = S.f32_to_bf16_bits(rng.standard_normal((B * Lmax, 512)).astype(np.float32))
+    pe = S.f32_to_bf16_bits(rng.standard_normal((B * Lmax, 64)).astype(np.float32))
+    offs = np.arange(B, dtype=np.int64) * Lmax
+    inp = S.kv_side_inputs(B, seed, 601)
+    cs = S.rope_table(lens_before).reshape(B, 1, 32, 2)
+    w = S.kv_weights(H, seed, 601)
+    q = S.normal_bf16_rows(B, H * 192, 1.0, (seed, 601, S.T_Q)).reshape(B, H, 192)
+    kv_d, pe_d = dev_bf16(kv), dev_bf16(pe)
+    binding.kv_append(dev_bf16(inp["kv_a"].reshape(B, 1, 576)), dev(inp["kv_gamma"]), dev(cs),
+                      dev(lens_before), kv_d, pe_d, Lmax)
+    lens = lens_before + 1
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    out, _ = binding.decode(dev_bf16(q), dev_bf16(w), kv_d, pe_d, dev(lens), Lmax, lse=lse)
+    torch.cuda.synchronize()
+    lat, kpe = O.kv_side(inp["kv_a"], inp["kv_gamma"], cs.reshape(B, 32, 2), staged=True)
+    kv_o, pe_o = O.cache_append(kv, pe, offs, lens_before, O.bf16_encode(lat)[:, None],
+                                O.bf16_encode(kpe)[:, None], Lmax)
+    oo, lo = O.decode_batch(O.bf16_decode(q), w, kv_o, pe_o, offs, lens, SCALE, round_output=False)
+    assert_bf16_parity(host_bits(out), oo, "decode out")
+    qv = O.bf16_decode(q)
+    mag = np.stack([O.decode_score_magnitude(qv[b], w, kv_o[offs[b]:offs[b] + lens[b]],
+                                             pe_o[offs[b]:offs[b] + lens[b]], SCALE) for b in range(B)])
+    assert_f32_parity(lse.cpu().numpy(), lo, "decode lse", magnitude=mag)
+
+
+# ----------------------------------------------------------------------------------- prefix prefill
+def _run_prefix(q_bits, lat, kpe, w, H):
+    B, Tq = q_bits.shape[:2]
+    lse = torch.empty((B, H, Tq), dtype=torch.float32, device="cuda")
+    out, _ = binding.prefill_with_prefix(dev_bf16(q_bits), dev_bf16(lat), dev_bf16(kpe), dev_bf16(w), lse=lse)
+    torch.cuda.synchronize()
+    return host_bits(out), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("H,B,Tq,Skv", [(16, 1, 1, 1), (16, 2, 5, 70), (64, 1, 64, 164), (32, 1, 130, 257),
+                                        (128, 1, 65, 300), (16, 1, 1, 513), (64, 2, 200, 200)])
+def test_prefill_with_prefix_parity(H, B, Tq, Skv):
+    say(f"prefill_with_prefix H={H} B={B} q_len={Tq} kv_len={Skv}")
+    case = S.PrefillCase("t", 700 + H + Tq + Skv, H, B, Skv)
+    d = S.prefill_inputs(case, seed=5, with_q_latent=False)
+    q = S.prefill_query(case, seed=5)[:, Skv - Tq:].copy()
+    out, lse = _run_prefix(q, d["kv_latent"], d["k_pe"], d["wkv_b"], H)
+    for b in range(B):
+        qv = O.bf16_decode(q[b])
+        oo, lo = O.prefill_causal(qv, d["kv_latent"][b], d["k_pe"][b], d["wkv_b"], SCALE, round_output=False)
+        assert_bf16_parity(out[b], oo, f"out[b={b}]")
+        mag = O.prefill_score_magnitude(qv, d["kv_latent"][b], d["k_pe"][b], d["wkv_b"], SCALE)
+        assert_f32_parity(lse[b], lo, f"lse[b={b}]", magnitude=mag)
+
+
+@pytest.mark.slow
+def test_prefill_with_prefix_chunk_of_4096_sampled():
+    """The second half of the 4096-token prefill as a chunk over its 2048-position prefix."""
+    H, S_, Tq = 128, 4096, 2048
+    case = S.PrefillCase("chunk", 2, H, 1, S_)
+    d = S.prefill_inputs(case, seed=0, with_q_latent=False)
+    q = S.prefill_query(case, seed=0)[:, S_ - Tq:].copy()
+    say(f"prefill_with_prefix H={H} q_len={Tq} kv_len={S_}: oracle on sampled rows and heads")
+    out, lse = _run_prefix(q, d["kv_latent"], d["k_pe"], d["wkv_b"], H)
+    rows, heads = [0, 1, 63, 64, 1000, 2046, 2047], [0, 50, 127]
+    qv = O.bf16_decode(q[0])
+    oo, lo = O.prefill_causal(qv, d["kv_latent"][0], d["k_pe"][0], d["wkv_b"], SCALE, heads=heads, rows=rows,
+                              round_output=False)
+    assert_bf16_parity(out[0][rows][:, heads], oo, "out")
+    mag = O.prefill_score_magnitude(qv, d["kv_latent"][0], d["k_pe"][0], d["wkv_b"], SCALE, heads=heads, rows=rows)
+    assert_f32_parity(lse[0][heads][:, rows], lo, "lse", magnitude=mag)
+
+
+def test_chunked_prefill_on_own_cache():
+    """Two chunks of one sequence: kv_append writes each chunk's rows into the cache, and each
+    chunk's prefill reads the cache's first kv_len rows; both chunks match the oracle's whole
+    prefill rows."""
+    H, S_, c1 = 32, 200, 120
+    seed = 11
+    inp = S.kv_side_inputs(S_, seed, 801)
+    cs = S.rope_table(np.arange(S_))
+    w = S.kv_weights(H, seed, 801)
+    q = S.normal_bf16_rows(S_, H * 192, 1.0, (seed, 801, S.T_Q)).reshape(1, S_, H, 192)
+    kv_d = torch.zeros((S_, 512), dtype=torch.bfloat16, device="cuda")
+    pe_d = torch.zeros((S_, 64), dtype=torch.bfloat16, device="cuda")
+    outs = []
+    for a, b in [(0, c1), (c1, S_)]:
+        binding.kv_append(dev_bf16(inp["kv_a"][a:b].reshape(1, b - a, 576)), dev(inp["kv_gamma"]),
+                          dev(cs[a:b].reshape(1, b - a, 32, 2)), dev(np.array([a], np.int32)), kv_d, pe_d, S_)
+        o, _ = binding.prefill_with_prefix(dev_bf16(q[:, a:b]), kv_d[:b].reshape(1, b, 512),
+                                           pe_d[:b].reshape(1, b, 64), dev_bf16(w))
+        outs.append(host_bits(o)[0])
+    torch.cuda.synchronize()
+    lat, kpe = O.kv_side(inp["kv_a"], inp["kv_gamma"], cs, staged=True)
+    oo, _ = O.prefill_causal(O.bf16_decode(q[0]), O.bf16_encode(lat), O.bf16_encode(kpe), w, SCALE,
+                             round_output=False)
+    assert_bf16_parity(np.concatenate(outs), oo, "chunked prefill out")
