@@ -57,11 +57,13 @@ def _lib():
         lib.mla_decode.argtypes = [dp, _I32, _P, _P, _P, _P, _P, _P, _I64, _P, _SZ, _P, _P, _P]
         lib.mla_prefill_workspace_size.argtypes = [dp, _I32, _I32, ctypes.POINTER(_SZ)]
         lib.mla_prefill.argtypes = [dp, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]
+        lib.mla_decode_sparse_workspace_size.argtypes = [dp, _I32, _I64, _I32, ctypes.POINTER(_SZ)]
+        lib.mla_decode_sparse.argtypes = [dp, _I32, _P, _P, _P, _P, _P, _P, _I64, _P, _I32, _P, _SZ, _P, _P, _P]
         lib.mla_prefill_with_prefix.argtypes = [dp, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]
         lib.mla_kv_append.argtypes = [dp, _I32, _I32, _P, _P, _P, _P, _P, _I64, _P, _P, _P]
         for f in ("mla_dims_default", "mla_query_path_workspace_size", "mla_query_path", "mla_decode_workspace_size",
                   "mla_decode", "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_with_prefix",
-                  "mla_kv_append"):
+                  "mla_kv_append", "mla_decode_sparse_workspace_size", "mla_decode_sparse"):
             getattr(lib, f).restype = ctypes.c_int
         lib.mla_status_string.argtypes = [ctypes.c_int]
         lib.mla_status_string.restype = ctypes.c_char_p
@@ -302,3 +304,55 @@ def kv_append(kv_a: torch.Tensor, kv_norm_w: torch.Tensor, rope_cs: torch.Tensor
     _check(_lib().mla_kv_append(ctypes.byref(d), B, T, _ptr(kv_a), _ptr(kv_norm_w), _ptr(rope_cs), _ptr(start_pos),
                                 _ptr(cache_row_offset), int(max_seqlen), _ptr(kv_cache), _ptr(pe_cache), _stream()),
            "mla_kv_append")
+
+
+def decode_sparse_workspace_size(n_heads: int, batch: int, max_seqlen: int, topk: int,
+                                 d: Optional[MlaDims] = None) -> int:
+    d = d or dims(n_heads)
+    n = _SZ(0)
+    _check(_lib().mla_decode_sparse_workspace_size(ctypes.byref(d), batch, max_seqlen, topk, ctypes.byref(n)),
+           "mla_decode_sparse_workspace_size")
+    return n.value
+
+
+def decode_sparse(q: torch.Tensor, wkv_b: torch.Tensor, kv_cache: torch.Tensor, pe_cache: torch.Tensor,
+                  cache_seqlens: torch.Tensor, max_seqlen: int, topk_indices: torch.Tensor,
+                  cache_row_offset: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                  d: Optional[MlaDims] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """decode() restricted to the positions topk_indices (int32 [B, k]) names for each sequence."""
+    _need(q, "q", torch.bfloat16)
+    if q.dim() != 3 or q.shape[2] != QK:
+        raise ValueError("q must be [B, H, 192]")
+    B, H = int(q.shape[0]), int(q.shape[1])
+    d = d or dims(H)
+    _need(wkv_b, "wkv_b", torch.bfloat16, (H * (NOPE + V_DIM), KV_LORA))
+    _need(kv_cache, "kv_cache", torch.bfloat16)
+    _need(pe_cache, "pe_cache", torch.bfloat16)
+    if kv_cache.shape[-1] != KV_LORA or pe_cache.shape[-1] != ROPE:
+        raise ValueError("kv_cache rows must be 512 wide and pe_cache rows 64 wide")
+    if kv_cache.numel() // KV_LORA != pe_cache.numel() // ROPE:
+        raise ValueError("kv_cache and pe_cache must hold the same number of rows")
+    _need(cache_seqlens, "cache_seqlens", torch.int32, (B,))
+    _need(topk_indices, "topk_indices", torch.int32)
+    if topk_indices.dim() != 2 or topk_indices.shape[0] != B:
+        raise ValueError("topk_indices must be [B, k]")
+    k = int(topk_indices.shape[1])
+    if cache_row_offset is not None:
+        _need(cache_row_offset, "cache_row_offset", torch.int64, (B,))
+    elif kv_cache.numel() // KV_LORA < B * max_seqlen:
+        raise ValueError("padded caches (no row offsets) need batch * max_seqlen rows")
+    need = decode_sparse_workspace_size(H, B, max_seqlen, k, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    if out is None:
+        out = torch.empty((B, H, V_DIM), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (B, H, V_DIM))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, H))
+    _check(_lib().mla_decode_sparse(ctypes.byref(d), B, _ptr(q), _ptr(wkv_b), _ptr(kv_cache), _ptr(pe_cache),
+                                    _ptr(cache_row_offset), _ptr(cache_seqlens), int(max_seqlen),
+                                    _ptr(topk_indices) if k else None, k, _ptr(workspace), workspace.numel(),
+                                    _ptr(out), _ptr(lse), _stream()), "mla_decode_sparse")
+    return out, lse

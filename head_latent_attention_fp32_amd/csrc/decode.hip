@@ -118,6 +118,39 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
+// 0. Top-k mode ("DeepSeek-V3.2-Exp · Attention update", mla-decode excerpt: the indexer's top-k
+//    positions of each sequence become a mask of 0 at those positions and -inf elsewhere, added to
+//    the scores). Block b keeps, in order, the entries of its list that name a position of the
+//    sequence (0 <= index < L_b) and counts them; the attention then runs over that many rows of
+//    sequence b, read through the compacted list. Entries outside [0, L_b) name nothing.
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void topk_compact_kernel(const int32_t* __restrict__ topk, int k,
+                                                           const int32_t* __restrict__ seqlens, int64_t max_seqlen,
+                                                           int32_t* __restrict__ list, int32_t* __restrict__ counts) {
+  __shared__ int wave_count[4];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t L = min<int64_t>(max<int64_t>(seqlens[b], 0), max_seqlen);
+  const int32_t* src = topk + static_cast<int64_t>(b) * k;
+  int32_t* dst = list + static_cast<int64_t>(b) * k;
+  int base = 0;
+  for (int j0 = 0; j0 < k; j0 += 256) {
+    const int j = j0 + static_cast<int>(threadIdx.x);
+    const int32_t idx = j < k ? src[j] : -1;
+    const bool keep = idx >= 0 && idx < L;
+    const uint64_t m = __ballot(keep);
+    if (lane == 0) wave_count[wave] = __popcll(m);
+    __syncthreads();
+    int off = base;
+    for (int w = 0; w < wave; ++w) off += wave_count[w];
+    if (keep) dst[off + __popcll(m & ((uint64_t(1) << lane) - 1))] = idx;
+    base += wave_count[0] + wave_count[1] + wave_count[2] + wave_count[3];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) counts[b] = base;
+}
+
+// ---------------------------------------------------------------------------------------------
 // 2. Split-KV attention over runs.
 //
 //    Block = 8 waves and 64 heads: head group hg covers heads [64 hg, 64 hg + 64); slots past
@@ -234,6 +267,8 @@ struct AttendCtx {
   const uint16_t* pe;
   const int64_t* row_offset;
   int64_t max_seqlen;
+  const int32_t* list;       // top-k mode: attended positions of each sequence, compacted; else null
+  int list_pitch;
   const int64_t* cum;
   int batch, n_heads, head0;
   int64_t g, start, end;
@@ -250,8 +285,9 @@ struct AttendCtx {
 
 struct Segment {
   int b, n_rows, n_tiles;
-  const uint16_t* kv_seg;   // first row of the segment
+  const uint16_t* kv_seg;   // first row of the segment (top-k mode: of the sequence)
   const uint16_t* pe_seg;
+  const int32_t* list_seg;  // top-k mode: the segment's positions
 };
 
 // First sequence of the run; then advance() steps through the sequences the run covers.
@@ -274,9 +310,11 @@ struct SegmentWalk {
     sg.b = b;
     sg.n_rows = static_cast<int>(seg_end - start);
     sg.n_tiles = (sg.n_rows + kTileTok - 1) / kTileTok;
-    const int64_t row0 = (c.row_offset ? c.row_offset[b] : static_cast<int64_t>(b) * c.max_seqlen) + t0;
+    const int64_t base = c.row_offset ? c.row_offset[b] : static_cast<int64_t>(b) * c.max_seqlen;
+    const int64_t row0 = c.list ? base : base + t0;
     sg.kv_seg = c.kv + row0 * kKvLora;
     sg.pe_seg = c.pe + row0 * kRope;
+    sg.list_seg = c.list ? c.list + static_cast<int64_t>(b) * c.list_pitch + t0 : nullptr;
     start = seg_end;
     ++b;
     while (b < c.batch && c.cum[b + 1] <= start) ++b;
@@ -303,6 +341,38 @@ __device__ __forceinline__ void issue_tile(const AttendCtx& c, const Segment& sg
 #pragma unroll
   for (int k = 0; k < 8; ++k) dma16(rk, dst + (v + 4 * k) * 1024, kv_voff[k]);
   dma16(rp, dst + kKvBytes + v * 1024, pe_voff);
+}
+
+// Top-k mode: the tile's rows are the cache rows of the positions list_seg[32 t .. 32 t + 31] of
+// the sequence (read with scalar loads: the list is uniform across the wave and never changes
+// during the kernel). Rows past the segment get a position one past the descriptors' range
+// (max_seqlen rows from the sequence's first), so they read as zeros. kv_chunk[k] and pe_chunk are
+// the lane's byte offsets within its row.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+__device__ __forceinline__ void issue_tile_gather(const AttendCtx& c, const Segment& sg, int t, const uint32_t* kv_chunk,
+                                                  uint32_t pe_chunk) {
+  const int v = c.wave & 3;
+  const int left = sg.n_rows - t * kTileTok;
+  const uint32_t past = static_cast<uint32_t>(c.max_seqlen);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(sg.kv_seg, past * 1024u);
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(sg.pe_seg, past * 128u);
+  const const_i32_ptr ti = (const_i32_ptr)(sg.list_seg + t * kTileTok);
+  const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)c.ring)) +
+                       (t % kStages) * kTileBytes;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int row = v + 4 * k;
+    const uint32_t pos = row < left ? static_cast<uint32_t>(ti[row]) : past;
+    dma16(rk, dst + row * 1024, pos * 1024u + kv_chunk[k]);
+  }
+  uint32_t ppos = past;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = 8 * v + j;
+    const uint32_t pos = row < left ? static_cast<uint32_t>(ti[row]) : past;
+    ppos = (c.lane >> 3) == j ? pos : ppos;
+  }
+  dma16(rp, dst + kKvBytes + v * 1024, ppos * 128u + pe_chunk);
 }
 
 // Score waves 0-3. Wave w = (kh, hh) = (w & 1, w >> 1) holds the query of the 32 heads of half hh
@@ -465,17 +535,22 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
 }
 
 // Value waves 4-7: O^T += V^T P^T for latent columns [128 w, 128 w + 128) of all 64 heads.
+template <bool kGather>
 __device__ __forceinline__ void value_role(const AttendCtx& c) {
   constexpr int L = 9;   // loads per tile
   const int w = c.wave & 3, lane = c.lane, r = lane & 15, grp = lane >> 4;
-  uint32_t kv_voff[8];
+  uint32_t kv_voff[8];   // byte offset of the lane's chunk (dense mode: from the tile's first row)
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int row = w + 4 * k;
-    kv_voff[k] = static_cast<uint32_t>(row * 1024 + ((lane ^ fk(row)) << 4));
+    kv_voff[k] = static_cast<uint32_t>((kGather ? 0 : row * 1024) + ((lane ^ fk(row)) << 4));
   }
   const int pe_row = 8 * w + (lane >> 3);
-  const uint32_t pe_voff = static_cast<uint32_t>(pe_row * 128 + (((lane & 7) ^ fp(pe_row)) << 4));
+  const uint32_t pe_voff = static_cast<uint32_t>((kGather ? 0 : pe_row * 128) + (((lane & 7) ^ fp(pe_row)) << 4));
+  auto issue = [&](const Segment& sg, int t) {
+    if (kGather) issue_tile_gather(c, sg, t, kv_voff, pe_voff);
+    else issue_tile(c, sg, t, kv_voff, pe_voff);
+  };
   // V^T: source row 4 grp + (r>>2) (+16), columns 16 (8 w + cb) + 4 (r&3) .. +3 at physical chunk
   // pair (8 w + cb) ^ (row & 7). P^T: head 16 hb + r, chunk grp.
   const int vrow = 4 * grp + (r >> 2);
@@ -489,7 +564,7 @@ __device__ __forceinline__ void value_role(const AttendCtx& c) {
   while (walk.next(c, sg)) {
     const int n_tiles = sg.n_tiles;
     int issued = 0;
-    while (issued < kStages && issued < n_tiles) issue_tile(c, sg, issued++, kv_voff, pe_voff);
+    while (issued < kStages && issued < n_tiles) issue(sg, issued++);
 
     f32x4 o[8][4];   // O^T[16 (8 w + cb) + 4 grp + j][16 hb + r]
 #pragma unroll
@@ -535,7 +610,7 @@ __device__ __forceinline__ void value_role(const AttendCtx& c) {
       // phase A: operand reads, then loads (bound by the load unit), while the score waves'
       // MFMAs own the pipes
       read_values(it);
-      if (issued < n_tiles && issued <= it + 3) issue_tile(c, sg, issued++, kv_voff, pe_voff);
+      if (issued < n_tiles && issued <= it + 3) issue(sg, issued++);
       lds_barrier();
       // phase B: the value MFMAs of tile it beside the softmax of tile it+1
       values(it);
@@ -559,9 +634,11 @@ __device__ __forceinline__ void value_role(const AttendCtx& c) {
   }
 }
 
+template <bool kGather>
 __global__ __launch_bounds__(512, 1) void attend_kernel(
     const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const uint16_t* __restrict__ pe, const int64_t* __restrict__ row_offset, int64_t max_seqlen,
+    const int32_t* __restrict__ list, int list_pitch,
     const Plan* __restrict__ plan, const int64_t* __restrict__ cum, int batch, int n_heads, float scale_log2,
     float* __restrict__ part_o, float* __restrict__ part_l) {
   // The blocks of the head groups of one run share blockIdx mod 8 -- the same XCD and its L2 --
@@ -582,6 +659,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(
 
   AttendCtx c;
   c.q_lat = q_lat; c.q = q; c.kv = kv; c.pe = pe; c.row_offset = row_offset; c.max_seqlen = max_seqlen;
+  c.list = kGather ? list : nullptr; c.list_pitch = list_pitch;
   c.cum = cum; c.batch = batch; c.n_heads = n_heads; c.head0 = hg * kBlockHeads;
   c.g = g; c.start = run_start(g, N, G); c.end = run_start(g + 1, N, G);
   c.scale_log2 = scale_log2; c.part_o = part_o; c.part_l = part_l;
@@ -589,7 +667,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: wave-derived values live in SGPRs
   c.lane = threadIdx.x & 63;
   if (c.wave < 4) score_role(c);
-  else value_role(c);
+  else value_role<kGather>(c);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -676,10 +754,11 @@ __global__ __launch_bounds__(256) void value_proj_kernel(
 
 }  // namespace
 
-DecodeLayout decode_layout(int n_heads, int batch, int64_t max_seqlen) {
+DecodeLayout decode_layout(int n_heads, int batch, int64_t max_seqlen, int topk) {
   DecodeLayout L{};
   L.min_unit_tokens = 256;
-  const int64_t upper = static_cast<int64_t>(batch) * max_seqlen;
+  // attended rows: at most max_seqlen per sequence, or topk in top-k mode (topk >= 0)
+  const int64_t upper = static_cast<int64_t>(batch) * (topk >= 0 ? topk : max_seqlen);
   int64_t units = (upper + L.min_unit_tokens - 1) / L.min_unit_tokens;
   // one block per compute unit: 256 CUs, shared by the head groups of a run
   const int64_t max_units = 256 / ((n_heads + 63) / 64);
@@ -694,14 +773,21 @@ DecodeLayout decode_layout(int n_heads, int batch, int64_t max_seqlen) {
   L.part_o_off = off; off = align_up(off + slots * H * kKvLora * sizeof(float));
   L.part_l_off = off; off = align_up(off + slots * H * sizeof(float));
   L.olat_off = off;   off = align_up(off + B * H * kKvLora * sizeof(uint16_t));
+  L.list_off = L.count_off = 0;
+  if (topk >= 0) {
+    // 64 entries of slack: the attention's scalar loads of a last partial tile may read past a
+    // sequence's count (those values are never used)
+    L.list_off = off;  off = align_up(off + (B * static_cast<size_t>(topk) + 64) * sizeof(int32_t));
+    L.count_off = off; off = align_up(off + B * sizeof(int32_t));
+  }
   L.total = off;
   return L;
 }
 
 hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16_t* wkv_b,
                          const uint16_t* kv_cache, const uint16_t* pe_cache, const int64_t* row_offset,
-                         const int32_t* seqlens, int64_t max_seqlen, void* workspace,
-                         const DecodeLayout& lay, uint16_t* out, float* lse, float scale,
+                         const int32_t* seqlens, int64_t max_seqlen, const int32_t* topk_indices, int topk,
+                         void* workspace, const DecodeLayout& lay, uint16_t* out, float* lse, float scale,
                          hipStream_t stream, hipEvent_t* ev) {
   char* ws = static_cast<char*>(workspace);
   Plan* plan = reinterpret_cast<Plan*>(ws + lay.plan_off);
@@ -712,15 +798,26 @@ hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16
   uint16_t* o_lat = reinterpret_cast<uint16_t*>(ws + lay.olat_off);
   const float scale_log2 = scale * kLog2e;
 
+  const bool sparse = topk >= 0;
+  int32_t* list = sparse ? reinterpret_cast<int32_t*>(ws + lay.list_off) : nullptr;
+  int32_t* counts = sparse ? reinterpret_cast<int32_t*>(ws + lay.count_off) : nullptr;
+
   mark(ev, 0, stream);
+  if (sparse) topk_compact_kernel<<<batch, 256, 0, stream>>>(topk_indices, topk, seqlens, max_seqlen, list, counts);
+  // the run plan covers the attended rows: L_b per sequence, or the count of its top-k positions
   absorb_plan_kernel<<<dim3(n_heads, kKvLora / 64), 256, 0, stream>>>(
-      q, wkv_b, batch, n_heads, q_lat, seqlens, max_seqlen, lay.units, lay.min_unit_tokens, plan, cum);
+      q, wkv_b, batch, n_heads, q_lat, sparse ? counts : seqlens, sparse ? topk : max_seqlen, lay.units,
+      lay.min_unit_tokens, plan, cum);
   mark(ev, 1, stream);
   {
     const int n_groups = (n_heads + 63) / 64;
     const int blocks = (lay.units + 7) / 8 * 8 * n_groups;
-    attend_kernel<<<blocks, 512, 0, stream>>>(q_lat, q, kv_cache, pe_cache, row_offset, max_seqlen, plan, cum, batch,
-                                              n_heads, scale_log2, part_o, part_l);
+    if (sparse)
+      attend_kernel<true><<<blocks, 512, 0, stream>>>(q_lat, q, kv_cache, pe_cache, row_offset, max_seqlen, list, topk,
+                                                      plan, cum, batch, n_heads, scale_log2, part_o, part_l);
+    else
+      attend_kernel<false><<<blocks, 512, 0, stream>>>(q_lat, q, kv_cache, pe_cache, row_offset, max_seqlen, nullptr,
+                                                       0, plan, cum, batch, n_heads, scale_log2, part_o, part_l);
   }
   mark(ev, 2, stream);
   combine_kernel<<<dim3(batch, n_heads / 16), 256, 0, stream>>>(plan, cum, n_heads, part_o, part_l, o_lat, lse);

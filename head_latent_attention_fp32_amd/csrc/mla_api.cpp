@@ -28,6 +28,8 @@ constexpr int64_t kMaxSeqlen = int64_t(1) << 21;
 // The largest query-path token count: the product's grid has ceil(n / 128) blocks in y (at most
 // 65535).
 constexpr int64_t kMaxTokens = int64_t(65535) * 128;
+// The longest top-k list of one sequence (a list of one sequence's positions).
+constexpr int32_t kMaxTopk = 1 << 21;
 
 }  // namespace
 
@@ -108,9 +110,53 @@ mla_status_t mla_decode_ex(const mla_dims_t* dims, int32_t batch, const uint16_t
   const mla::DecodeLayout lay = mla::decode_layout(dims->n_heads, batch, max_seqlen);
   if (workspace_bytes < lay.total) return MLA_ERR_WORKSPACE;
   hipError_t e = mla::launch_decode(dims->n_heads, batch, q, wkv_b, kv_cache, pe_cache, cache_row_offset,
-                                    cache_seqlens, max_seqlen, workspace, lay, out, lse, dims->softmax_scale, stream,
-                                    stage_events);
+                                    cache_seqlens, max_seqlen, nullptr, -1, workspace, lay, out, lse,
+                                    dims->softmax_scale, stream, stage_events);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_decode_sparse_workspace_size(const mla_dims_t* dims, int32_t batch, int64_t max_seqlen,
+                                              int32_t topk, size_t* bytes) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!bytes) return MLA_ERR_INVALID_ARG;
+  if (batch < 0 || batch > kMaxBatch || max_seqlen < 0 || max_seqlen > kMaxSeqlen || topk < 0 || topk > kMaxTopk)
+    return MLA_ERR_SHAPE;
+  *bytes = batch == 0 ? 0 : mla::decode_layout(dims->n_heads, batch, max_seqlen, topk).total;
+  return MLA_OK;
+}
+
+mla_status_t mla_decode_sparse_ex(const mla_dims_t* dims, int32_t batch, const uint16_t* q, const uint16_t* wkv_b,
+                                  const uint16_t* kv_cache, const uint16_t* pe_cache,
+                                  const int64_t* cache_row_offset, const int32_t* cache_seqlens, int64_t max_seqlen,
+                                  const int32_t* topk_indices, int32_t topk, void* workspace, size_t workspace_bytes,
+                                  uint16_t* out, float* lse, hipStream_t stream, hipEvent_t* stage_events) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || batch > kMaxBatch || max_seqlen < 0 || max_seqlen > kMaxSeqlen || topk < 0 || topk > kMaxTopk)
+    return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!q || !wkv_b || !kv_cache || !pe_cache || !cache_seqlens || !workspace || !out || (topk > 0 && !topk_indices))
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(wkv_b) || !aligned16(kv_cache) || !aligned16(pe_cache) ||
+      !aligned16(cache_seqlens) || !aligned16(workspace) || !aligned16(out) || (topk > 0 && !aligned16(topk_indices)) ||
+      (cache_row_offset && !aligned16(cache_row_offset)) || (lse && !aligned16(lse)))
+    return MLA_ERR_ALIGNMENT;
+  const mla::DecodeLayout lay = mla::decode_layout(dims->n_heads, batch, max_seqlen, topk);
+  if (workspace_bytes < lay.total) return MLA_ERR_WORKSPACE;
+  hipError_t e = mla::launch_decode(dims->n_heads, batch, q, wkv_b, kv_cache, pe_cache, cache_row_offset,
+                                    cache_seqlens, max_seqlen, topk_indices, topk, workspace, lay, out, lse,
+                                    dims->softmax_scale, stream, stage_events);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_decode_sparse(const mla_dims_t* dims, int32_t batch, const uint16_t* q, const uint16_t* wkv_b,
+                               const uint16_t* kv_cache, const uint16_t* pe_cache, const int64_t* cache_row_offset,
+                               const int32_t* cache_seqlens, int64_t max_seqlen, const int32_t* topk_indices,
+                               int32_t topk, void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
+                               hipStream_t stream) {
+  return mla_decode_sparse_ex(dims, batch, q, wkv_b, kv_cache, pe_cache, cache_row_offset, cache_seqlens, max_seqlen,
+                              topk_indices, topk, workspace, workspace_bytes, out, lse, stream, nullptr);
 }
 
 mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, const uint16_t* q, const uint16_t* wkv_b,

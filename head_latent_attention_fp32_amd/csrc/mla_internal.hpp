@@ -18,12 +18,14 @@ inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a
 // Split-KV decode. The cached tokens of all sequences, taken back to back, are cut into at most
 // `units` equal runs; one workgroup attends one run (which may span several sequences) and writes
 // one partial result per (run, sequence) pair it touches, in slot run + sequence.
+// Top-k mode (topk >= 0) attends, per sequence, only the positions its list names: the list is
+// first compacted (list_off, count_off) and the runs cover the compacted positions.
 struct DecodeLayout {
   int units;            // workgroups launched for the split attention
   int min_unit_tokens;  // fewer tokens than this per run are not worth a partial
-  size_t plan_off, cum_off, qlat_off, part_o_off, part_l_off, olat_off, total;
+  size_t plan_off, cum_off, qlat_off, part_o_off, part_l_off, olat_off, list_off, count_off, total;
 };
-DecodeLayout decode_layout(int n_heads, int batch, int64_t max_seqlen);
+DecodeLayout decode_layout(int n_heads, int batch, int64_t max_seqlen, int topk = -1);
 
 struct PrefillLayout {
   int64_t t_pad;        // sequence length padded to the key tile
@@ -43,10 +45,11 @@ hipError_t launch_query_path(int n_heads, int64_t n_tokens, const uint16_t* q_la
                              void* workspace, const QueryLayout& lay, float eps, hipStream_t stream,
                              hipEvent_t* ev);
 
+// topk < 0: dense decode; else top-k mode over int32 [batch, topk] positions topk_indices.
 hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16_t* wkv_b,
                          const uint16_t* kv_cache, const uint16_t* pe_cache, const int64_t* row_offset,
-                         const int32_t* seqlens, int64_t max_seqlen, void* workspace,
-                         const DecodeLayout& lay, uint16_t* out, float* lse, float scale,
+                         const int32_t* seqlens, int64_t max_seqlen, const int32_t* topk_indices, int topk,
+                         void* workspace, const DecodeLayout& lay, uint16_t* out, float* lse, float scale,
                          hipStream_t stream, hipEvent_t* ev);
 
 // Causal prefill of the last q_len of kv_len positions (q_len <= kv_len); the workspace layout is

@@ -150,6 +150,30 @@ mla_status_t mla_prefill(const mla_dims_t* dims, int32_t batch, int32_t seqlen, 
                          void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
                          hipStream_t stream);
 
+/* Bytes of device workspace mla_decode_sparse needs for `batch` sequences and lists of `topk`
+ * entries (host-only, no HIP calls). topk in [0, 2^21]. */
+mla_status_t mla_decode_sparse_workspace_size(const mla_dims_t* dims, int32_t batch, int64_t max_seqlen,
+                                              int32_t topk, size_t* bytes);
+
+/* Absorbed decode restricted to each sequence's top-k positions ("DeepSeek-V3.2-Exp · Attention
+ * update", mla-decode excerpt: the indexer's top-k positions give a mask of 0 at those positions and
+ * -inf elsewhere, added to the scores before the softmax). Same computation and arguments as
+ * mla_decode, over the rows of sequence b at the positions topk_indices[b, :] names:
+ *   topk_indices  int32 [batch, topk], device: positions within sequence b (0-based, as cache rows
+ *                 cache_row_offset[b] + position). Entries outside [0, L_b) name no position (e.g.
+ *                 -1 padding of a list longer than the sequence). The positions of one list must be
+ *                 distinct, as a top-k selection's are: a position listed twice is attended twice
+ *                 (the mask of the excerpt would count it once).
+ *   topk          entries per list, 0 .. 2^21
+ *   workspace     >= mla_decode_sparse_workspace_size(dims, batch, max_seqlen, topk) bytes
+ * The order of a list does not matter beyond floating-point summation order. A sequence with no
+ * valid entry gets out = 0, lse = -inf. */
+mla_status_t mla_decode_sparse(const mla_dims_t* dims, int32_t batch, const uint16_t* q, const uint16_t* wkv_b,
+                               const uint16_t* kv_cache, const uint16_t* pe_cache, const int64_t* cache_row_offset,
+                               const int32_t* cache_seqlens, int64_t max_seqlen, const int32_t* topk_indices,
+                               int32_t topk, void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
+                               hipStream_t stream);
+
 /* Causal prefill of new tokens over a cached prefix ("Kimi-K2 · value_states", mla-prefill excerpt:
  * once past keys join the new ones the weights and mask are (q_len, kv_seq_len)). The sequence has
  * kv_len positions; the queries are its last q_len (q_len <= kv_len), query i at position
@@ -198,6 +222,7 @@ mla_status_t mla_kv_append(const mla_dims_t* dims, int32_t batch, int32_t seqlen
  *   mla_query_path_ex: 2 stages (RMSNorm pass -- empty when fused into the product, 32 tokens or
  *                      fewer --, product + RoPE)
  *   mla_decode_ex:     4 stages (absorb + run plan, split-KV attention, log-sum-exp combine, value projection)
+ *   mla_decode_sparse_ex: the same 4 stages, the first also compacting the top-k lists
  *   mla_prefill_ex, mla_prefill_with_prefix_ex: 2 stages (latent expansion, causal attention) */
 mla_status_t mla_query_path_ex(const mla_dims_t* dims, int64_t n_tokens,
                                const uint16_t* q_latent, const float* q_norm_w, const uint16_t* wq_b,
@@ -213,6 +238,11 @@ mla_status_t mla_prefill_ex(const mla_dims_t* dims, int32_t batch, int32_t seqle
                             const uint16_t* kv_latent, const uint16_t* k_pe, const uint16_t* wkv_b,
                             void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
                             hipStream_t stream, hipEvent_t* stage_events);
+mla_status_t mla_decode_sparse_ex(const mla_dims_t* dims, int32_t batch, const uint16_t* q, const uint16_t* wkv_b,
+                                  const uint16_t* kv_cache, const uint16_t* pe_cache, const int64_t* cache_row_offset,
+                                  const int32_t* cache_seqlens, int64_t max_seqlen, const int32_t* topk_indices,
+                                  int32_t topk, void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
+                                  hipStream_t stream, hipEvent_t* stage_events);
 mla_status_t mla_prefill_with_prefix_ex(const mla_dims_t* dims, int32_t batch, int32_t q_len, int32_t kv_len,
                                         const uint16_t* q, const uint16_t* kv_latent, const uint16_t* k_pe,
                                         const uint16_t* wkv_b, void* workspace, size_t workspace_bytes,

@@ -29,7 +29,8 @@ def test_header_declares_the_three_entry_points():
     names = declared_functions()
     for f in ("mla_query_path", "mla_query_path_workspace_size", "mla_decode", "mla_prefill",
               "mla_decode_workspace_size",
-              "mla_prefill_workspace_size", "mla_status_string", "mla_prefill_with_prefix", "mla_kv_append"):
+              "mla_prefill_workspace_size", "mla_status_string", "mla_prefill_with_prefix", "mla_kv_append",
+              "mla_decode_sparse", "mla_decode_sparse_workspace_size"):
         assert f in names
 
 
@@ -175,6 +176,29 @@ def test_kv_append_validation():
     d2 = _dims()
     d2.kv_lora_rank = 256
     assert ap(*args(dims=ctypes.byref(d2))) == 2
+
+
+def test_decode_sparse_validation():
+    lib = _lib()
+    d = _dims()
+    n = ctypes.c_size_t(0)
+    assert lib.mla_decode_sparse_workspace_size(ctypes.byref(d), 32, 4096, 2048, ctypes.byref(n)) == 0
+    need = n.value
+    m = ctypes.c_size_t(0)
+    assert lib.mla_decode_workspace_size(ctypes.byref(d), 32, 4096, ctypes.byref(m)) == 0
+    assert need > 32 * 2048 * 4                        # holds the compacted lists
+    assert lib.mla_decode_sparse_workspace_size(ctypes.byref(d), 32, 4096, -1, ctypes.byref(n)) == 3
+    assert lib.mla_decode_sparse_workspace_size(ctypes.byref(d), 32, 4096, (1 << 21) + 1, ctypes.byref(n)) == 3
+    sp = lib.mla_decode_sparse
+    args = lambda **kw: [kw.get(k, v) for k, v in [
+        ("dims", ctypes.byref(d)), ("batch", 32), ("q", FAKE), ("w", FAKE), ("kv", FAKE), ("pe", FAKE),
+        ("off", None), ("lens", FAKE), ("maxl", 4096), ("idx", FAKE), ("k", 2048), ("ws", FAKE), ("wsb", need),
+        ("out", FAKE), ("lse", None), ("stream", None)]]
+    assert sp(*args(batch=0, q=None)) == 0
+    assert sp(*args(idx=None)) == 1
+    assert sp(*args(k=-3)) == 3
+    assert sp(*args(idx=MIS)) == 4
+    assert sp(*args(wsb=need - 1)) == 5
 
 
 def test_status_strings():

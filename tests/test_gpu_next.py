@@ -173,3 +173,89 @@ def test_chunked_prefill_on_own_cache():
     oo, _ = O.prefill_causal(O.bf16_decode(q[0]), O.bf16_encode(lat), O.bf16_encode(kpe), w, SCALE,
                              round_output=False)
     assert_bf16_parity(np.concatenate(outs), oo, "chunked prefill out")
+
+
+# ----------------------------------------------------------------------------------- top-k decode
+def _selected(idx, L):
+    idx = np.asarray(idx, np.int64)
+    return np.unique(idx[(idx >= 0) & (idx < L)])
+
+
+def _check_sparse(case, q_bits, d, topk, out_bits, lse, ids):
+    qv = O.bf16_decode(q_bits)
+    lens = np.clip(d["lengths"].astype(np.int64), 0, int(case.max_seqlen))
+    oo, lo = O.decode_topk_batch(qv, d["wkv_b"], d["kv_cache"], d["pe_cache"], d["row_offset"], lens, topk, SCALE,
+                                 batch_ids=ids, round_output=False)
+    assert_bf16_parity(out_bits[ids], oo, "out")
+    mags = []
+    for b in ids:
+        r0 = int(d["row_offset"][b])
+        rows = r0 + _selected(topk[b], lens[b])
+        mags.append(O.decode_score_magnitude(qv[b], d["wkv_b"], d["kv_cache"][rows], d["pe_cache"][rows], SCALE))
+    assert_f32_parity(lse[ids], lo, "lse", magnitude=np.stack(mags))
+
+
+def _run_sparse(case, q_bits, d, topk):
+    B, H = case.batch, case.n_heads
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    out, _ = binding.decode_sparse(dev_bf16(q_bits), dev_bf16(d["wkv_b"]), dev_bf16(d["kv_cache"]),
+                                   dev_bf16(d["pe_cache"]), dev(d["lengths"]), int(case.max_seqlen),
+                                   dev(np.ascontiguousarray(topk, np.int32)),
+                                   cache_row_offset=None if case.layout == "padded" else dev(d["row_offset"]), lse=lse)
+    torch.cuda.synchronize()
+    return host_bits(out), lse.cpu().numpy()
+
+
+SPARSE_SMALL = [
+    (16, [1], 1, "padded"), (64, [100], 33, "padded"), (64, [40, 0, 300], 64, "padded"),
+    (128, [1000, 2, 64], 200, "packed"), (32, [500, 37], 37, "packed"), (128, [5000], 2048, "padded"),
+]
+
+
+@pytest.mark.parametrize("H,lens,k,layout", SPARSE_SMALL)
+def test_decode_sparse_parity(H, lens, k, layout):
+    say(f"decode_sparse H={H} lens={lens} k={k} layout={layout}")
+    case = S.DecodeCase("t", 900 + H + len(lens) + k, H, np.array(lens, np.int32), layout=layout,
+                        max_seqlen=max(max(lens), 1))
+    d = S.decode_inputs(case, seed=9, with_q_latent=False)
+    q = S.decode_query(case, seed=9)
+    topk = S.topk_indices(case.lengths, k, seed=9, case_id=case.case_id)
+    # entries that name no position: past the sequence (the padding rows hold NaN) and negative
+    rng = np.random.default_rng(k)
+    for b, L in enumerate(lens):
+        free = np.flatnonzero(topk[b] == -1)
+        bad = np.array([L, L + 1, L + 1000, -5, 2 ** 31 - 1], np.int64)
+        topk[b, free[: len(bad)]] = bad[: len(free)]
+        rng.shuffle(topk[b])
+    out, lse = _run_sparse(case, q, d, topk)
+    _check_sparse(case, q, d, topk, out, lse, list(range(case.batch)))
+
+
+def test_decode_sparse_empty_lists_and_full_lists():
+    case = S.DecodeCase("t", 950, 64, np.array([0, 50, 7], np.int32), max_seqlen=50)
+    d = S.decode_inputs(case, seed=10, with_q_latent=False)
+    q = S.decode_query(case, seed=10)
+    # k = 0: nothing selected anywhere
+    out, lse = _run_sparse(case, q, d, np.zeros((3, 0), np.int32))
+    assert np.all(O.bf16_decode(out) == 0) and np.all(np.isneginf(lse))
+    # every position listed: the dense decode
+    topk = S.topk_indices(case.lengths, 50, seed=10, case_id=950)
+    out_s, lse_s = _run_sparse(case, q, d, topk)
+    lse_d = torch.empty((3, 64), dtype=torch.float32, device="cuda")
+    out_d, _ = binding.decode(dev_bf16(q), dev_bf16(d["wkv_b"]), dev_bf16(d["kv_cache"]), dev_bf16(d["pe_cache"]),
+                              dev(d["lengths"]), 50, lse=lse_d)
+    torch.cuda.synchronize()
+    _check_sparse(case, q, d, topk, out_s, lse_s, [0, 1, 2])
+    np.testing.assert_allclose(O.bf16_decode(out_s), O.bf16_decode(host_bits(out_d)), rtol=0, atol=0.05)
+
+
+@pytest.mark.slow
+def test_decode_sparse_config1_top2048_sampled():
+    """32 sequences of 4096 cached positions, 2048 of them selected per sequence."""
+    case = S.workload(1)
+    d = S.decode_inputs(case, seed=0, with_q_latent=False)
+    q = S.decode_query(case, seed=0)
+    topk = S.topk_indices(case.lengths, 2048, seed=0, case_id=case.case_id)
+    say(f"decode_sparse {case.name} k=2048: oracle on sequences 0, 13, 31")
+    out, lse = _run_sparse(case, q, d, topk)
+    _check_sparse(case, q, d, topk, out, lse, [0, 13, 31])
