@@ -59,11 +59,14 @@ def _lib():
         lib.mla_prefill.argtypes = [dp, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]
         lib.mla_decode_sparse_workspace_size.argtypes = [dp, _I32, _I64, _I32, ctypes.POINTER(_SZ)]
         lib.mla_decode_sparse.argtypes = [dp, _I32, _P, _P, _P, _P, _P, _P, _I64, _P, _I32, _P, _SZ, _P, _P, _P]
+        lib.mla_output_proj_workspace_size.argtypes = [dp, _I64, _I32, ctypes.POINTER(_SZ)]
+        lib.mla_output_proj.argtypes = [dp, _I64, _I32, _P, _P, _P, _SZ, _P, _P]
         lib.mla_prefill_with_prefix.argtypes = [dp, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]
         lib.mla_kv_append.argtypes = [dp, _I32, _I32, _P, _P, _P, _P, _P, _I64, _P, _P, _P]
         for f in ("mla_dims_default", "mla_query_path_workspace_size", "mla_query_path", "mla_decode_workspace_size",
                   "mla_decode", "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_with_prefix",
-                  "mla_kv_append", "mla_decode_sparse_workspace_size", "mla_decode_sparse"):
+                  "mla_kv_append", "mla_decode_sparse_workspace_size", "mla_decode_sparse",
+                  "mla_output_proj_workspace_size", "mla_output_proj"):
             getattr(lib, f).restype = ctypes.c_int
         lib.mla_status_string.argtypes = [ctypes.c_int]
         lib.mla_status_string.restype = ctypes.c_char_p
@@ -356,3 +359,41 @@ def decode_sparse(q: torch.Tensor, wkv_b: torch.Tensor, kv_cache: torch.Tensor, 
                                     _ptr(topk_indices) if k else None, k, _ptr(workspace), workspace.numel(),
                                     _ptr(out), _ptr(lse), _stream()), "mla_decode_sparse")
     return out, lse
+
+
+def output_proj_workspace_size(n_heads: int, n_tokens: int, dim: int, d: Optional[MlaDims] = None) -> int:
+    d = d or dims(n_heads)
+    n = _SZ(0)
+    _check(_lib().mla_output_proj_workspace_size(ctypes.byref(d), n_tokens, dim, ctypes.byref(n)),
+           "mla_output_proj_workspace_size")
+    return n.value
+
+
+def output_proj(x: torch.Tensor, wo: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                y: Optional[torch.Tensor] = None, d: Optional[MlaDims] = None) -> torch.Tensor:
+    """x bf16 [..., H, 128] or [..., H*128]; wo bf16 [dim, H*128] -> y bf16 [..., dim]."""
+    _need(x, "x", torch.bfloat16)
+    _need(wo, "wo", torch.bfloat16)
+    if wo.dim() != 2 or wo.shape[1] % V_DIM:
+        raise ValueError("wo must be [dim, H*128]")
+    dim, K = int(wo.shape[0]), int(wo.shape[1])
+    H = K // V_DIM
+    d = d or dims(H)
+    if x.numel() % K:
+        raise ValueError("x must hold H*128 features per token")
+    n = x.numel() // K
+    lead = tuple(x.shape[:-2]) if x.shape[-1] == V_DIM and x.dim() >= 2 and x.shape[-2] == H else tuple(x.shape[:-1])
+    need = output_proj_workspace_size(H, n, dim, d)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
+    if y is None:
+        y = torch.empty(lead + (dim,), dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", torch.bfloat16)
+    if y.numel() != n * dim:
+        raise ValueError("y must be [n_tokens, dim]")
+    _check(_lib().mla_output_proj(ctypes.byref(d), n, dim, _ptr(x), _ptr(wo), _ptr(workspace),
+                                  0 if workspace is None else workspace.numel(), _ptr(y), _stream()),
+           "mla_output_proj")
+    return y

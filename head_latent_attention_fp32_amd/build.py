@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla.so")
-SOURCES = ["mla_api.cpp", "query_path.hip", "decode.hip", "prefill.hip", "kv_side.hip"]
+SOURCES = ["mla_api.cpp", "query_path.hip", "decode.hip", "prefill.hip", "kv_side.hip", "out_proj.hip"]
 ARCH = "gfx950"
 
 COMMON = [

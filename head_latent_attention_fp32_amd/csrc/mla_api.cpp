@@ -28,6 +28,9 @@ constexpr int64_t kMaxSeqlen = int64_t(1) << 21;
 // The largest query-path token count: the product's grid has ceil(n / 128) blocks in y (at most
 // 65535).
 constexpr int64_t kMaxTokens = int64_t(65535) * 128;
+// Output projection: the token and weight matrices are addressed through buffer descriptors with
+// 32-bit byte ranges (elements of 2 bytes).
+constexpr int64_t kMaxOutElems = (int64_t(1) << 31) - 1;
 // The longest top-k list of one sequence (a list of one sequence's positions).
 constexpr int32_t kMaxTopk = 1 << 21;
 
@@ -246,6 +249,42 @@ mla_status_t mla_prefill(const mla_dims_t* dims, int32_t batch, int32_t seqlen, 
                          size_t workspace_bytes, uint16_t* out, float* lse, hipStream_t stream) {
   return mla_prefill_ex(dims, batch, seqlen, q, kv_latent, k_pe, wkv_b, workspace, workspace_bytes, out, lse, stream,
                         nullptr);
+}
+
+mla_status_t mla_output_proj_workspace_size(const mla_dims_t* dims, int64_t n_tokens, int32_t dim, size_t* bytes) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!bytes) return MLA_ERR_INVALID_ARG;
+  const int64_t K = static_cast<int64_t>(dims->n_heads) * dims->v_head_dim;
+  if (n_tokens < 0 || dim <= 0 || dim % 64 != 0 || n_tokens * K > kMaxOutElems || dim * K > kMaxOutElems)
+    return MLA_ERR_SHAPE;
+  *bytes = n_tokens == 0 ? 0 : mla::out_proj_layout(dims->n_heads, n_tokens, dim).total;
+  return MLA_OK;
+}
+
+mla_status_t mla_output_proj_ex(const mla_dims_t* dims, int64_t n_tokens, int32_t dim, const uint16_t* x,
+                                const uint16_t* wo, void* workspace, size_t workspace_bytes, uint16_t* y,
+                                hipStream_t stream, hipEvent_t* stage_events) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  const int64_t K = static_cast<int64_t>(dims->n_heads) * dims->v_head_dim;
+  if (n_tokens < 0 || dim <= 0 || dim % 64 != 0 || n_tokens * K > kMaxOutElems || dim * K > kMaxOutElems)
+    return MLA_ERR_SHAPE;
+  if (n_tokens == 0) return MLA_OK;
+  if (!x || !wo || !y) return MLA_ERR_INVALID_ARG;
+  const mla::OutProjLayout lay = mla::out_proj_layout(dims->n_heads, n_tokens, dim);
+  if (lay.total > 0 && !workspace) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(wo) || !aligned16(y) || (workspace && !aligned16(workspace)))
+    return MLA_ERR_ALIGNMENT;
+  if (workspace_bytes < lay.total) return MLA_ERR_WORKSPACE;
+  hipError_t e = mla::launch_out_proj(dims->n_heads, n_tokens, dim, x, wo, workspace, lay, y, stream, stage_events);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_output_proj(const mla_dims_t* dims, int64_t n_tokens, int32_t dim, const uint16_t* x,
+                             const uint16_t* wo, void* workspace, size_t workspace_bytes, uint16_t* y,
+                             hipStream_t stream) {
+  return mla_output_proj_ex(dims, n_tokens, dim, x, wo, workspace, workspace_bytes, y, stream, nullptr);
 }
 
 const char* mla_status_string(mla_status_t s) {

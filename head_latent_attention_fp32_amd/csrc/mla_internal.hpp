@@ -59,6 +59,18 @@ hipError_t launch_prefill(int n_heads, int batch, int q_len, int kv_len, const u
                           const PrefillLayout& lay, uint16_t* out, float* lse, float scale,
                           hipStream_t stream, hipEvent_t* ev);
 
+// Output projection: up to kOutSmallTokens tokens stream wo, more use the tiled GEMM; either runs
+// in `slices` K-slices whose fp32 partials (workspace, slices > 1) a second kernel sums.
+constexpr int kOutSmallTokens = 64;
+struct OutProjLayout {
+  int slices;
+  size_t total;
+};
+OutProjLayout out_proj_layout(int n_heads, int64_t n_tokens, int dim);
+hipError_t launch_out_proj(int n_heads, int64_t n_tokens, int dim, const uint16_t* x, const uint16_t* wo,
+                           void* workspace, const OutProjLayout& lay, uint16_t* y, hipStream_t stream,
+                           hipEvent_t* ev);
+
 hipError_t launch_kv_append(int batch, int seqlen, const uint16_t* kv_a, const float* kv_norm_w,
                             const float* rope_cs, const int32_t* start_pos, const int64_t* row_offset,
                             int64_t max_seqlen, float eps, uint16_t* kv_cache, uint16_t* pe_cache,

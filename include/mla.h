@@ -215,6 +215,23 @@ mla_status_t mla_kv_append(const mla_dims_t* dims, int32_t batch, int32_t seqlen
                            const int64_t* cache_row_offset, int64_t max_seqlen, uint16_t* kv_cache,
                            uint16_t* pe_cache, hipStream_t stream);
 
+/* Bytes of device workspace mla_output_proj needs (host-only, no HIP calls). */
+mla_status_t mla_output_proj_workspace_size(const mla_dims_t* dims, int64_t n_tokens, int32_t dim, size_t* bytes);
+
+/* Output projection ("DeepSeek-V3.2-Exp · Attention update", mla-output excerpt and the update's
+ * shape [B, 1, 7168]; "DeepSeek-V3.2-Exp · Query heads", MLA __init__: wo maps n_heads * v_head_dim
+ * features to the model width):
+ *   y[m, j] = bf16(sum_f x[m, f] wo[j, f]),  f = h*128 + d  (the head outputs flattened head-major)
+ *   x     bf16 [n_tokens, n_heads*128]   attention outputs, e.g. mla_decode / mla_prefill `out`
+ *   wo    bf16 [dim, n_heads*128]        output x input, as a Linear stores its weight
+ *   y     bf16 [n_tokens, dim]
+ *   dim   model width, a positive multiple of 64 (7168 for DeepSeek-V3.2)
+ *   workspace >= mla_output_proj_workspace_size bytes (NULL allowed when that is 0)
+ * n_tokens * n_heads * 128 and dim * n_heads * 128 must stay below 2^31 (else MLA_ERR_SHAPE). */
+mla_status_t mla_output_proj(const mla_dims_t* dims, int64_t n_tokens, int32_t dim, const uint16_t* x,
+                             const uint16_t* wo, void* workspace, size_t workspace_bytes, uint16_t* y,
+                             hipStream_t stream);
+
 /* Instrumented variants: identical work, plus hipEventRecord of caller-created events on `stream`
  * at the boundaries of the library's kernel stages, so a caller can time each stage on the stream
  * it runs on. stage_events is NULL or an array of (number of stages + 1) events, any of which may be
@@ -223,6 +240,7 @@ mla_status_t mla_kv_append(const mla_dims_t* dims, int32_t batch, int32_t seqlen
  *                      fewer --, product + RoPE)
  *   mla_decode_ex:     4 stages (absorb + run plan, split-KV attention, log-sum-exp combine, value projection)
  *   mla_decode_sparse_ex: the same 4 stages, the first also compacting the top-k lists
+ *   mla_output_proj_ex: 2 stages (product, sum of the K-slice partials -- empty above 64 tokens)
  *   mla_prefill_ex, mla_prefill_with_prefix_ex: 2 stages (latent expansion, causal attention) */
 mla_status_t mla_query_path_ex(const mla_dims_t* dims, int64_t n_tokens,
                                const uint16_t* q_latent, const float* q_norm_w, const uint16_t* wq_b,
@@ -243,6 +261,9 @@ mla_status_t mla_decode_sparse_ex(const mla_dims_t* dims, int32_t batch, const u
                                   const int32_t* cache_seqlens, int64_t max_seqlen, const int32_t* topk_indices,
                                   int32_t topk, void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
                                   hipStream_t stream, hipEvent_t* stage_events);
+mla_status_t mla_output_proj_ex(const mla_dims_t* dims, int64_t n_tokens, int32_t dim, const uint16_t* x,
+                                const uint16_t* wo, void* workspace, size_t workspace_bytes, uint16_t* y,
+                                hipStream_t stream, hipEvent_t* stage_events);
 mla_status_t mla_prefill_with_prefix_ex(const mla_dims_t* dims, int32_t batch, int32_t q_len, int32_t kv_len,
                                         const uint16_t* q, const uint16_t* kv_latent, const uint16_t* k_pe,
                                         const uint16_t* wkv_b, void* workspace, size_t workspace_bytes,

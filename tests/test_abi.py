@@ -30,7 +30,8 @@ def test_header_declares_the_three_entry_points():
     for f in ("mla_query_path", "mla_query_path_workspace_size", "mla_decode", "mla_prefill",
               "mla_decode_workspace_size",
               "mla_prefill_workspace_size", "mla_status_string", "mla_prefill_with_prefix", "mla_kv_append",
-              "mla_decode_sparse", "mla_decode_sparse_workspace_size"):
+              "mla_decode_sparse", "mla_decode_sparse_workspace_size", "mla_output_proj",
+              "mla_output_proj_workspace_size"):
         assert f in names
 
 
@@ -199,6 +200,26 @@ def test_decode_sparse_validation():
     assert sp(*args(k=-3)) == 3
     assert sp(*args(idx=MIS)) == 4
     assert sp(*args(wsb=need - 1)) == 5
+
+
+def test_output_proj_validation():
+    lib = _lib()
+    d = _dims()
+    n = ctypes.c_size_t(7)
+    assert lib.mla_output_proj_workspace_size(ctypes.byref(d), 32, 7168, ctypes.byref(n)) == 0
+    need = n.value
+    assert need >= 2 * 32 * 7168 * 4                    # fp32 partials of the K-slices
+    assert lib.mla_output_proj_workspace_size(ctypes.byref(d), 4096, 7168, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.mla_output_proj_workspace_size(ctypes.byref(d), 128, 7168, ctypes.byref(n)) == 0 and n.value > 0
+    assert lib.mla_output_proj_workspace_size(ctypes.byref(d), 32, 7000, ctypes.byref(n)) == 3   # not x64
+    assert lib.mla_output_proj_workspace_size(ctypes.byref(d), 1 << 20, 7168, ctypes.byref(n)) == 3
+    op = lib.mla_output_proj
+    assert op(ctypes.byref(d), 0, 7168, None, None, None, 0, None, None) == 0
+    assert op(ctypes.byref(d), 32, 7168, FAKE, FAKE, None, 0, FAKE, None) == 1      # workspace needed
+    assert op(ctypes.byref(d), 32, 7168, FAKE, None, FAKE, need, FAKE, None) == 1
+    assert op(ctypes.byref(d), 32, 7168, MIS, FAKE, FAKE, need, FAKE, None) == 4
+    assert op(ctypes.byref(d), 32, 7168, FAKE, FAKE, FAKE, need - 1, FAKE, None) == 5
+    assert op(ctypes.byref(d), 32, 0, FAKE, FAKE, FAKE, need, FAKE, None) == 3
 
 
 def test_status_strings():

@@ -259,3 +259,47 @@ def test_decode_sparse_config1_top2048_sampled():
     say(f"decode_sparse {case.name} k=2048: oracle on sequences 0, 13, 31")
     out, lse = _run_sparse(case, q, d, topk)
     _check_sparse(case, q, d, topk, out, lse, [0, 13, 31])
+
+
+# ----------------------------------------------------------------------------------- output projection
+def _run_out_proj(x_bits, wo_bits):
+    y = binding.output_proj(dev_bf16(x_bits), dev_bf16(wo_bits))
+    torch.cuda.synchronize()
+    return host_bits(y)
+
+
+@pytest.mark.parametrize("H,n,dim", [(16, 1, 64), (16, 5, 320), (32, 16, 1024), (128, 32, 7168), (64, 33, 512),
+                                     (16, 64, 192), (16, 65, 320), (32, 300, 704), (16, 513, 256),
+                                     (128, 128, 7168), (64, 100, 1024)])
+def test_output_proj_parity(H, n, dim):
+    say(f"output_proj H={H} n={n} dim={dim}")
+    x = S.head_outputs(n, H, seed=12, case_id=1000 + n)
+    wo = S.wo_weights(H, seed=12, case_id=1000 + n, dim=dim, workers=S.default_workers())
+    y = _run_out_proj(x, wo)
+    assert_bf16_parity(y, O.output_proj(x, wo, staged=False), "y")
+
+
+@pytest.mark.slow
+def test_output_proj_prefill_4096_sampled():
+    H, n, dim = 128, 4096, 7168
+    say(f"output_proj H={H} n={n} dim={dim}: oracle on sampled tokens")
+    x = S.head_outputs(n, H, seed=0, case_id=2, workers=S.default_workers())
+    wo = S.wo_weights(H, seed=0, case_id=2, dim=dim, workers=S.default_workers())
+    y = _run_out_proj(x, wo)
+    rows = [0, 1, 255, 256, 2047, 4000, 4095]
+    assert_bf16_parity(y[rows], O.output_proj(x[rows], wo, staged=False), "y rows")
+
+
+def test_decode_then_output_proj():
+    """A decode step's head outputs projected by wo: the composition the attention update is."""
+    case = S.DecodeCase("t", 1100, 64, np.array([300, 7], np.int32), max_seqlen=300)
+    d = S.decode_inputs(case, seed=13, with_q_latent=False)
+    q = S.decode_query(case, seed=13)
+    wo = S.wo_weights(64, seed=13, case_id=1100, dim=512)
+    out, _ = binding.decode(dev_bf16(q), dev_bf16(d["wkv_b"]), dev_bf16(d["kv_cache"]), dev_bf16(d["pe_cache"]),
+                            dev(d["lengths"]), 300)
+    y = binding.output_proj(out, dev_bf16(wo))
+    torch.cuda.synchronize()
+    oo, _ = O.decode_batch(O.bf16_decode(q), d["wkv_b"], d["kv_cache"], d["pe_cache"], d["row_offset"],
+                           d["lengths"], SCALE)
+    assert_bf16_parity(host_bits(y), O.output_proj(O.bf16_encode(oo), wo, staged=False), "attention update")
