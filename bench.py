@@ -20,6 +20,11 @@ The printed JSON line carries:
               causal attention, TFLOP/s of algorithmic flops against 2.5 PFLOP/s bf16
   cpu_baseline the CPU oracle on a bounded sample of the same workload (whole sequences, one at a
               time, for about half of --cpu-budget seconds)
+  next_rows   the steps next to the path, each with its time, roofline fraction and an oracle
+              sample: mla_kv_append (32 decode / 4096 prefill tokens), mla_decode_sparse (the decode
+              workload with 2048 of 4096 positions per sequence), mla_prefill_with_prefix (the last
+              2048 of the 4096 prefill positions over the first 2048), mla_output_proj (wo 7168 x
+              16384 after 32 and 4096 tokens)
 
     python bench.py --copy-calibration MIB   only runs a plain device copy of MIB MiB (for scaling
                                              the rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
@@ -161,11 +166,9 @@ def decode_bench(args, torch, binding, S):
     return res, d
 
 
-def prefill_bench(args, torch, binding, S):
+def prefill_bench(args, torch, binding, S, p):
     case = S.workload(2)
     B, T, H = case.batch, case.seqlen, case.n_heads
-    log(f"[bench] generating {case.name}")
-    p = S.prefill_inputs(case, seed=0)
     L = binding.lib()
     dims = binding.dims(H)
     xs = to_dev_bf16(torch, p["q_latent"])
@@ -219,6 +222,199 @@ def prefill_bench(args, torch, binding, S):
             "causal_attention": {"ms": t_a, "tflops": f_attn / (t_a * 1e-3) / 1e12},
         },
     }
+
+
+def _time_calls(torch, fn, n_stages, warmup=3, reps=10):
+    """Mean per-stage times (ms) of fn(events) over `reps` calls, each recording n_stages + 1 events
+    on the stream the library runs on."""
+    ev = HipEvents((n_stages + 1) * reps)
+    for _ in range(warmup):
+        fn(None)
+    torch.cuda.synchronize()
+    for k in range(reps):
+        fn(ev.ptr((n_stages + 1) * k))
+    torch.cuda.synchronize()
+    return np.array([[ev.ms((n_stages + 1) * k + j, (n_stages + 1) * k + j + 1) for j in range(n_stages)]
+                     for k in range(reps)]).mean(0)
+
+
+def _cpu_timed(fn, budget_s, unit_per_call, unit):
+    """Oracle calls repeated for about budget_s (at least one): rate in `unit` per second."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        fn()
+        n += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": n * unit_per_call / dt, "unit": unit, "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "seconds": dt, "calls": n}
+
+
+def next_rows_bench(args, torch, binding, S, dec_d, pre_inputs):
+    """The steps next to the hot path, each on a workload of the benchmark's shapes: the key/value
+    side with its cache write, top-k decode, prefill over a cached prefix and the output projection.
+    Each reports its time, its algorithmic bytes or flops against the roofline, and the CPU oracle on
+    a small sample (about --next-cpu-budget seconds each)."""
+    from oracle import mla_oracle as O
+    L = binding.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    P = ctypes.POINTER(ctypes.c_void_p)
+    L.mla_decode_sparse_ex.argtypes = list(L.mla_decode_sparse.argtypes) + [P]
+    L.mla_prefill_with_prefix_ex.argtypes = list(L.mla_prefill_with_prefix.argtypes) + [P]
+    L.mla_output_proj_ex.argtypes = list(L.mla_output_proj.argtypes) + [P]
+    budget = args.next_cpu_budget
+    rows = {}
+
+    # N1: key/value side + cache write, 32 decode tokens and 4096 prefill tokens
+    kvres = {}
+    for name, B, T in (("decode_b32", 32, 1), ("prefill_t4096", 1, 4096)):
+        H = 128
+        dims = binding.dims(H)
+        inp = S.kv_side_inputs(B * T, 0, 30 + T)
+        cs = S.rope_table(np.arange(B * T) % 4096).reshape(B, T, 32, 2)
+        max_seqlen = T + 64
+        kv_a = to_dev_bf16(torch, inp["kv_a"]).view(B, T, 576)
+        g = torch.from_numpy(inp["kv_gamma"]).cuda()
+        csd = torch.from_numpy(cs).cuda()
+        start = torch.full((B,), 64, dtype=torch.int32, device="cuda")
+        kvc = torch.zeros((B * max_seqlen, 512), dtype=torch.bfloat16, device="cuda")
+        pec = torch.zeros((B * max_seqlen, 64), dtype=torch.bfloat16, device="cuda")
+        ev_holder = {}
+
+        def call(evp, B=B, T=T, kv_a=kv_a, g=g, csd=csd, start=start, kvc=kvc, pec=pec, max_seqlen=max_seqlen,
+                 dims=dims):
+            # no staged variant: events recorded around the call on the same stream
+            if evp is not None:
+                ev_holder["ev"].hip.hipEventRecord(ctypes.c_void_p(evp[0]), ctypes.c_void_p(stream))
+            assert L.mla_kv_append(ctypes.byref(dims), B, T, kv_a.data_ptr(), g.data_ptr(), csd.data_ptr(),
+                                   start.data_ptr(), None, max_seqlen, kvc.data_ptr(), pec.data_ptr(), stream) == 0
+            if evp is not None:
+                ev_holder["ev"].hip.hipEventRecord(ctypes.c_void_p(evp[1]), ctypes.c_void_p(stream))
+
+        reps = 10
+        ev = HipEvents(2 * reps)
+        ev_holder["ev"] = ev
+        for _ in range(3):
+            call(None)
+        torch.cuda.synchronize()
+        for k in range(reps):
+            call([ev.ev[2 * k], ev.ev[2 * k + 1]])
+        torch.cuda.synchronize()
+        ms = float(np.mean([ev.ms(2 * k, 2 * k + 1) for k in range(reps)]))
+        n = B * T
+        byts = n * (576 * 2 + 256 + 1152) + 512 * 4
+        kvres[name] = {"tokens": n, "us": ms * 1e3, "achieved_gbps": byts / (ms * 1e-3) / 1e9,
+                       "frac_of_hbm_peak": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "bytes": byts}
+    a_cpu = S.kv_side_inputs(4096, 0, 4126)
+    cs_cpu = S.rope_table(np.arange(4096))
+    kvres["cpu_baseline"] = _cpu_timed(lambda: O.kv_side(a_cpu["kv_a"], a_cpu["kv_gamma"], cs_cpu), budget, 4096,
+                                       "tokens/s")
+    kvres["cpu_baseline"]["sample"] = "kv_side of 4096 tokens (fp64 NumPy), repeated"
+    rows["kv_append"] = {"bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS,
+                         "bytes_per_token": 576 * 2 + 256 + 1152, **kvres}
+
+    # N2: top-k decode on the decode workload's caches, 2048 positions per sequence
+    case = S.workload(1)
+    B, H = case.batch, case.n_heads
+    dims = binding.dims(H)
+    k = 2048
+    topk = S.topk_indices(case.lengths, k, 0, case.case_id)
+    q = to_dev_bf16(torch, S.decode_query(case, 0))
+    wkv = to_dev_bf16(torch, dec_d["wkv_b"])
+    kvd, ped = to_dev_bf16(torch, dec_d["kv_cache"]), to_dev_bf16(torch, dec_d["pe_cache"])
+    lens = torch.from_numpy(dec_d["lengths"]).cuda()
+    tk = torch.from_numpy(topk).cuda()
+    wsb = binding.decode_sparse_workspace_size(H, B, int(case.max_seqlen), k)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, H, 128), dtype=torch.bfloat16, device="cuda")
+    st = _time_calls(torch, lambda e: L.mla_decode_sparse_ex(
+        ctypes.byref(dims), B, q.data_ptr(), wkv.data_ptr(), kvd.data_ptr(), ped.data_ptr(), None, lens.data_ptr(),
+        int(case.max_seqlen), tk.data_ptr(), k, ws.data_ptr(), wsb, out.data_ptr(), None, stream, e), 4)
+    sel = int(np.sum(topk >= 0))
+    attn_bytes = sel * BYTES_PER_CACHED_TOKEN
+    tot_bytes = attn_bytes + 2 * H * 128 * 512 * 2 + B * H * (192 + 128) * 2 + B * k * 4
+    qv = O.bf16_decode(S.decode_query(case, 0))
+
+    def cpu_sparse():
+        b = 0
+        O.decode_topk(qv[b], dec_d["wkv_b"], dec_d["kv_cache"][:4096], dec_d["pe_cache"][:4096], topk[b], 192 ** -0.5)
+    c = _cpu_timed(cpu_sparse, budget, H * k, "selected-token·heads/s")
+    c["sample"] = "decode_topk of sequence 0 (2048 of 4096 positions, fp64 NumPy), repeated"
+    rows["decode_sparse"] = {
+        "workload": f"{case.name}_top{k}", "selected_tokens": sel, "us": float(st.sum()) * 1e3,
+        "stages_us": [float(x) * 1e3 for x in st],
+        "value": H * sel / (float(st.sum()) * 1e-3), "unit": "selected-token·heads/s",
+        "roofline": {"bound": "hbm", "kernel": "gathering split-KV attention",
+                     "achieved": attn_bytes / (float(st[1]) * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": attn_bytes / (float(st[1]) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                     "bytes_per_launch": attn_bytes},
+        "decode_gbps": tot_bytes / (float(st.sum()) * 1e-3) / 1e9, "cpu_baseline": c}
+
+    # N3: the second half of the prefill workload as a chunk over its first half
+    p = pre_inputs
+    pc = S.workload(2)
+    T, H = pc.seqlen, pc.n_heads
+    dims = binding.dims(H)
+    tq = T // 2
+    qfull = to_dev_bf16(torch, S.prefill_query(pc, 0))
+    qc = qfull[:, T - tq:].contiguous()
+    lat, kpe, wkv2 = to_dev_bf16(torch, p["kv_latent"]), to_dev_bf16(torch, p["k_pe"]), to_dev_bf16(torch, p["wkv_b"])
+    wsb = binding.prefill_workspace_size(H, 1, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    outp = torch.empty((1, tq, H, 128), dtype=torch.bfloat16, device="cuda")
+    st = _time_calls(torch, lambda e: L.mla_prefill_with_prefix_ex(
+        ctypes.byref(dims), 1, tq, T, qc.data_ptr(), lat.data_ptr(), kpe.data_ptr(), wkv2.data_ptr(), ws.data_ptr(),
+        wsb, outp.data_ptr(), None, stream, e), 2, reps=5)
+    pairs = sum(T - tq + i + 1 for i in range(tq))
+    f_exp = 2.0 * T * 512 * 256 * H
+    f_att = 640.0 * pairs * H
+    qcv = O.bf16_decode(S.prefill_query(pc, 0)[0, T - tq:])
+    c = _cpu_timed(lambda: O.prefill_causal(qcv, p["kv_latent"][0], p["k_pe"][0], p["wkv_b"], 192 ** -0.5,
+                                            heads=[0], rows=[tq - 1]), budget, 2.0 * T * 512 * 256 + 640.0 * T,
+                   "FLOP/s")
+    c["sample"] = ("one head's expansion of the 4096 keys and the chunk's last query row over them "
+                   "(fp64 NumPy), repeated")
+    t_tot = float(st.sum())
+    rows["prefill_with_prefix"] = {
+        "workload": f"dsv32_prefill_chunk_q{tq}_kv{T}_h{H}", "ms": t_tot,
+        "tflops": (f_exp + f_att) / (t_tot * 1e-3) / 1e12,
+        "stages": {"expansion": {"ms": float(st[0]), "tflops": f_exp / (float(st[0]) * 1e-3) / 1e12},
+                   "causal_attention": {"ms": float(st[1]), "tflops": f_att / (float(st[1]) * 1e-3) / 1e12}},
+        "roofline": {"bound": "mfma", "kernel": "causal attention", "achieved": f_att / (float(st[1]) * 1e-3) / 1e12,
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": f_att / (float(st[1]) * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "cpu_baseline": c}
+
+    # N4: output projection after a decode step (32 tokens) and after the prefill (4096 tokens)
+    dim = S.MODEL_DIM
+    wo = to_dev_bf16(torch, S.wo_weights(128, 0, 40, dim, workers=S.default_workers()))
+    dims = binding.dims(128)
+    opres = {}
+    for name, n in (("decode_b32", 32), ("prefill_t4096", 4096)):
+        x = to_dev_bf16(torch, S.head_outputs(n, 128, 0, 41, workers=S.default_workers()))
+        y = torch.empty((n, dim), dtype=torch.bfloat16, device="cuda")
+        wsb = binding.output_proj_workspace_size(128, n, dim)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        st = _time_calls(torch, lambda e: L.mla_output_proj_ex(ctypes.byref(dims), n, dim, x.data_ptr(), wo.data_ptr(),
+                                                              ws.data_ptr() if wsb else None, wsb, y.data_ptr(),
+                                                              stream, e), 2)
+        t = float(st.sum())
+        fl = 2.0 * n * 128 * 128 * dim
+        by = dim * 128 * 128 * 2 + n * 128 * 128 * 2 + n * dim * 2
+        opres[name] = {"tokens": n, "us": t * 1e3, "tflops": fl / (t * 1e-3) / 1e12, "gbps": by / (t * 1e-3) / 1e9,
+                       "roofline": ({"bound": "hbm", "achieved": by / (t * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                                     "unit": "GB/s", "frac": by / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS} if n <= 64 else
+                                    {"bound": "mfma", "achieved": fl / (t * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": fl / (t * 1e-3) / 1e12 / BF16_PEAK_TFLOPS})}
+    wo_h = S.wo_weights(128, 0, 40, dim, workers=S.default_workers())
+    x1 = S.head_outputs(1, 128, 0, 41)
+    c = _cpu_timed(lambda: O.output_proj(x1, wo_h), budget, 2.0 * 128 * 128 * dim, "FLOP/s")
+    c["sample"] = "one token through the 7168 x 16384 wo (fp64 NumPy), repeated"
+    opres["cpu_baseline"] = c
+    rows["output_proj"] = {"dim": dim, **opres}
+    return rows
 
 
 def measured_traffic():
@@ -297,6 +493,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-next", action="store_true", help="skip the steps next to the path")
+    ap.add_argument("--next-cpu-budget", type=float, default=2.0, help="oracle seconds per next-row baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -320,9 +518,19 @@ def main():
     res, d = decode_bench(args, torch, binding, S)
     case = res["case"]
     log(f"[bench] decode step {res['ms'] * 1e3:.1f} us; stages (ms) {json.dumps(res['stages_ms'])}")
-    pre = None if args.no_prefill else prefill_bench(args, torch, binding, S)
+    p_in = None
+    if not (args.no_prefill and args.no_next):
+        log(f"[bench] generating {S.workload(2).name}")
+        p_in = S.prefill_inputs(S.workload(2), seed=0)
+    pre = None if args.no_prefill else prefill_bench(args, torch, binding, S, p_in)
     if pre:
         log(f"[bench] prefill {pre['ms']:.3f} ms, {pre['tflops']:.1f} TFLOP/s")
+    nxt = None
+    if not args.no_next:
+        dec_d = d if case.name == S.workload(1).name else S.decode_inputs(S.workload(1), seed=0)
+        log("[bench] steps next to the path (kv append, top-k decode, prefix prefill, output projection)")
+        nxt = next_rows_bench(args, torch, binding, S, dec_d, p_in)
+        log(f"[bench] next rows: {json.dumps({k: v.get('us', v.get('ms')) for k, v in nxt.items()})}")
     cpu = None
     if not args.no_cpu:
         log("[bench] timing the CPU oracle")
@@ -351,6 +559,7 @@ def main():
             "workload": pre["workload"], "ms": pre["ms"], "tflops": pre["tflops"],
             "frac_of_bf16_peak": pre["tflops"] / BF16_PEAK_TFLOPS, "stages": pre["stages"]},
         "cpu_baseline": cpu,
+        "next_rows": nxt,
     }
     print(json.dumps(line), flush=True)
 
