@@ -1,0 +1,156 @@
+// Tiled bf16 product on gfx950 for the projections of the path whose two operands are both stored
+// with k contiguous ("NT"): C[m][n] = sum_k X[m][k] W[n][k], X = token rows, W = weight rows
+// (output features), fp32 accumulation on MFMA.
+//
+// Block tile 256 tokens x 256 features, 8 waves as 2 (tokens) x 4 (features), 128 x 64 each; k in
+// steps of 64 through two LDS stages (64 KB each: 256 weight rows, then 256 token rows of 128 B)
+// filled by 16-byte direct-to-LDS buffer loads, the next step's loads in flight during this step's
+// MFMAs; one barrier per step. Rows past either operand's end read as zeros (descriptor range).
+// Stage rows: 16-byte chunk c of row r at c ^ ((r >> 1) & 7), so every 128-bit operand read
+// (16 rows, 4 chunks) is free of LDS bank conflicts.
+// Per wave and k-step: 4 weight and 8 token operands (ds_read_b128), 32 MFMA 16x16x32.
+// Orientation: normally the weight row is the MFMA A operand, so a lane ends with four consecutive
+// features of one token; an epilogue may ask a wave for the transposed product instead (token as A:
+// four consecutive tokens of one feature), chosen per wave.
+#pragma once
+
+#include <type_traits>
+
+#include "mla_common.hpp"
+
+namespace mla {
+namespace gemm {
+
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kStageBytes = (kBM + kBN) * kBK * 2;              // 64 KB
+constexpr int kLoadsPerWave = kStageBytes / 1024 / 8;           // 8 loads of 1 KB per wave and step
+constexpr uint32_t kRsrcWord3 = 0x00020000u;                    // raw buffer, 32-bit data format
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)),
+                                           kRsrcWord3);
+}
+
+// 16-byte direct-to-LDS buffer load (lane l's bytes land at lds_addr + 16 l); completion is tracked
+// with an explicit vmcnt wait. The asm block writes no registers.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "{m0}"(lds_addr)
+               : "memory");
+}
+
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// One block tile: features [n0, n0 + 256) of W (w_rows rows in all), tokens [m0, m0 + 256) of X
+// (x_rows rows), k in [k_begin, k_begin + k_len) (k_len a multiple of 64; rows are K elements).
+// At the end calls, per wave and 16 x 16 sub-tile,
+//   epi.store(m, n, v, false)  v = C[m][n .. n+3]      (normal orientation), or
+//   epi.store(m, n, v, true)   v = C[m .. m+3][n]      (when epi.transposed(wn) for the wave)
+// for tokens m < x_rows and features n < w_rows only.
+template <class Epi>
+__device__ __forceinline__ void nt_tile(const uint16_t* __restrict__ w, int64_t w_rows, const uint16_t* __restrict__ x,
+                                        int64_t x_rows, int K, int n0, int64_t m0, int k_begin, int k_len,
+                                        uint8_t* stage, const Epi& epi) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, grp = lane >> 4;
+  const int wm = wave >> 2, wn = wave & 3;
+
+  // Loads: instruction d (0..63) of a step covers 8 rows x 128 B: d < 32 weight rows 8d.., else
+  // token rows 8(d-32)..; wave w issues d = w + 8e. Lane l: row 8d' + l/8, physical chunk l%8
+  // holding logical chunk (l%8) ^ swz(row).
+  uint32_t voff[kLoadsPerWave];
+#pragma unroll
+  for (int e = 0; e < kLoadsPerWave; ++e) {
+    const int d = wave + 8 * e;
+    const int row = 8 * (d & 31) + (lane >> 3);
+    voff[e] = static_cast<uint32_t>(row * K * 2 + (((lane & 7) ^ swz(row)) << 4));
+  }
+  const uint32_t st_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void_t*)stage));
+  const int64_t w_left = w_rows - n0, x_left = x_rows - m0;
+  auto issue = [&](int kt) {
+    // descriptors rebuilt per step (scalar work): short-lived, they stay in SGPRs
+    const __amdgpu_buffer_rsrc_t rw = rsrc(w + static_cast<int64_t>(n0) * K, static_cast<uint32_t>(w_left * K * 2));
+    const __amdgpu_buffer_rsrc_t rx = rsrc(x + m0 * K, static_cast<uint32_t>(x_left * K * 2));
+    const uint32_t koff = static_cast<uint32_t>(k_begin + kt * kBK) * 2u;
+    const uint32_t dst = st_lds + (kt & 1) * kStageBytes;
+#pragma unroll
+    for (int e = 0; e < kLoadsPerWave; ++e) {
+      const int d = wave + 8 * e;
+      if (d < 32) dma16(rw, dst + d * 1024, voff[e] + koff);
+      else dma16(rx, dst + d * 1024, voff[e] + koff);
+    }
+  };
+
+  // operand offsets in a stage: weight row 64 wn + 16 nb + r, token row 128 wm + 16 mb + r;
+  // chunk 4 ks + grp (+ 16 nb / 16 mb rows keep swz)
+  int a_off[2], b_off[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int ra = 64 * wn + r, rb = 128 * wm + r;
+    a_off[ks] = ra * 128 + (((4 * ks + grp) ^ swz(ra)) << 4);
+    b_off[ks] = kBN * 128 + rb * 128 + (((4 * ks + grp) ^ swz(rb)) << 4);
+  }
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const bool tr = epi.transposed(wn);
+  auto run = [&](auto transposed) {
+    constexpr bool T = decltype(transposed)::value;
+    const int n_kt = k_len / kBK;
+    issue(0);
+    for (int kt = 0; kt < n_kt; ++kt) {
+      __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));   // vmcnt(0): this wave's loads of kt
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      __builtin_amdgcn_s_barrier();                                // everyone's; stage kt-1 free
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      if (kt + 1 < n_kt) issue(kt + 1);
+      const uint8_t* st = stage + (kt & 1) * kStageBytes;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 af[4], bf[8];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) af[nb] = *reinterpret_cast<const bf16x8*>(st + a_off[ks] + nb * 16 * 128);
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) bf[mb] = *reinterpret_cast<const bf16x8*>(st + b_off[ks] + mb * 16 * 128);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int mb = 0; mb < 8; ++mb)
+            acc[nb][mb] = T ? mfma16x16x32(bf[mb], af[nb], acc[nb][mb]) : mfma16x16x32(af[nb], bf[mb], acc[nb][mb]);
+      }
+    }
+  };
+  if (tr) run(std::true_type{});
+  else run(std::false_type{});
+
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      if (!tr) {
+        // C[m][n .. n+3]: m = m0 + 128 wm + 16 mb + r, n = n0 + 64 wn + 16 nb + 4 grp
+        const int64_t m = m0 + 128 * wm + 16 * mb + r;
+        const int n = n0 + 64 * wn + 16 * nb + 4 * grp;
+        if (m < x_rows && n < w_rows) epi.store(m, n, acc[nb][mb], false);
+      } else {
+        // C[m .. m+3][n]: m = m0 + 128 wm + 16 mb + 4 grp, n = n0 + 64 wn + 16 nb + r
+        const int64_t m = m0 + 128 * wm + 16 * mb + 4 * grp;
+        const int n = n0 + 64 * wn + 16 * nb + r;
+        if (m < x_rows && n < w_rows) epi.store(m, n, acc[nb][mb], true);
+      }
+    }
+}
+
+}  // namespace gemm
+}  // namespace mla

@@ -56,7 +56,7 @@ mla_status_t mla_query_path_workspace_size(const mla_dims_t* dims, int64_t n_tok
   if (st != MLA_OK) return st;
   if (!bytes) return MLA_ERR_INVALID_ARG;
   if (n_tokens < 0 || n_tokens > kMaxTokens) return MLA_ERR_SHAPE;
-  *bytes = mla::query_layout(n_tokens).total;
+  *bytes = mla::query_layout(dims->n_heads, n_tokens).total;
   return MLA_OK;
 }
 
@@ -69,7 +69,7 @@ mla_status_t mla_query_path_ex(const mla_dims_t* dims, int64_t n_tokens, const u
   if (n_tokens < 0 || n_tokens > kMaxTokens) return MLA_ERR_SHAPE;
   if (n_tokens == 0) return MLA_OK;
   if (!q_latent || !q_norm_w || !wq_b || !rope_cs || !q_out) return MLA_ERR_INVALID_ARG;
-  const mla::QueryLayout lay = mla::query_layout(n_tokens);
+  const mla::QueryLayout lay = mla::query_layout(dims->n_heads, n_tokens);
   if (lay.total > 0 && !workspace) return MLA_ERR_INVALID_ARG;
   if (!aligned16(q_latent) || !aligned16(q_norm_w) || !aligned16(wq_b) || !aligned16(rope_cs) ||
       !aligned16(q_out) || (inv_rms && !aligned16(inv_rms)) || (workspace && !aligned16(workspace)))

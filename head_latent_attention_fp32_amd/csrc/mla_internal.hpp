@@ -34,11 +34,13 @@ struct PrefillLayout {
 PrefillLayout prefill_layout(int n_heads, int batch, int seqlen);
 
 // Query path for more than 32 tokens: the normalised activation y [n][1536] bf16 and, when the
-// caller passes no inv_rms, the per-token statistics. Empty for 32 tokens or fewer.
+// caller passes no inv_rms, the per-token statistics; for many tokens (large) also wq_b transposed
+// ([H*192][1536]). Empty for 32 tokens or fewer.
 struct QueryLayout {
-  size_t y_off, inv_off, total;
+  bool large;
+  size_t y_off, wt_off, inv_off, total;
 };
-QueryLayout query_layout(int64_t n_tokens);
+QueryLayout query_layout(int n_heads, int64_t n_tokens);
 
 hipError_t launch_query_path(int n_heads, int64_t n_tokens, const uint16_t* q_latent, const float* gamma,
                              const uint16_t* wq_b, const float* rope_cs, uint16_t* q_out, float* inv_rms,

@@ -12,16 +12,14 @@
 //          consecutive quarters of the slice with the same columns, and their partial sums meet in
 //          LDS. Several K-slices per column tile fill the chip; their fp32 partials are summed in
 //          a fixed order by the reduce kernel (deterministic).
-//   big    (prefill): 256 x 256 output tiles, 8 waves (2 along tokens x 4 along columns, 128 x 64
-//          each), K in steps of 64 through two LDS stages filled by 16-byte direct-to-LDS loads
-//          (the next step's loads fly during this step's MFMAs). Stage rows are 128 bytes, 16-byte
-//          chunk c of row r at c ^ ((r >> 1) & 7): every 128-bit operand read is free of bank
-//          conflicts.
+//   big    (prefill): the tiled MFMA product of gemm_nt.hpp (256 x 256 output tiles, direct-to-LDS
+//          operand stages), split along K when the tiles alone are too few to fill the chip.
 // In both, the MFMA A operand is a weight row (output column) and B a token, so a lane ends with
 // four consecutive output columns of one token: one 8-byte store.
 // The k order inside a 128-k chunk of the small kernel is permuted (lane group g holds k
 // 32 g .. 32 g + 31 for its four k-steps) identically for both operands, which leaves the sum
 // unchanged and makes each lane's loads contiguous.
+#include "gemm_nt.hpp"
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
@@ -165,113 +163,38 @@ __global__ __launch_bounds__(256) void out_proj_reduce_kernel(const float* __res
 }
 
 // ---------------------------------------------------------------------------------------------
-// Many tokens.
+// Many tokens: the tiled product of gemm_nt.hpp; blockIdx.y = K-slice of k_per_block. With more
+// than one slice (gridDim.y > 1) the fp32 partial of the slice goes to part[slice][m][n] for the
+// reduce kernel.
 // ---------------------------------------------------------------------------------------------
-constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kStageBytes = (kBM + kBN) * kBK * 2;   // 64 KB: weight rows, then token rows
-constexpr int kLoadsPerWave = (kBM + kBN) * kBK * 2 / 1024 / 8;   // 8
+struct OutEpi {
+  uint16_t* y;
+  float* part;
+  int64_t n_tokens;
+  int dim, slice, slices;
+  __device__ bool transposed(int) const { return false; }
+  __device__ void store(int64_t m, int n, f32x4 v, bool) const {
+    if (slices > 1) {
+      *reinterpret_cast<f32x4*>(part + (static_cast<int64_t>(slice) * n_tokens + m) * dim + n) = v;
+      return;
+    }
+    uint2 u;
+    u.x = pack_bf16x2(v[0], v[1]);
+    u.y = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<uint2*>(y + m * dim + n) = u;
+  }
+};
 
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
-
-// blockIdx.y = K-slice of k_per_block; with more than one slice (gridDim.y > 1) the fp32 partial
-// of the slice goes to part[slice][m][n] for the reduce kernel.
 __global__ __launch_bounds__(512, 1) void out_proj_big_kernel(const uint16_t* __restrict__ x,
                                                               const uint16_t* __restrict__ wo, int n_tokens, int K,
                                                               int dim, int k_per_block, float* __restrict__ part,
                                                               uint16_t* __restrict__ y) {
-  __shared__ __attribute__((aligned(1024))) uint8_t stage[2][kStageBytes];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r = lane & 15, grp = lane >> 4;
-  const int wm = wave >> 2, wn = wave & 3;            // wave tile: tokens 128 wm.., columns 64 wn..
-  const int n_tiles = (dim + kBN - 1) / kBN;
+  __shared__ __attribute__((aligned(1024))) uint8_t stage[2 * gemm::kStageBytes];
+  const int n_tiles = (dim + gemm::kBN - 1) / gemm::kBN;
   const int nt = blockIdx.x % n_tiles, mt = blockIdx.x / n_tiles;
-  const int n0 = nt * kBN;
-  const int64_t m0 = static_cast<int64_t>(mt) * kBM;
-  const int k_begin = blockIdx.y * k_per_block;
-
-  // Loads: instruction d (0..63) of a stage covers 8 rows x 128 B: d < 32 weight rows 8d.., else
-  // token rows 8(d-32)..; wave w issues d = w + 8e. Lane l: row 8d' + l/8, physical chunk l%8
-  // holding logical chunk (l%8) ^ swz(row).
-  uint32_t voff[kLoadsPerWave];
-#pragma unroll
-  for (int e = 0; e < kLoadsPerWave; ++e) {
-    const int d = wave + 8 * e;
-    const int row = 8 * (d & 31) + (lane >> 3);
-    voff[e] = static_cast<uint32_t>(row * K * 2 + (((lane & 7) ^ swz(row)) << 4));
-  }
-  const uint32_t st_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)&stage[0][0]));
-  auto issue = [&](int kt) {
-    const __amdgpu_buffer_rsrc_t rw =
-        make_rsrc(wo + static_cast<int64_t>(n0) * K, static_cast<uint32_t>(dim - n0) * K * 2u);
-    const __amdgpu_buffer_rsrc_t rx =
-        make_rsrc(x + m0 * K, static_cast<uint32_t>(n_tokens - m0) * K * 2u);
-    const uint32_t koff = static_cast<uint32_t>(k_begin + kt * kBK) * 2u;
-    const uint32_t dst = st_lds + (kt & 1) * kStageBytes;
-#pragma unroll
-    for (int e = 0; e < kLoadsPerWave; ++e) {
-      const int d = wave + 8 * e;
-      if (d < 32) dma16(rw, dst + d * 1024, voff[e] + koff);
-      else dma16(rx, dst + d * 1024, voff[e] + koff);
-    }
-  };
-
-  // operand offsets in a stage: weight row 64 wn + 16 nb + r, token row 128 wm + 16 mb + r;
-  // chunk 4 ks + grp
-  int a_off[2], b_off[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int ra = 64 * wn + r, rb = 128 * wm + r;     // + 16 nb / 16 mb keeps swz(row)
-    a_off[ks] = ra * 128 + (((4 * ks + grp) ^ swz(ra)) << 4);
-    b_off[ks] = kBN * 128 + rb * 128 + (((4 * ks + grp) ^ swz(rb)) << 4);
-  }
-
-  f32x4 acc[4][8];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int n_kt = k_per_block / kBK;
-  issue(0);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));   // vmcnt(0): this wave's loads of kt
-    lds_barrier();                                               // everyone's; stage kt-1 free
-    if (kt + 1 < n_kt) issue(kt + 1);
-    const uint8_t* st = &stage[kt & 1][0];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 af[4], bf[8];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) af[nb] = *reinterpret_cast<const bf16x8*>(st + a_off[ks] + nb * 16 * 128);
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) bf[mb] = *reinterpret_cast<const bf16x8*>(st + b_off[ks] + mb * 16 * 128);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb) acc[nb][mb] = mfma16x16x32(af[nb], bf[mb], acc[nb][mb]);
-    }
-  }
-
-  // lane holds y[m][n .. n+3], m = m0 + 128 wm + 16 mb + r, n = n0 + 64 wn + 16 nb + 4 grp
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb) {
-    const int64_t m = m0 + 128 * wm + 16 * mb + r;
-    if (m >= n_tokens) continue;
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int n = n0 + 64 * wn + 16 * nb + 4 * grp;
-      if (n >= dim) continue;
-      if (gridDim.y > 1) {
-        *reinterpret_cast<f32x4*>(part + (static_cast<int64_t>(blockIdx.y) * n_tokens + m) * dim + n) = acc[nb][mb];
-        continue;
-      }
-      uint2 u;
-      u.x = pack_bf16x2(acc[nb][mb][0], acc[nb][mb][1]);
-      u.y = pack_bf16x2(acc[nb][mb][2], acc[nb][mb][3]);
-      *reinterpret_cast<uint2*>(y + m * dim + n) = u;
-    }
-  }
+  const OutEpi epi{y, part, n_tokens, dim, static_cast<int>(blockIdx.y), static_cast<int>(gridDim.y)};
+  gemm::nt_tile(wo, dim, x, n_tokens, K, nt * gemm::kBN, static_cast<int64_t>(mt) * gemm::kBM,
+                blockIdx.y * k_per_block, k_per_block, stage, epi);
 }
 
 // K-slices of the small kernel: enough blocks to give every SIMD about two waves, each wave at
@@ -286,9 +209,9 @@ int small_slices(int K, int dim) {
 // K-slices of the big kernel: one when the output tiles alone give the chip about one block per
 // compute unit; else enough (at most 8) to reach that, each slice at least 16 k-steps.
 int big_slices(int K, int dim, int64_t n_tokens) {
-  const int64_t tiles = static_cast<int64_t>((dim + kBN - 1) / kBN) * ((n_tokens + kBM - 1) / kBM);
+  const int64_t tiles = static_cast<int64_t>((dim + gemm::kBN - 1) / gemm::kBN) * ((n_tokens + gemm::kBM - 1) / gemm::kBM);
   int s = 1;
-  while (tiles * s < 200 && s < 8 && (K / (2 * s)) % kBK == 0 && K / (2 * s) >= 16 * kBK) s *= 2;
+  while (tiles * s < 200 && s < 8 && (K / (2 * s)) % gemm::kBK == 0 && K / (2 * s) >= 16 * gemm::kBK) s *= 2;
   return s;
 }
 
@@ -323,7 +246,8 @@ hipError_t launch_out_proj(int n_heads, int64_t n_tokens, int dim, const uint16_
                                                                                               n_out, y);
     }
   } else {
-    const int64_t tiles = static_cast<int64_t>((dim + kBN - 1) / kBN) * ((n_tokens + kBM - 1) / kBM);
+    const int64_t tiles =
+        static_cast<int64_t>((dim + gemm::kBN - 1) / gemm::kBN) * ((n_tokens + gemm::kBM - 1) / gemm::kBM);
     float* part = static_cast<float*>(workspace);
     out_proj_big_kernel<<<dim3(static_cast<unsigned>(tiles), lay.slices), 512, 0, stream>>>(
         x, wo, static_cast<int>(n_tokens), K, dim, K / lay.slices, part, y);

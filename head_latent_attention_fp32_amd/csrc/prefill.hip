@@ -9,14 +9,15 @@
 // 0 .. kv_len - q_len + i.
 //
 // Two kernels:
-//   1. expand   [k_nope | v] = latent . wkv_b^T per head for all kv_len positions (MFMA GEMM, bf16 outputs as the bf16
-//               Linear of the excerpt). k_nope is written [b][h][t][128] and v transposed,
-//               [b][h][128][t], so that the attention kernel's P.V operand reads runs of keys;
+//   1. expand   [k_nope | v] = latent . wkv_b^T per head for all kv_len positions (MFMA GEMM, bf16
+//               outputs as the bf16 Linear of the excerpt). k_nope is written [b][h][t][128] and v
+//               transposed, [b][h][128][t], so that the attention kernel's P.V operand reads runs of keys;
 //               within every 32 keys the order is permuted (key 16a + 4g + j at 8g + 4a + j) to
 //               match the key order in which P^T leaves the score accumulators.
 //   2. attend   flash-style causal attention: block = (b, h, 128 queries), wave = 32 queries;
 //               S^T = K . Q^T and O^T += V^T . P^T on MFMA with an fp32 online softmax; the
 //               score matrix never leaves registers.
+#include "gemm_nt.hpp"
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
@@ -27,10 +28,13 @@ namespace {
 constexpr int kKBlk = 64;     // key padding granule of the expanded k_nope / V^T
 
 // ---------------------------------------------------------------------------------------------
-// 1. Expansion: rows = B*T tokens, columns = H*256 (k_nope then v per head), K = 512.
-//    Block tile 64 tokens x 64 columns; wave (wt, wc) owns 32 x 32.
+// 1. Expansion: rows = B*S tokens (S = kv_len), columns = H*256 (k_nope then v per head), K = 512,
+//    on the tiled product of gemm_nt.hpp: a 256-column tile is one head. Waves on its k_nope half
+//    keep the normal orientation (four consecutive features of one token: an 8-byte store into
+//    k_nope[b][h][t][:]); waves on its value half take the transposed product (four consecutive
+//    tokens of one feature: an 8-byte store into V^T[b][h][d][:], whose key order is permuted
+//    within groups of 32 but keeps groups of 4 consecutive keys together).
 // ---------------------------------------------------------------------------------------------
-constexpr int EX_BT = 64, EX_BC = 64, EX_BK = 64, EX_LD = EX_BK + 8;
 
 // Position of key t in its V^T row: within each group of 32, key 16a + 4g + j sits at 8g + 4a + j.
 __device__ __forceinline__ int64_t vt_pos(int64_t t) {
@@ -38,99 +42,60 @@ __device__ __forceinline__ int64_t vt_pos(int64_t t) {
   return (t - w) + ((w >> 2) & 3) * 8 + (w >> 4) * 4 + (w & 3);
 }
 
-__global__ __launch_bounds__(256) void expand_kernel(const uint16_t* __restrict__ lat, const uint16_t* __restrict__ wkv_b,
-                                                     int n_heads, int seqlen, int64_t t_pad, int64_t n_rows,
-                                                     uint16_t* __restrict__ knope, uint16_t* __restrict__ vt) {
-  __shared__ __attribute__((aligned(16))) uint16_t as[EX_BT * EX_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t bs[EX_BC * EX_LD];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = lane & 15, grp = lane >> 4;
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * EX_BT;
-  const int col0 = blockIdx.y * EX_BC;
-
-  uint4 areg[2], breg[2];
-  auto fetch = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + 256 * i;
-      const int rr = idx >> 3, ch = idx & 7;
-      areg[i] = ldg16(lat + min(row0 + rr, n_rows - 1) * kKvLora + k0 + ch * 8);
-      breg[i] = ldg16(wkv_b + static_cast<int64_t>(col0 + rr) * kKvLora + k0 + ch * 8);
-    }
-  };
-  auto stash = [&]() {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + 256 * i;
-      const int rr = idx >> 3, ch = idx & 7;
-      *reinterpret_cast<uint4*>(&as[rr * EX_LD + ch * 8]) = areg[i];
-      *reinterpret_cast<uint4*>(&bs[rr * EX_LD + ch * 8]) = breg[i];
-    }
-  };
-
-  const int wt = wave >> 1, wc = wave & 1;
-  f32x4 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  fetch(0);
-  for (int k0 = 0; k0 < kKvLora; k0 += EX_BK) {
-    __syncthreads();
-    stash();
-    __syncthreads();
-    if (k0 + EX_BK < kKvLora) fetch(k0 + EX_BK);
-#pragma unroll
-    for (int kk = 0; kk < EX_BK; kk += 32) {
-      bf16x8 a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const bf16x8*>(&as[(wt * 32 + i * 16 + r) * EX_LD + kk + grp * 8]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const bf16x8*>(&bs[(wc * 32 + j * 16 + r) * EX_LD + kk + grp * 8]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+struct ExpandEpi {
+  uint16_t* knope;
+  uint16_t* vt;
+  int n_heads, seqlen;
+  int64_t t_pad, n_rows, m0, b0;   // b0 = m0 / seqlen
+  __device__ bool transposed(int wn) const { return wn >= 2; }
+  // (b, t) of token row m of this tile
+  __device__ void locate(int64_t m, int64_t& b, int64_t& t) const {
+    b = b0;
+    t = m - b0 * seqlen;
+    while (t >= seqlen) {
+      t -= seqlen;
+      ++b;
     }
   }
-
-  // lane holds D[token row0 + wt*32 + i*16 + 4*grp + e][column col0 + wc*32 + j*16 + r]
+  __device__ void store(int64_t m, int n, f32x4 v, bool tr) const {
+    const int h = n / kKvRows, j = n % kKvRows;
+    int64_t b, t;
+    locate(m, b, t);
+    if (!tr) {
+      uint2 u;
+      u.x = pack_bf16x2(v[0], v[1]);
+      u.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(knope + ((b * n_heads + h) * t_pad + t) * kNope + j) = u;
+      return;
+    }
+    const int d = j - kNope;
+    if ((t & 3) == 0 && t + 3 < seqlen) {   // four consecutive keys of one sequence, aligned
+      uint2 u;
+      u.x = pack_bf16x2(v[0], v[1]);
+      u.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(vt + ((b * n_heads + h) * kVDim + d) * t_pad + vt_pos(t)) = u;
+      return;
+    }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = col0 + wc * 32 + j * 16 + r;
-    const int h = col / kKvRows, jj = col % kKvRows;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t tok0 = row0 + wt * 32 + i * 16 + grp * 4;
-      if (tok0 >= n_rows) continue;
-      const int64_t b = tok0 / seqlen;
-      const int64_t t = tok0 - b * seqlen;   // 4 consecutive tokens stay in one sequence when seqlen % 4 == 0
-      const int64_t tp = vt_pos(t);          // and at 4 consecutive permuted positions
-      const int64_t bh = b * n_heads + h;
-      if (jj < kNope) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t tk = tok0 + e;
-          if (tk >= n_rows) break;
-          const int64_t bb = tk / seqlen, tt = tk - bb * seqlen;
-          knope[((bb * n_heads + h) * t_pad + tt) * kNope + jj] = f32_to_bf16_bits(acc[i][j][e]);
-        }
-      } else if (seqlen % 4 == 0) {
-        uint2 u;
-        u.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
-        u.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-        *reinterpret_cast<uint2*>(&vt[(bh * kVDim + (jj - kNope)) * t_pad + tp]) = u;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t tk = tok0 + e;
-          if (tk >= n_rows) break;
-          const int64_t bb = tk / seqlen, tt = tk - bb * seqlen;
-          vt[((bb * n_heads + h) * kVDim + (jj - kNope)) * t_pad + vt_pos(tt)] = f32_to_bf16_bits(acc[i][j][e]);
-        }
-      }
+    for (int e = 0; e < 4; ++e) {
+      if (m + e >= n_rows) break;
+      int64_t bb, tt;
+      locate(m + e, bb, tt);
+      vt[((bb * n_heads + h) * kVDim + d) * t_pad + vt_pos(tt)] = f32_to_bf16_bits(v[e]);
     }
   }
+};
+
+__global__ __launch_bounds__(512, 1) void expand_kernel(const uint16_t* __restrict__ lat,
+                                                        const uint16_t* __restrict__ wkv_b, int n_heads, int seqlen,
+                                                        int64_t t_pad, int64_t n_rows, uint16_t* __restrict__ knope,
+                                                        uint16_t* __restrict__ vt) {
+  __shared__ __attribute__((aligned(1024))) uint8_t stage[2 * gemm::kStageBytes];
+  const int h = blockIdx.x % n_heads;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x / n_heads) * gemm::kBM;
+  const ExpandEpi epi{knope, vt, n_heads, seqlen, t_pad, n_rows, m0, m0 / seqlen};
+  gemm::nt_tile(wkv_b, static_cast<int64_t>(n_heads) * kKvRows, lat, n_rows, kKvLora, h * kKvRows, m0, 0, kKvLora,
+                stage, epi);
 }
 
 // Zero the V^T entries of keys seqlen .. t_pad-1: they sit inside the last key tile, where P is
@@ -413,8 +378,9 @@ hipError_t launch_prefill(int n_heads, int batch, int q_len, int kv_len, const u
     const int64_t n = rows * (lay.t_pad - seqlen);
     zero_vt_tail_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(vt, rows, seqlen, lay.t_pad);
   }
-  const dim3 g1(static_cast<unsigned>((n_rows + EX_BT - 1) / EX_BT), n_heads * kKvRows / EX_BC);
-  expand_kernel<<<g1, 256, 0, stream>>>(kv_latent, wkv_b, n_heads, seqlen, lay.t_pad, n_rows, knope, vt);
+  const int64_t m_tiles = (n_rows + gemm::kBM - 1) / gemm::kBM;
+  expand_kernel<<<static_cast<unsigned>(m_tiles * n_heads), 512, 0, stream>>>(kv_latent, wkv_b, n_heads, seqlen,
+                                                                              lay.t_pad, n_rows, knope, vt);
   mark(ev, 1, stream);
   {
     // blocks of one (b, h) on one XCD: grid = 8 x ceil(B H / 8) x query blocks

@@ -11,6 +11,7 @@
 // output (n contiguous), so its tiles are transposed into LDS ([n][k]) on the way in; the
 // activation tile is normalised, multiplied by the gain and rounded to bf16 on the way in,
 // which keeps the rounding point of the RMSNorm excerpt ahead of the product.
+#include "gemm_nt.hpp"
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
@@ -21,10 +22,11 @@ namespace {
 // ---------------------------------------------------------------------------------------------
 // Many tokens: the RMSNorm runs once per token, ahead of the product.
 // One wave per token: inv_rms = 1/sqrt(mean x^2 + eps) in fp32, then y = bf16(gain * (x * inv_rms))
-// (the rounding point of the RMSNorm excerpt) into the workspace, laid out as the LDS image of the
-// product's activation stages: [24 k-stages of 64][tiles of 128 tokens][128 rows][128 B], 16-byte
-// chunk c of row r at c ^ ((r >> 1) & 7). A stage of a block is then one contiguous run, loaded
-// 1 KB per instruction. Rows past the last token are written as zeros.
+// (the rounding point of the RMSNorm excerpt) into the workspace. For the mid-size product
+// (kTiled) y is laid out as the LDS image of its activation stages: [24 k-stages of 64][tiles of
+// 128 tokens][128 rows][128 B], 16-byte chunk c of row r at c ^ ((r >> 1) & 7), so that a stage of
+// a block is one contiguous run, loaded 1 KB per instruction; rows past the last token are written
+// as zeros. For the large product y is row-major [n][1536].
 // ---------------------------------------------------------------------------------------------
 constexpr int kYTile = 128;   // tokens per activation tile
 
@@ -38,17 +40,19 @@ __device__ __forceinline__ int64_t y_chunk_offset(int64_t m, int k, int64_t n_ti
   return (((static_cast<int64_t>(ks) * n_tiles + (m >> 7)) * kYTile + r) * 64) + ((c ^ ((r >> 1) & 7)) << 3);
 }
 
+template <bool kTiled>
 __global__ __launch_bounds__(256) void normalize_kernel(const uint16_t* __restrict__ x, const float* __restrict__ gamma,
                                                         int64_t n_tokens, int64_t n_tiles, float eps,
                                                         float* __restrict__ inv_rms, uint16_t* __restrict__ y) {
   const int64_t m = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (m >= n_tiles * kYTile) return;
+  if (m >= (kTiled ? n_tiles * kYTile : n_tokens)) return;
+  auto at = [&](int k) { return kTiled ? y_chunk_offset(m, k, n_tiles) : m * kQLora + k; };
   constexpr int kPer = kQLora / (64 * 8);   // 3 chunks of 8 per lane
   if (m >= n_tokens) {
     const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) *reinterpret_cast<uint4*>(y + y_chunk_offset(m, (i * 64 + lane) * 8, n_tiles)) = z;
+    for (int i = 0; i < kPer; ++i) *reinterpret_cast<uint4*>(y + at((i * 64 + lane) * 8)) = z;
     return;
   }
   const uint16_t* row = x + m * kQLora;
@@ -76,7 +80,7 @@ __global__ __launch_bounds__(256) void normalize_kernel(const uint16_t* __restri
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = g[e] * (static_cast<float>(v[i][e]) * iv);
-    *reinterpret_cast<bf16x8*>(y + y_chunk_offset(m, k, n_tiles)) = bf16x8_from_f32(o);
+    *reinterpret_cast<bf16x8*>(y + at(k)) = bf16x8_from_f32(o);
   }
 }
 
@@ -485,14 +489,91 @@ __global__ __launch_bounds__(256, 1) void query_gemm_big_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Large token counts (prefill, >= kNtTokens): wq_b is first transposed into the workspace
+// (wt[n][k], k contiguous), so that both operands of the product have k contiguous, and the tiled
+// product of gemm_nt.hpp (256 x 256 tiles, plain 128-bit operand reads) runs on wt and the
+// row-major y. The epilogue is the one above: bf16 rounding of the Linear output, RoPE of the
+// rotary pairs in registers, one 8-byte store per lane.
+// ---------------------------------------------------------------------------------------------
+constexpr int64_t kNtTokens = 1024;
+
+// wt[n][k] = wq_b[k][n], tiles of 64 k x 64 n through LDS.
+__global__ __launch_bounds__(256) void transpose_w_kernel(const uint16_t* __restrict__ w, int n_cols,
+                                                          uint16_t* __restrict__ wt) {
+  __shared__ __attribute__((aligned(16))) uint16_t t[64][64 + 8];
+  const int n0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int idx = tid + 256 * i, k = idx >> 3, ch = idx & 7;
+    *reinterpret_cast<uint4*>(&t[k][ch * 8]) = ldg16(w + static_cast<int64_t>(k0 + k) * n_cols + n0 + ch * 8);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int idx = tid + 256 * i, n = idx >> 3, kc = idx & 7;
+    uint32_t p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      p[e] = static_cast<uint32_t>(t[kc * 8 + 2 * e][n]) | (static_cast<uint32_t>(t[kc * 8 + 2 * e + 1][n]) << 16);
+    *reinterpret_cast<uint4*>(wt + static_cast<int64_t>(n0 + n) * kQLora + k0 + kc * 8) = make_uint4(p[0], p[1], p[2], p[3]);
+  }
+}
+
+struct QueryEpi {
+  const float* rope_cs;
+  uint16_t* q_out;
+  int n_cols;
+  __device__ bool transposed(int) const { return false; }
+  __device__ void store(int64_t m, int n, f32x4 acc, bool) const {
+    const int hd = n % kQk;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = round_bf16(acc[e]);   // bf16 Linear output
+    if (hd >= kNope) {
+      const int pair = (hd - kNope) >> 1;
+      const float4 cs = *reinterpret_cast<const float4*>(rope_cs + (m * (kRope / 2) + pair) * 2);
+      const float a0 = v[0], b0 = v[1], a1 = v[2], b1 = v[3];
+      v[0] = a0 * cs.x - b0 * cs.y;
+      v[1] = a0 * cs.y + b0 * cs.x;
+      v[2] = a1 * cs.z - b1 * cs.w;
+      v[3] = a1 * cs.w + b1 * cs.z;
+    }
+    uint2 u;
+    u.x = pack_bf16x2(v[0], v[1]);
+    u.y = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<uint2*>(q_out + m * n_cols + n) = u;
+  }
+};
+
+__global__ __launch_bounds__(512, 1) void query_gemm_nt_kernel(const uint16_t* __restrict__ wt,
+                                                               const uint16_t* __restrict__ y,
+                                                               const float* __restrict__ rope_cs, int64_t n_tokens,
+                                                               int n_cols, uint16_t* __restrict__ q_out) {
+  __shared__ __attribute__((aligned(1024))) uint8_t stage[2 * gemm::kStageBytes];
+  const int n_tiles = n_cols / gemm::kBN;
+  const int nt = blockIdx.x % n_tiles;
+  const int64_t mt = blockIdx.x / n_tiles;
+  const QueryEpi epi{rope_cs, q_out, n_cols};
+  gemm::nt_tile(wt, n_cols, y, n_tokens, kQLora, nt * gemm::kBN, mt * gemm::kBM, 0, kQLora, stage, epi);
+}
+
 }  // namespace
 
-QueryLayout query_layout(int64_t n_tokens) {
+QueryLayout query_layout(int n_heads, int64_t n_tokens) {
   QueryLayout L{};
   if (n_tokens <= kSmallM) return L;
-  const int64_t n_pad = y_tiles(n_tokens) * kYTile;
-  L.y_off = 0;
-  L.inv_off = align_up(static_cast<size_t>(n_pad) * kQLora * sizeof(uint16_t));
+  if (n_tokens >= kNtTokens) {
+    L.large = true;
+    L.y_off = 0;
+    L.wt_off = align_up(static_cast<size_t>(n_tokens) * kQLora * sizeof(uint16_t));
+    L.inv_off = align_up(L.wt_off + static_cast<size_t>(n_heads) * kQk * kQLora * sizeof(uint16_t));
+  } else {
+    const int64_t n_pad = y_tiles(n_tokens) * kYTile;
+    L.y_off = 0;
+    L.inv_off = align_up(static_cast<size_t>(n_pad) * kQLora * sizeof(uint16_t));
+  }
   L.total = align_up(L.inv_off + static_cast<size_t>(n_tokens) * sizeof(float));
   return L;
 }
@@ -513,14 +594,19 @@ hipError_t launch_query_path(int n_heads, int64_t n_tokens, const uint16_t* q_la
     char* ws = static_cast<char*>(workspace);
     uint16_t* y = reinterpret_cast<uint16_t*>(ws + lay.y_off);
     float* inv = inv_rms ? inv_rms : reinterpret_cast<float*>(ws + lay.inv_off);
-    const int64_t n_tiles = y_tiles(n_tokens);
-    normalize_kernel<<<static_cast<unsigned>(n_tiles * kYTile / 4), 256, 0, stream>>>(q_latent, gamma, n_tokens, n_tiles,
-                                                                                     eps, inv, y);
-    mark(ev, 1, stream);
-    if (n_tokens >= 1024) {
-      const dim3 grid(n_cols / 128, static_cast<unsigned>((n_tokens + 255) / 256));
-      query_gemm_big_kernel<128, 256><<<grid, 256, 0, stream>>>(y, wq_b, rope_cs, n_tokens, n_cols, q_out);
+    if (lay.large) {
+      uint16_t* wt = reinterpret_cast<uint16_t*>(ws + lay.wt_off);
+      transpose_w_kernel<<<dim3(n_cols / 64, kQLora / 64), 256, 0, stream>>>(wq_b, n_cols, wt);
+      normalize_kernel<false><<<static_cast<unsigned>((n_tokens + 3) / 4), 256, 0, stream>>>(q_latent, gamma, n_tokens,
+                                                                                            0, eps, inv, y);
+      mark(ev, 1, stream);
+      const int64_t blocks = static_cast<int64_t>(n_cols / gemm::kBN) * ((n_tokens + gemm::kBM - 1) / gemm::kBM);
+      query_gemm_nt_kernel<<<static_cast<unsigned>(blocks), 512, 0, stream>>>(wt, y, rope_cs, n_tokens, n_cols, q_out);
     } else {
+      const int64_t n_tiles = y_tiles(n_tokens);
+      normalize_kernel<true><<<static_cast<unsigned>(n_tiles * kYTile / 4), 256, 0, stream>>>(q_latent, gamma, n_tokens,
+                                                                                             n_tiles, eps, inv, y);
+      mark(ev, 1, stream);
       const dim3 grid(n_cols / 128, static_cast<unsigned>((n_tokens + 127) / 128));
       query_gemm_big_kernel<128, 128><<<grid, 256, 0, stream>>>(y, wq_b, rope_cs, n_tokens, n_cols, q_out);
     }
