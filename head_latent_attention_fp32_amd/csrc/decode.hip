@@ -5,7 +5,7 @@
 // the 64-wide rotary dot times the softmax scale, the softmax-weighted sum of cached latents is
 // projected out through the value half of wkv_b ("Kimi-K2 · value_states": [B,1,512] -> [B,H,1,128]).
 //
-// Four kernels, enqueued back to back on the caller's stream:
+// Three kernels, enqueued back to back on the caller's stream:
 //   1. absorb_plan   q_lat = bf16(q_nope . W_UK) per head (MFMA), and (block 0) the run plan:
 //                    prefix sums of the clamped lengths and the number of runs.
 //   2. attend        split-KV attention: the tokens of all sequences, back to back, are cut into
@@ -13,8 +13,8 @@
 //                    time, computes S^T = [kv|pe] . [q_lat|q_pe]^T and O^T += kv^T . P^T on MFMA
 //                    with an fp32 online softmax, and writes one normalised partial (o, lse) per
 //                    sequence it touches.
-//   3. combine       log-sum-exp merge of the partials of each (sequence, head) -> o_lat (bf16), lse.
-//   4. value_proj    out = bf16(o_lat . W_UV^T) per head (MFMA).
+//   3. combine_proj  log-sum-exp merge of the partials of each (sequence, head) -> o_lat (bf16, LDS)
+//                    and lse, then out = bf16(o_lat . W_UV^T) per head (MFMA).
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
@@ -671,84 +671,74 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// 3. Merge the partials of (b, 16 heads): thread = (head, 32 consecutive latent columns).
+// 3. Merge and project out, per (head h, 16 sequences): the partials of each (sequence, h) over its
+//    runs are merged by their log-sum-exp weights (o_lat = sum_s e^(lse_s - M) o_s / sum_s
+//    e^(lse_s - M), lse = M + ln sum_s e^(lse_s - M)) into a bf16 o_lat tile in LDS (thread =
+//    sequence x 16 latent columns), then out[b,h,d] = bf16(sum_c o_lat[b,c] W_UV[h,d,c]) on MFMA
+//    (A: o_lat rows from LDS; B: W_UV rows 16 w .. 16 w + 15 for wave w, from VGPRs). A sequence
+//    with no rows gets out = 0, lse = -inf.
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void combine_kernel(
-    const Plan* __restrict__ plan, const int64_t* __restrict__ cum, int n_heads,
-    const float* __restrict__ part_o, const float* __restrict__ part_l, uint16_t* __restrict__ o_lat,
-    float* __restrict__ lse) {
-  const int b = blockIdx.x;
-  const int h = blockIdx.y * 16 + (threadIdx.x >> 4);
-  const int c0 = (threadIdx.x & 15) * 32;
+__global__ __launch_bounds__(512) void combine_proj_kernel(
+    const Plan* __restrict__ plan, const int64_t* __restrict__ cum, int batch, int n_heads,
+    const float* __restrict__ part_o, const float* __restrict__ part_l, const uint16_t* __restrict__ wkv_b,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(16))) uint16_t ol[16][kKvLora + 8];
+  const int h = blockIdx.x, b0 = blockIdx.y * 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, grp = lane >> 4;
   const int64_t N = plan->total_tokens, G = plan->runs;
-  const int64_t x0 = cum[b], x1 = cum[b + 1];
-  uint16_t* dst = o_lat + (static_cast<int64_t>(b) * n_heads + h) * kKvLora + c0;
-  if (x1 <= x0) {
+
+  const uint16_t* wrow = wkv_b + (static_cast<int64_t>(h) * kKvRows + kNope + wave * 16 + r) * kKvLora + grp * 8;
+  bf16x8 bw[16];
 #pragma unroll
-    for (int i = 0; i < 32; i += 8) *reinterpret_cast<uint4*>(dst + i) = make_uint4(0, 0, 0, 0);
-    if (lse && (threadIdx.x & 15) == 0) lse[static_cast<int64_t>(b) * n_heads + h] = -INFINITY;
-    return;
-  }
-  const int64_t g0 = run_of(x0, N, G), g1 = run_of(x1 - 1, N, G);
-  float M = -INFINITY;
-  for (int64_t g = g0; g <= g1; ++g) M = fmaxf(M, part_l[(g + b) * n_heads + h]);
-  float acc[32];
+  for (int ks = 0; ks < 16; ++ks) bw[ks] = as_bf16x8(ldg16(wrow + ks * 32));
+
+  const int j = tid >> 5, c0 = (tid & 31) * 16;   // merge: sequence b0 + j, columns c0 .. c0 + 15
+  const int b = b0 + j;
+  float acc[16];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) acc[i] = 0.f;
-  float wsum = 0.f;
-  for (int64_t g = g0; g <= g1; ++g) {
-    const int64_t slot = g + b;
-    const float w = __expf(part_l[slot * n_heads + h] - M);
-    wsum += w;
-    const float4* src = reinterpret_cast<const float4*>(part_o + (slot * n_heads + h) * kKvLora + c0);
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  float M = -INFINITY, wsum = 0.f;
+  if (b < batch) {
+    const int64_t x0 = cum[b], x1 = cum[b + 1];
+    if (x1 > x0) {
+      const int64_t g0 = run_of(x0, N, G), g1 = run_of(x1 - 1, N, G);
+      for (int64_t g = g0; g <= g1; ++g) M = fmaxf(M, part_l[(g + b) * n_heads + h]);
+      for (int64_t g = g0; g <= g1; ++g) {
+        const int64_t slot = g + b;
+        const float w = __expf(part_l[slot * n_heads + h] - M);
+        wsum += w;
+        const float4* src = reinterpret_cast<const float4*>(part_o + (slot * n_heads + h) * kKvLora + c0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 v = src[i];
-      acc[4 * i + 0] += w * v.x;
-      acc[4 * i + 1] += w * v.y;
-      acc[4 * i + 2] += w * v.z;
-      acc[4 * i + 3] += w * v.w;
+        for (int i = 0; i < 4; ++i) {
+          const float4 v = src[i];
+          acc[4 * i + 0] += w * v.x;
+          acc[4 * i + 1] += w * v.y;
+          acc[4 * i + 2] += w * v.z;
+          acc[4 * i + 3] += w * v.w;
+        }
+      }
     }
+    if (lse && (tid & 31) == 0) lse[static_cast<int64_t>(b) * n_heads + h] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
   }
-  const float inv = 1.f / wsum;
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
-  for (int i = 0; i < 32; i += 8) {
+  for (int i = 0; i < 16; i += 8) {
     uint4 u;
     u.x = pack_bf16x2(acc[i + 0] * inv, acc[i + 1] * inv);
     u.y = pack_bf16x2(acc[i + 2] * inv, acc[i + 3] * inv);
     u.z = pack_bf16x2(acc[i + 4] * inv, acc[i + 5] * inv);
     u.w = pack_bf16x2(acc[i + 6] * inv, acc[i + 7] * inv);
-    *reinterpret_cast<uint4*>(dst + i) = u;
+    *reinterpret_cast<uint4*>(&ol[j][c0 + i]) = u;
   }
-  if (lse && (threadIdx.x & 15) == 0) lse[static_cast<int64_t>(b) * n_heads + h] = M + __logf(wsum);
-}
-
-// ---------------------------------------------------------------------------------------------
-// 4. out[b,h,d] = bf16(sum_c o_lat[b,h,c] W_UV[h,d,c]); block (h, 64 values of d), wave = 16 d.
-// ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void value_proj_kernel(
-    const uint16_t* __restrict__ o_lat, const uint16_t* __restrict__ wkv_b, int batch, int n_heads,
-    uint16_t* __restrict__ out) {
-  const int h = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane & 15, grp = lane >> 4;
-  const int d = blockIdx.y * 64 + wave * 16 + r;
-  const uint16_t* wrow = wkv_b + (static_cast<int64_t>(h) * kKvRows + kNope + d) * kKvLora + grp * 8;
-  bf16x8 bw[16];
+  __syncthreads();
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) bw[ks] = as_bf16x8(ldg16(wrow + ks * 32));
-  for (int b0 = 0; b0 < batch; b0 += 16) {
-    const int b = min(b0 + r, batch - 1);
-    const uint16_t* arow = o_lat + (static_cast<int64_t>(b) * n_heads + h) * kKvLora + grp * 8;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int ks = 0; ks < 16; ++ks) o = mfma16x16x32(*reinterpret_cast<const bf16x8*>(&ol[r][ks * 32 + grp * 8]), bw[ks], o);
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) acc = mfma16x16x32(as_bf16x8(ldg16(arow + ks * 32)), bw[ks], acc);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int bb = b0 + grp * 4 + j;
-      if (bb < batch) out[(static_cast<int64_t>(bb) * n_heads + h) * kVDim + blockIdx.y * 64 + wave * 16 + r] =
-          f32_to_bf16_bits(acc[j]);
-    }
+  for (int e = 0; e < 4; ++e) {
+    const int bb = b0 + grp * 4 + e;
+    if (bb < batch) out[(static_cast<int64_t>(bb) * n_heads + h) * kVDim + wave * 16 + r] = f32_to_bf16_bits(o[e]);
   }
 }
 
@@ -772,7 +762,6 @@ DecodeLayout decode_layout(int n_heads, int batch, int64_t max_seqlen, int topk)
   L.qlat_off = off;   off = align_up(off + B * H * kKvLora * sizeof(uint16_t));
   L.part_o_off = off; off = align_up(off + slots * H * kKvLora * sizeof(float));
   L.part_l_off = off; off = align_up(off + slots * H * sizeof(float));
-  L.olat_off = off;   off = align_up(off + B * H * kKvLora * sizeof(uint16_t));
   L.list_off = L.count_off = 0;
   if (topk >= 0) {
     // 64 entries of slack: the attention's scalar loads of a last partial tile may read past a
@@ -795,7 +784,6 @@ hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16
   uint16_t* q_lat = reinterpret_cast<uint16_t*>(ws + lay.qlat_off);
   float* part_o = reinterpret_cast<float*>(ws + lay.part_o_off);
   float* part_l = reinterpret_cast<float*>(ws + lay.part_l_off);
-  uint16_t* o_lat = reinterpret_cast<uint16_t*>(ws + lay.olat_off);
   const float scale_log2 = scale * kLog2e;
 
   const bool sparse = topk >= 0;
@@ -820,10 +808,9 @@ hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16
                                                        0, plan, cum, batch, n_heads, scale_log2, part_o, part_l);
   }
   mark(ev, 2, stream);
-  combine_kernel<<<dim3(batch, n_heads / 16), 256, 0, stream>>>(plan, cum, n_heads, part_o, part_l, o_lat, lse);
+  combine_proj_kernel<<<dim3(n_heads, (batch + 15) / 16), 512, 0, stream>>>(plan, cum, batch, n_heads, part_o, part_l,
+                                                                           wkv_b, out, lse);
   mark(ev, 3, stream);
-  value_proj_kernel<<<dim3(n_heads, kVDim / 64), 256, 0, stream>>>(o_lat, wkv_b, batch, n_heads, out);
-  mark(ev, 4, stream);
   return hipGetLastError();
 }
 

@@ -238,8 +238,8 @@ mla_status_t mla_output_proj(const mla_dims_t* dims, int64_t n_tokens, int32_t d
  * NULL: event i is recorded before stage i and the last after the final stage.
  *   mla_query_path_ex: 2 stages (RMSNorm pass -- empty when fused into the product, 32 tokens or
  *                      fewer --, product + RoPE)
- *   mla_decode_ex:     4 stages (absorb + run plan, split-KV attention, log-sum-exp combine, value projection)
- *   mla_decode_sparse_ex: the same 4 stages, the first also compacting the top-k lists
+ *   mla_decode_ex:     3 stages (absorb + run plan, split-KV attention, log-sum-exp combine + value projection)
+ *   mla_decode_sparse_ex: the same 3 stages, the first also compacting the top-k lists
  *   mla_output_proj_ex: 2 stages (product, sum of the K-slice partials -- empty above 64 tokens)
  *   mla_prefill_ex, mla_prefill_with_prefix_ex: 2 stages (latent expansion, causal attention) */
 mla_status_t mla_query_path_ex(const mla_dims_t* dims, int64_t n_tokens,
