@@ -28,6 +28,11 @@ COMMON = [
 ]
 
 
+# The attention kernels take row maxima of scores that are finite or -inf (masked), never NaN:
+# without NaN semantics each fmaxf is one v_max instead of two operand-quieting v_max plus the max.
+PER_FILE = {"decode.hip": ["-fno-honor-nans"], "prefill.hip": ["-fno-honor-nans"]}
+
+
 def hipcc() -> str:
     exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(exe):
@@ -57,7 +62,7 @@ def build(verbose: bool = False) -> str:
         o = os.path.join(objdir, os.path.splitext(s)[0] + ".o")
         objs.append(o)
         lang = ["-x", "hip"] if s.endswith(".cpp") else []
-        jobs.append([cc] + COMMON + lang + ["-c", os.path.join(CSRC, s), "-o", o])
+        jobs.append([cc] + COMMON + PER_FILE.get(s, []) + lang + ["-c", os.path.join(CSRC, s), "-o", o])
     with ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     tmp = LIB + ".tmp"
