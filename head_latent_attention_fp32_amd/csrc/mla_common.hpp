@@ -65,6 +65,28 @@ __device__ __forceinline__ bf16x8 bf16x8_from_f32(const float* v) {
   return as_bf16x8(u);
 }
 
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+
+// D(16x16, fp32) += A(16x32, f16) * B(32x16, f16), same lane layout as the bf16 form.
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Two fp32 -> one packed f16 pair, round-to-nearest-even.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), f16x2));
+}
+
+__device__ __forceinline__ f16x8 f16x8_from_f32(const float* v) {
+  uint4 u;
+  u.x = pack_f16x2(v[0], v[1]);
+  u.y = pack_f16x2(v[2], v[3]);
+  u.z = pack_f16x2(v[4], v[5]);
+  u.w = pack_f16x2(v[6], v[7]);
+  return __builtin_bit_cast(f16x8, u);
+}
+
 // Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48): the k-groups
 // of an MFMA operand / the row groups of its 16x16 result. v_permlane16_swap / v_permlane32_swap
 // exchange rows between two registers; called with the same value twice, the two results hold

@@ -10,7 +10,9 @@
 //
 // Two kernels:
 //   1. expand   [k_nope | v] = latent . wkv_b^T per head for all kv_len positions (MFMA GEMM, bf16
-//               outputs as the bf16 Linear of the excerpt). k_nope is written [b][h][t][128] and v
+//               outputs as the bf16 Linear of the excerpt; the values, bf16-rounded, are stored as f16,
+//               which holds every bf16 value below 65504 exactly and lets P be rounded to f16 rather
+//               than bf16 for the P.V product). k_nope is written [b][h][t][128] and v
 //               transposed, [b][h][128][t], so that the attention kernel's P.V operand reads runs of keys;
 //               within every 32 keys the order is permuted (key 16a + 4g + j at 8g + 4a + j) to
 //               match the key order in which P^T leaves the score accumulators.
@@ -68,11 +70,12 @@ struct ExpandEpi {
       *reinterpret_cast<uint2*>(knope + ((b * n_heads + h) * t_pad + t) * kNope + j) = u;
       return;
     }
+    // values: the bf16 Linear output, stored as f16 (exact for |v| < 65504) for the f16 P.V product
     const int d = j - kNope;
     if ((t & 3) == 0 && t + 3 < seqlen) {   // four consecutive keys of one sequence, aligned
       uint2 u;
-      u.x = pack_bf16x2(v[0], v[1]);
-      u.y = pack_bf16x2(v[2], v[3]);
+      u.x = pack_f16x2(round_bf16(v[0]), round_bf16(v[1]));
+      u.y = pack_f16x2(round_bf16(v[2]), round_bf16(v[3]));
       *reinterpret_cast<uint2*>(vt + ((b * n_heads + h) * kVDim + d) * t_pad + vt_pos(t)) = u;
       return;
     }
@@ -81,7 +84,8 @@ struct ExpandEpi {
       if (m + e >= n_rows) break;
       int64_t bb, tt;
       locate(m + e, bb, tt);
-      vt[((bb * n_heads + h) * kVDim + d) * t_pad + vt_pos(tt)] = f32_to_bf16_bits(v[e]);
+      vt[((bb * n_heads + h) * kVDim + d) * t_pad + vt_pos(tt)] =
+          static_cast<uint16_t>(pack_f16x2(round_bf16(v[e]), 0.f) & 0xFFFFu);
     }
   }
 };
@@ -287,7 +291,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
           }
       }
     }
-    bf16x8 pb[2][2];   // [query half][key group of 32]
+    f16x8 pb[2][2];   // [query half][key group of 32]
     bool any_up = false;
     float alpha[2];
 #pragma unroll
@@ -313,8 +317,8 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
       for (int e = 0; e < 16; e += 4) ps += (p[e] + p[e + 1]) + (p[e + 2] + p[e + 3]);
       lsum[qh] = lsum[qh] * alpha[qh] + ps;
       // k-group order of the 32-key groups: keys 4 grp + j (block 2g) then 16 + 4 grp + j (block 2g+1)
-      pb[qh][0] = bf16x8_from_f32(p);
-      pb[qh][1] = bf16x8_from_f32(p + 8);
+      pb[qh][0] = f16x8_from_f32(p);
+      pb[qh][1] = f16x8_from_f32(p + 8);
     }
     if (__any(any_up)) {
 #pragma unroll
@@ -326,9 +330,9 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
     for (int db = 0; db < 8; ++db)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 a = lds_b128(st + db * 16 * 128 + v_rd[ks]);
-        o[0][db] = mfma16x16x32(a, pb[0][ks], o[0][db]);
-        o[1][db] = mfma16x16x32(a, pb[1][ks], o[1][db]);
+        const f16x8 a = *reinterpret_cast<const f16x8*>(st + db * 16 * 128 + v_rd[ks]);
+        o[0][db] = mfma16x16x32_f16(a, pb[0][ks], o[0][db]);
+        o[1][db] = mfma16x16x32_f16(a, pb[1][ks], o[1][db]);
       }
   }
 
