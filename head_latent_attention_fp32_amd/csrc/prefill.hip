@@ -13,7 +13,8 @@
 //               outputs as the bf16 Linear of the excerpt; the values, bf16-rounded, are stored as f16,
 //               which holds every bf16 value below 65504 exactly and lets P be rounded to f16 rather
 //               than bf16 for the P.V product). k_nope is written [b][h][t][128] and v
-//               transposed, [b][h][128][t], so that the attention kernel's P.V operand reads runs of keys;
+//               transposed in key tiles of 64, [b][h][t/64][128][64], so that the attention kernel's
+//               P.V operand reads runs of keys and each tile's V^T is one contiguous 16 KB run;
 //               within every 32 keys the order is permuted (key 16a + 4g + j at 8g + 4a + j) to
 //               match the key order in which P^T leaves the score accumulators.
 //   2. attend   flash-style causal attention: block = (b, h, 128 queries), wave = 32 queries;
@@ -34,7 +35,7 @@ constexpr int kKBlk = 64;     // key padding granule of the expanded k_nope / V^
 //    on the tiled product of gemm_nt.hpp: a 256-column tile is one head. Waves on its k_nope half
 //    keep the normal orientation (four consecutive features of one token: an 8-byte store into
 //    k_nope[b][h][t][:]); waves on its value half take the transposed product (four consecutive
-//    tokens of one feature: an 8-byte store into V^T[b][h][d][:], whose key order is permuted
+//    tokens of one feature: an 8-byte store into V^T of (b, h, d), whose key order is permuted
 //    within groups of 32 but keeps groups of 4 consecutive keys together).
 // ---------------------------------------------------------------------------------------------
 
@@ -42,6 +43,13 @@ constexpr int kKBlk = 64;     // key padding granule of the expanded k_nope / V^
 __device__ __forceinline__ int64_t vt_pos(int64_t t) {
   const int64_t w = t & 31;
   return (t - w) + ((w >> 2) & 3) * 8 + (w >> 4) * 4 + (w & 3);
+}
+
+// Element offset of V^T entry (dim d, key t) within one (b, h): the keys are kept in tiles of 64
+// ([t / 64][128 dims][64 keys], 16 KB per tile), so that the attention kernel's V^T tile is one
+// contiguous run; inside a tile the keys are permuted as vt_pos does.
+__device__ __forceinline__ int64_t vt_index(int d, int64_t t) {
+  return ((t >> 6) * kVDim + d) * 64 + (vt_pos(t) & 63);
 }
 
 struct ExpandEpi {
@@ -76,7 +84,7 @@ struct ExpandEpi {
       uint2 u;
       u.x = pack_f16x2(round_bf16(v[0]), round_bf16(v[1]));
       u.y = pack_f16x2(round_bf16(v[2]), round_bf16(v[3]));
-      *reinterpret_cast<uint2*>(vt + ((b * n_heads + h) * kVDim + d) * t_pad + vt_pos(t)) = u;
+      *reinterpret_cast<uint2*>(vt + (b * n_heads + h) * kVDim * t_pad + vt_index(d, t)) = u;
       return;
     }
 #pragma unroll
@@ -84,7 +92,7 @@ struct ExpandEpi {
       if (m + e >= n_rows) break;
       int64_t bb, tt;
       locate(m + e, bb, tt);
-      vt[((bb * n_heads + h) * kVDim + d) * t_pad + vt_pos(tt)] =
+      vt[(bb * n_heads + h) * kVDim * t_pad + vt_index(d, tt)] =
           static_cast<uint16_t>(pack_f16x2(round_bf16(v[e]), 0.f) & 0xFFFFu);
     }
   }
@@ -110,7 +118,7 @@ __global__ __launch_bounds__(256) void zero_vt_tail_kernel(uint16_t* __restrict_
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= rows * w) return;
   const int64_t row = i / w;
-  vt[row * t_pad + vt_pos(seqlen + (i - row * w))] = 0;
+  vt[(row / kVDim) * kVDim * t_pad + vt_index(static_cast<int>(row % kVDim), seqlen + (i - row * w))] = 0;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -212,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
     const int key = 4 * d + (lane >> 4);
     kn_off[e] = static_cast<uint32_t>(key * 256 + (((lane & 15) ^ swz_kn(key)) << 4));
     const int dim = 8 * d + (lane >> 3);
-    vt_off[e] = static_cast<uint32_t>(dim * t_pad * 2 + (((lane & 7) ^ swz_128(dim)) << 4));
+    vt_off[e] = static_cast<uint32_t>(dim * 128 + (((lane & 7) ^ swz_128(dim)) << 4));
   }
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
@@ -226,7 +234,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
     const auto rk = make_rsrc(kn + static_cast<int64_t>(k0) * kNope, static_cast<uint32_t>(t_pad - k0) * 256u);
     const int rows_pe = kv_len - k0;
     const auto rp = make_rsrc(pe + static_cast<int64_t>(k0) * kRope, static_cast<uint32_t>(rows_pe) * 128u);
-    const auto rv = make_rsrc(vh + k0, static_cast<uint32_t>(kVDim * t_pad - k0) * 2u);
+    const auto rv = make_rsrc(vh + static_cast<int64_t>(k0) * kVDim, static_cast<uint32_t>(kVDim * (t_pad - k0)) * 2u);
 #pragma unroll
     for (int e = 0; e < 4; ++e) dma16(rk, dst + (wave + 4 * e) * 1024, kn_off[e]);
 #pragma unroll
