@@ -31,6 +31,16 @@ struct Plan {
 };
 
 __device__ __forceinline__ int64_t run_start(int64_t g, int64_t N, int64_t G) { return g * N / G; }
+
+// Where run g starts: its first sequence b, the position t0 of its first row in b, the boundary
+// cum[b + 1] where b ends, and b's first cache row (written by the plan so that an attention block
+// reaches its first rows with one load).
+struct RunStart {
+  int64_t row_base;
+  int64_t next;
+  int32_t b;
+  int32_t t0;
+};
 // Run containing global token x (0 <= x < N).
 __device__ __forceinline__ int64_t run_of(int64_t x, int64_t N, int64_t G) { return ((x + 1) * G - 1) / N; }
 
@@ -42,13 +52,15 @@ __device__ __forceinline__ int64_t run_of(int64_t x, int64_t N, int64_t G) { ret
 __global__ __launch_bounds__(256) void absorb_plan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ wkv_b, int batch, int n_heads,
     uint16_t* __restrict__ q_lat, const int32_t* __restrict__ seqlens, int64_t max_seqlen,
-    int units, int min_unit_tokens, Plan* __restrict__ plan, int64_t* __restrict__ cum) {
+    int units, int min_unit_tokens, Plan* __restrict__ plan, int64_t* __restrict__ cum,
+    const int64_t* __restrict__ row_offset, int64_t cache_rows_per_seq, RunStart* __restrict__ runs) {
   const int tid = threadIdx.x;
   const int h = blockIdx.x;
   const int c0 = blockIdx.y * 64;
 
   __shared__ uint16_t wt[64][kNope + 8];
   __shared__ int64_t scan[256];
+  __shared__ int64_t total_runs[2];
 
   if (blockIdx.x == 0 && blockIdx.y == 0) {
     // cum[b] = sum_{b' < b} clamp(L_b', 0, max_seqlen); each thread owns a contiguous chunk.
@@ -64,7 +76,8 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
       scan[tid] += v;
       __syncthreads();
     }
-    int64_t run = scan[tid] - s;
+    const int64_t chunk0 = scan[tid] - s;   // cum[b0]
+    int64_t run = chunk0;
     for (int b = b0; b < b1; ++b) {
       cum[b] = run;
       run += min<int64_t>(max<int64_t>(seqlens[b], 0), max_seqlen);
@@ -77,6 +90,28 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
       plan->total_tokens = N;
       plan->runs = static_cast<int32_t>(N > 0 ? max<int64_t>(G, 1) : 0);
       plan->pad = 0;
+      total_runs[0] = N;
+      total_runs[1] = N > 0 ? max<int64_t>(G, 1) : 0;
+    }
+    __syncthreads();   // the run count is known
+    // Each thread writes the records of the runs that start in its own sequences: run g starts in
+    // sequence b iff cum[b] <= g N / G < cum[b+1], i.e. ceil(cum[b] G / N) <= g < ceil(cum[b+1] G / N).
+    const int64_t N = total_runs[0], G = total_runs[1];
+    if (G > 0) {
+      int64_t lo = chunk0;
+      for (int b = b0; b < b1; ++b) {
+        const int64_t hi = lo + min<int64_t>(max<int64_t>(seqlens[b], 0), max_seqlen);
+        const int64_t row_base = row_offset ? row_offset[b] : static_cast<int64_t>(b) * cache_rows_per_seq;
+        for (int64_t g = (lo * G + N - 1) / N; g < (hi * G + N - 1) / N; ++g) {
+          RunStart rs;
+          rs.b = b;
+          rs.t0 = static_cast<int32_t>(run_start(g, N, G) - lo);
+          rs.next = hi;
+          rs.row_base = row_base;
+          runs[g] = rs;
+        }
+        lo = hi;
+      }
     }
   }
 
@@ -270,6 +305,7 @@ struct AttendCtx {
   const int32_t* list;       // top-k mode: attended positions of each sequence, compacted; else null
   int list_pitch;
   const int64_t* cum;
+  const RunStart* runs;
   int batch, n_heads, head0;
   int64_t g, start, end;
   float scale_log2;
@@ -294,23 +330,24 @@ struct Segment {
 struct SegmentWalk {
   int64_t start;
   int b;
-  __device__ SegmentWalk(const AttendCtx& c) : start(c.start) {
-    int lo = 0, hi = c.batch - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (c.cum[mid + 1] > start) hi = mid; else lo = mid + 1;
-    }
-    b = lo;
+  bool first;
+  RunStart rs;
+  __device__ SegmentWalk(const AttendCtx& c) : start(c.start), first(true) {
+    rs = c.runs[c.g];
+    b = rs.b;
   }
   __device__ bool next(const AttendCtx& c, Segment& sg) {
     if (start >= c.end) return false;
-    const int64_t seq0 = c.cum[b];
-    const int64_t seg_end = min(c.end, c.cum[b + 1]);
+    // the run's first segment comes from its record; later ones from the prefix sums
+    const int64_t seq0 = first ? start - rs.t0 : c.cum[b];
+    const int64_t seg_end = min(c.end, first ? rs.next : c.cum[b + 1]);
     const int t0 = static_cast<int>(start - seq0);
     sg.b = b;
     sg.n_rows = static_cast<int>(seg_end - start);
     sg.n_tiles = (sg.n_rows + kTileTok - 1) / kTileTok;
-    const int64_t base = c.row_offset ? c.row_offset[b] : static_cast<int64_t>(b) * c.max_seqlen;
+    const int64_t base = first ? rs.row_base
+                               : (c.row_offset ? c.row_offset[b] : static_cast<int64_t>(b) * c.max_seqlen);
+    first = false;
     const int64_t row0 = c.list ? base : base + t0;
     sg.kv_seg = c.kv + row0 * kKvLora;
     sg.pe_seg = c.pe + row0 * kRope;
@@ -639,8 +676,8 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(
     const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const uint16_t* __restrict__ pe, const int64_t* __restrict__ row_offset, int64_t max_seqlen,
     const int32_t* __restrict__ list, int list_pitch,
-    const Plan* __restrict__ plan, const int64_t* __restrict__ cum, int batch, int n_heads, float scale_log2,
-    float* __restrict__ part_o, float* __restrict__ part_l) {
+    const Plan* __restrict__ plan, const int64_t* __restrict__ cum, const RunStart* __restrict__ runs, int batch,
+    int n_heads, float scale_log2, float* __restrict__ part_o, float* __restrict__ part_l) {
   // The blocks of the head groups of one run share blockIdx mod 8 -- the same XCD and its L2 --
   // and are dispatched next to each other, so the tiles one of them pulls from HBM are L2 hits for
   // the others.
@@ -660,7 +697,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(
   AttendCtx c;
   c.q_lat = q_lat; c.q = q; c.kv = kv; c.pe = pe; c.row_offset = row_offset; c.max_seqlen = max_seqlen;
   c.list = kGather ? list : nullptr; c.list_pitch = list_pitch;
-  c.cum = cum; c.batch = batch; c.n_heads = n_heads; c.head0 = hg * kBlockHeads;
+  c.cum = cum; c.runs = runs; c.batch = batch; c.n_heads = n_heads; c.head0 = hg * kBlockHeads;
   c.g = g; c.start = run_start(g, N, G); c.end = run_start(g + 1, N, G);
   c.scale_log2 = scale_log2; c.part_o = part_o; c.part_l = part_l;
   c.ring = ring; c.pbuf = pbuf; c.xbuf = xbuf; c.alpha_s = alpha_s; c.flag_s = flag_s;
@@ -759,6 +796,7 @@ DecodeLayout decode_layout(int n_heads, int batch, int64_t max_seqlen, int topk)
   size_t off = 0;
   L.plan_off = off;   off = align_up(off + sizeof(Plan));
   L.cum_off = off;    off = align_up(off + (B + 1) * sizeof(int64_t));
+  L.runs_off = off;   off = align_up(off + static_cast<size_t>(L.units) * sizeof(RunStart));
   L.qlat_off = off;   off = align_up(off + B * H * kKvLora * sizeof(uint16_t));
   L.part_o_off = off; off = align_up(off + slots * H * kKvLora * sizeof(float));
   L.part_l_off = off; off = align_up(off + slots * H * sizeof(float));
@@ -781,6 +819,7 @@ hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16
   char* ws = static_cast<char*>(workspace);
   Plan* plan = reinterpret_cast<Plan*>(ws + lay.plan_off);
   int64_t* cum = reinterpret_cast<int64_t*>(ws + lay.cum_off);
+  RunStart* runs = reinterpret_cast<RunStart*>(ws + lay.runs_off);
   uint16_t* q_lat = reinterpret_cast<uint16_t*>(ws + lay.qlat_off);
   float* part_o = reinterpret_cast<float*>(ws + lay.part_o_off);
   float* part_l = reinterpret_cast<float*>(ws + lay.part_l_off);
@@ -795,17 +834,17 @@ hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16
   // the run plan covers the attended rows: L_b per sequence, or the count of its top-k positions
   absorb_plan_kernel<<<dim3(n_heads, kKvLora / 64), 256, 0, stream>>>(
       q, wkv_b, batch, n_heads, q_lat, sparse ? counts : seqlens, sparse ? topk : max_seqlen, lay.units,
-      lay.min_unit_tokens, plan, cum);
+      lay.min_unit_tokens, plan, cum, row_offset, max_seqlen, runs);
   mark(ev, 1, stream);
   {
     const int n_groups = (n_heads + 63) / 64;
     const int blocks = (lay.units + 7) / 8 * 8 * n_groups;
     if (sparse)
       attend_kernel<true><<<blocks, 512, 0, stream>>>(q_lat, q, kv_cache, pe_cache, row_offset, max_seqlen, list, topk,
-                                                      plan, cum, batch, n_heads, scale_log2, part_o, part_l);
+                                                      plan, cum, runs, batch, n_heads, scale_log2, part_o, part_l);
     else
       attend_kernel<false><<<blocks, 512, 0, stream>>>(q_lat, q, kv_cache, pe_cache, row_offset, max_seqlen, nullptr,
-                                                       0, plan, cum, batch, n_heads, scale_log2, part_o, part_l);
+                                                       0, plan, cum, runs, batch, n_heads, scale_log2, part_o, part_l);
   }
   mark(ev, 2, stream);
   combine_proj_kernel<<<dim3(n_heads, (batch + 15) / 16), 512, 0, stream>>>(plan, cum, batch, n_heads, part_o, part_l,
