@@ -47,7 +47,7 @@ __device__ __forceinline__ int64_t run_of(int64_t x, int64_t N, int64_t G) { ret
 // ---------------------------------------------------------------------------------------------
 // 1. q_lat[b,h,c] = bf16(sum_d q[b,h,d] W_UK[h,d,c]); block (h, 64-column slice of c).
 //    W_UK[h] rows are stored with c contiguous, so the slice is transposed into LDS ([c][d]) to
-//    give the MFMA B operand eight consecutive d per lane. Block (0,0) also builds the plan.
+//    give the MFMA B operand eight consecutive d per lane. Block (0, 8) builds the plan.
 // ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void absorb_plan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ wkv_b, int batch, int n_heads,
@@ -62,7 +62,9 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
   __shared__ int64_t scan[256];
   __shared__ int64_t total_runs[2];
 
-  if (blockIdx.x == 0 && blockIdx.y == 0) {
+  if (blockIdx.y == kKvLora / 64) {
+    // the plan, in a block of its own beside the absorb blocks
+    if (blockIdx.x != 0) return;
     // cum[b] = sum_{b' < b} clamp(L_b', 0, max_seqlen); each thread owns a contiguous chunk.
     const int per = (batch + 255) / 256;
     const int b0 = min(batch, tid * per), b1 = min(batch, b0 + per);
@@ -113,6 +115,17 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
         lo = hi;
       }
     }
+    return;
+  }
+
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, grp = lane >> 4;
+  // the first 16 queries' content part, loaded ahead of the weight slice
+  uint4 qa[4];
+  {
+    const uint16_t* qrow = q + (static_cast<int64_t>(min(r, batch - 1)) * n_heads + h) * kQk;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qa[ks] = ldg16(qrow + ks * 32 + grp * 8);
   }
 
   // Transposed W_UK[h][0:128][c0:c0+64] -> wt[c][d].
@@ -127,8 +140,6 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
   }
   __syncthreads();
 
-  const int lane = tid & 63, wave = tid >> 6;
-  const int r = lane & 15, grp = lane >> 4;
   bf16x8 bw[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
@@ -140,7 +151,7 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
     const uint16_t* qrow = q + (static_cast<int64_t>(min(b, batch - 1)) * n_heads + h) * kQk;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 a = as_bf16x8(ldg16(qrow + ks * 32 + grp * 8));
+      const bf16x8 a = as_bf16x8(b0 == 0 ? qa[ks] : ldg16(qrow + ks * 32 + grp * 8));
       acc = mfma16x16x32(a, bw[ks], acc);
     }
 #pragma unroll
@@ -832,7 +843,7 @@ hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16
   mark(ev, 0, stream);
   if (sparse) topk_compact_kernel<<<batch, 256, 0, stream>>>(topk_indices, topk, seqlens, max_seqlen, list, counts);
   // the run plan covers the attended rows: L_b per sequence, or the count of its top-k positions
-  absorb_plan_kernel<<<dim3(n_heads, kKvLora / 64), 256, 0, stream>>>(
+  absorb_plan_kernel<<<dim3(n_heads, kKvLora / 64 + 1), 256, 0, stream>>>(
       q, wkv_b, batch, n_heads, q_lat, sparse ? counts : seqlens, sparse ? topk : max_seqlen, lay.units,
       lay.min_unit_tokens, plan, cum, row_offset, max_seqlen, runs);
   mark(ev, 1, stream);
