@@ -88,27 +88,40 @@ __global__ __launch_bounds__(256) void normalize_kernel(const uint16_t* __restri
 // Small token counts (decode, n <= 32): the weights dominate (1536 x 192 H bf16), so the kernel
 // streams them at full width and keeps the activation in registers.
 //
-// Persistent: one block of 4 waves per CU walks a list of 64-column slices (4 n-blocks of 16; a
-// 128-byte line of each weight row).
+// One block of 4 waves per CU works on column slices of 16 NB columns (NB n-blocks of 16): 64
+// columns (128 B of each weight row) when the slices outnumber the CUs, persistent over a list of
+// them; otherwise 128 columns (256 B per row, which HBM streams faster), one slice per block.
 // Wave w owns the k-range [384 w, 384 w + 384) in 12 steps of 32: it holds x for its k-range and
 // both 16-token m-blocks in VGPRs (loaded once per block), takes the row statistics from those
-// registers (sums of squares exchanged through LDS), and streams the weight rows of all its slices
-// through a private 6-deep LDS ring with direct-to-LDS loads, without a break between slices and
-// without a barrier in the k loop. The MFMA A operand (W^T: 16 columns x 8 consecutive k) comes
-// from the ring with ds_read_b64_tr_b16, the transposing LDS read; B is y = bf16(gamma x inv_rms)
-// from registers. After each slice the four partial sums are added through LDS and the epilogue
-// (bf16 rounding of the Linear output, RoPE, bf16 store) is the one of query_gemm_kernel.
-// Ring step layout [32 k rows][128 B]: 16-byte chunk c of row k at c ^ 2 gx(k), gx(k) =
-// ((k >> 1) & 1) | (((k >> 3) & 1) << 1), so the 8 rows of a half-wave's transposing read (two
-// groups of 4 consecutive rows) fall into distinct 32-byte bank groups.
+// registers (sums of squares exchanged through LDS), and streams the weight rows of its slices
+// through a private LDS ring (6 steps of 4 KB, or 4 of 8 KB) with direct-to-LDS loads, without a
+// barrier in the k loop. The MFMA A operand (W^T: 16 columns x 8 consecutive k) comes from the ring
+// with ds_read_b64_tr_b16, the transposing LDS read; B is y = bf16(gamma x inv_rms) from
+// registers. After each slice the four partial sums are added through LDS (the ring itself when a
+// block has one slice) and the epilogue rounds the Linear output to bf16, rotates the rotary pairs
+// and stores bf16.
+// Ring step layout [32 k rows][16 NB columns], so that the 8 rows of a half-wave's transposing read
+// (two groups of 4 consecutive rows) fall into distinct 32-byte bank groups:
+//   NB = 4: 16-byte chunk c of row k at c ^ 2 gx(k), gx(k) = ((k >> 1) & 1) | (((k >> 3) & 1) << 1);
+//   NB = 8: 32-byte group g of row k at g ^ f(k), f(k) = (k & 3) | ((k >> 1) & 4).
 // ---------------------------------------------------------------------------------------------
-constexpr int kSmallN = 64;          // columns per slice
 constexpr int kSmallM = 32;          // largest token count of the small kernel
 constexpr int kWaveK = kQLora / 4;   // 384
 constexpr int kSteps = kWaveK / 32;  // 12 k-steps per slice
-constexpr int kRingSteps = 6;
-constexpr int kStepBytes = 32 * kSmallN * 2;   // 4096
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
+
+template <int NB>
+struct SmallCfg {
+  static constexpr int kCols = 16 * NB;                        // columns per slice
+  static constexpr int kRowBytes = kCols * 2;                  // 128 or 256
+  static constexpr int kStepBytes = 32 * kRowBytes;            // 4 or 8 KB
+  static constexpr int kLoads = kStepBytes / 1024;             // loads per wave and step
+  static constexpr int kRing = NB == 4 ? 6 : 4;                // steps in a wave's ring
+  static constexpr int kRingBytes = 4 * kRing * kStepBytes;    // 96 or 128 KB
+  static constexpr int kRedBytes = 4 * 2 * NB * 64 * 16;       // 32 or 64 KB
+  static constexpr bool kOneSlice = NB == 8;                   // one slice per block, reduction in the ring
+  static constexpr int kLdsBytes = kOneSlice ? kRingBytes : kRingBytes + kRedBytes;
+};
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
@@ -139,14 +152,17 @@ __device__ __forceinline__ void wait_vm() {
 // Slice t of XCD x's list: x, x + 8, x + 16, ...
 __device__ __forceinline__ int slice_of(int x, int t) { return x + 8 * t; }
 __device__ __forceinline__ int gx(int k) { return ((k >> 1) & 1) | (((k >> 3) & 1) << 1); }
+__device__ __forceinline__ int wswz(int k) { return (k & 3) | ((k >> 1) & 4); }
 
+template <int NB>
 __global__ __launch_bounds__(256, 1) void query_gemm_small_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ gamma, const uint16_t* __restrict__ wq_b,
     const float* __restrict__ rope_cs, int n_tokens, int n_cols, float eps, float* __restrict__ inv_rms,
     uint16_t* __restrict__ q_out) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[4][kRingSteps * kStepBytes];   // 96 KB
-  __shared__ __attribute__((aligned(16))) float4 red[4][8][64];                         // 32 KB
+  using C = SmallCfg<NB>;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLdsBytes];
   __shared__ float ss_s[4][kSmallM];
+  float4* red = reinterpret_cast<float4*>(lds + (C::kOneSlice ? 0 : C::kRingBytes));   // [4][2 NB][64]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -154,28 +170,36 @@ __global__ __launch_bounds__(256, 1) void query_gemm_small_kernel(
   const int k0 = wave * kWaveK;
   // this block's slices: entries i, i + per, i + 2 per, ... of its XCD's list
   const int xcd = blockIdx.x & 7, i0 = blockIdx.x >> 3, per = gridDim.x >> 3;
-  const int list_len = n_cols / kSmallN / 8;
+  const int list_len = n_cols / C::kCols / 8;
   const int n_mine = i0 < list_len ? (list_len - i0 + per - 1) / per : 0;
   const int total_steps = n_mine * kSteps;
 
   // Weight rows k0 .. k0 + 383 of the whole matrix through one descriptor; global step g is slice
-  // g / 12 of this block, k-step g % 12: four loads of 8 rows x 128 B.
+  // g / 12 of this block, k-step g % 12: kLoads loads of 1 KB (8 rows of 128 B or 4 rows of 256 B).
   const uint16_t* wbase = wq_b + static_cast<int64_t>(k0) * n_cols;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(wbase, static_cast<uint32_t>(kWaveK) * n_cols * 2u);
-  const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)&ring[wave][0]));
-  uint32_t w_voff[4];
+  uint8_t* ring = lds + wave * C::kRing * C::kStepBytes;
+  const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)ring));
+  uint32_t w_voff[C::kLoads];
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const int row = 8 * d + (lane >> 3);
-    const int chunk = (lane & 7) ^ (2 * gx(row));
-    w_voff[d] = static_cast<uint32_t>(row * n_cols * 2 + chunk * 16);
+  for (int d = 0; d < C::kLoads; ++d) {
+    if constexpr (NB == 4) {
+      const int row = 8 * d + (lane >> 3);
+      const int chunk = (lane & 7) ^ (2 * gx(row));
+      w_voff[d] = static_cast<uint32_t>(row * n_cols * 2 + chunk * 16);
+    } else {
+      const int row = 4 * d + (lane >> 4);
+      const int pc = lane & 15;
+      const int lc = (((pc >> 1) ^ wswz(row)) << 1) | (pc & 1);
+      w_voff[d] = static_cast<uint32_t>(row * n_cols * 2 + lc * 16);
+    }
   }
   auto issue = [&](int g) {
     const int sl = slice_of(xcd, i0 + per * (g / kSteps));
-    const uint32_t off = static_cast<uint32_t>(g % kSteps) * 32u * n_cols * 2u + sl * kSmallN * 2u;
-    const uint32_t dst = ring_lds + (g % kRingSteps) * kStepBytes;
+    const uint32_t off = static_cast<uint32_t>(g % kSteps) * 32u * n_cols * 2u + sl * C::kRowBytes;
+    const uint32_t dst = ring_lds + (g % C::kRing) * C::kStepBytes;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) dma16(rw, dst + d * 1024, w_voff[d] + off);
+    for (int d = 0; d < C::kLoads; ++d) dma16(rw, dst + d * 1024, w_voff[d] + off);
   };
   // Activation of tokens 16 mb + r (clamped to the last token), k-group grp of each step. Its loads
   // go out ahead of the weight ring (they are waited for first).
@@ -188,7 +212,7 @@ __global__ __launch_bounds__(256, 1) void query_gemm_small_kernel(
     for (int st = 0; st < kSteps; ++st) xf[mb][st] = as_bf16x8(ldg16(row + st * 32));
   }
   int issued = 0;
-  while (issued < kRingSteps && issued < total_steps) issue(issued++);
+  while (issued < C::kRing && issued < total_steps) issue(issued++);
   float ss[2] = {0.f, 0.f};
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
@@ -232,37 +256,42 @@ __global__ __launch_bounds__(256, 1) void query_gemm_small_kernel(
 
   // A operand of n-block nb, k rows 8 grp + 4 h .. +3 of a step: source lane j of a 16-lane group
   // reads row 8 grp + 4 h + j/4 at columns 16 nb + 4 (j%4) .. +3.
-  int a_off[4][2];
+  int a_off[NB][2];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int row = 8 * grp + 4 * h + (r >> 2);
-      const int c = 2 * nb + ((r & 3) >> 1);
-      a_off[nb][h] = row * 128 + ((c ^ (2 * gx(row))) << 4) + 8 * (r & 1);
+      if constexpr (NB == 4) {
+        const int c = 2 * nb + ((r & 3) >> 1);
+        a_off[nb][h] = row * 128 + ((c ^ (2 * gx(row))) << 4) + 8 * (r & 1);
+      } else {
+        a_off[nb][h] = row * 256 + ((nb ^ wswz(row)) << 5) + 8 * (r & 3);
+      }
     }
 
   for (int j = 0; j < n_mine; ++j) {
-    f32x4 acc[4][2];
+    f32x4 acc[NB][2];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
       const int g = j * kSteps + st;
-      // loads of up to 5 later steps may stay in flight
+      // loads of up to kRing - 1 later steps may stay in flight
       const int after = issued - 1 - g;
-      if (after >= 5) wait_vm<20>();
-      else if (after == 4) wait_vm<16>();
-      else if (after == 3) wait_vm<12>();
-      else if (after == 2) wait_vm<8>();
-      else if (after == 1) wait_vm<4>();
+      constexpr int L = C::kLoads;
+      if (C::kRing == 6 && after >= 5) wait_vm<5 * L>();
+      else if (C::kRing == 6 && after == 4) wait_vm<4 * L>();
+      else if (after >= 3) wait_vm<3 * L>();
+      else if (after == 2) wait_vm<2 * L>();
+      else if (after == 1) wait_vm<L>();
       else wait_vm<0>();
-      const uint8_t* base = &ring[wave][(g % kRingSteps) * kStepBytes];
-      bf16x8 af[4];
+      const uint8_t* base = ring + (g % C::kRing) * C::kStepBytes;
+      bf16x8 af[NB];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+      for (int nb = 0; nb < NB; ++nb) {
         const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(base + a_off[nb][0]));
         const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(base + a_off[nb][1]));
         af[nb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -273,62 +302,67 @@ __global__ __launch_bounds__(256, 1) void query_gemm_small_kernel(
         issue(issued++);
       }
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma16x16x32(af[nb], xf[mb][st], acc[nb][mb]);
     }
 
-    // Sum of the four waves' partials: wave w finalises output blocks (nb, mb) = (w, 0), (w, 1).
+    // Sum of the four waves' partials: wave w finalises n-blocks w NB/4 .. w NB/4 + NB/4 - 1.
+    if (C::kOneSlice) __syncthreads();   // every wave's ring reads are done before it is overwritten
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const f32x4 v = acc[nb][mb];
-        red[wave][nb * 2 + mb][lane] = make_float4(v[0], v[1], v[2], v[3]);
+        red[(wave * 2 * NB + nb * 2 + mb) * 64 + lane] = make_float4(v[0], v[1], v[2], v[3]);
       }
     __syncthreads();
-    float vv[2][4];
+    constexpr int kOwn = NB / 4;   // n-blocks finalised per wave
+    float vv[kOwn][2][4];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int o = 0; o < kOwn; ++o)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vv[mb][e] = 0.f;
+      for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float4 u = red[w][wave * 2 + mb][lane];
-        vv[mb][0] += u.x;
-        vv[mb][1] += u.y;
-        vv[mb][2] += u.z;
-        vv[mb][3] += u.w;
+        for (int e = 0; e < 4; ++e) vv[o][mb][e] = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float4 u = red[(w * 2 * NB + (wave * kOwn + o) * 2 + mb) * 64 + lane];
+          vv[o][mb][0] += u.x;
+          vv[o][mb][1] += u.y;
+          vv[o][mb][2] += u.z;
+          vv[o][mb][3] += u.w;
+        }
       }
-    }
-    __syncthreads();   // red is rewritten for the next slice
-    const int nb = wave;
+    if (!C::kOneSlice) __syncthreads();   // red is rewritten for the next slice
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-    // lane holds q[m][n .. n+3], m = 16 mb + r, n = n0 + 16 nb + 4 grp
-    float* v = vv[mb];
-    const int m = 16 * mb + r;
-    if (m < n_tokens) {
-      const int n = slice_of(xcd, i0 + per * j) * kSmallN + 16 * nb + 4 * grp;
-      const int hd = n % kQk;
+    for (int o = 0; o < kOwn; ++o)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = round_bf16(v[e]);   // bf16 Linear output
-      if (hd >= kNope) {
-        const int pair = (hd - kNope) >> 1;
-        const float4 cs =
-            *reinterpret_cast<const float4*>(rope_cs + (static_cast<int64_t>(m) * (kRope / 2) + pair) * 2);
-        const float a0 = v[0], b0 = v[1], a1 = v[2], b1 = v[3];
-        v[0] = a0 * cs.x - b0 * cs.y;
-        v[1] = a0 * cs.y + b0 * cs.x;
-        v[2] = a1 * cs.z - b1 * cs.w;
-        v[3] = a1 * cs.w + b1 * cs.z;
+      for (int mb = 0; mb < 2; ++mb) {
+        // lane holds q[m][n .. n+3], m = 16 mb + r, n = slice start + 16 nb + 4 grp
+        float* v = vv[o][mb];
+        const int m = 16 * mb + r;
+        if (m < n_tokens) {
+          const int n = slice_of(xcd, i0 + per * j) * C::kCols + 16 * (wave * kOwn + o) + 4 * grp;
+          const int hd = n % kQk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = round_bf16(v[e]);   // bf16 Linear output
+          if (hd >= kNope) {
+            const int pair = (hd - kNope) >> 1;
+            const float4 cs =
+                *reinterpret_cast<const float4*>(rope_cs + (static_cast<int64_t>(m) * (kRope / 2) + pair) * 2);
+            const float a0 = v[0], b0 = v[1], a1 = v[2], b1 = v[3];
+            v[0] = a0 * cs.x - b0 * cs.y;
+            v[1] = a0 * cs.y + b0 * cs.x;
+            v[2] = a1 * cs.z - b1 * cs.w;
+            v[3] = a1 * cs.w + b1 * cs.z;
+          }
+          uint2 u;
+          u.x = pack_bf16x2(v[0], v[1]);
+          u.y = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<uint2*>(q_out + static_cast<int64_t>(m) * n_cols + n) = u;
+        }
       }
-      uint2 u;
-      u.x = pack_bf16x2(v[0], v[1]);
-      u.y = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<uint2*>(q_out + static_cast<int64_t>(m) * n_cols + n) = u;
-    }
-    }
   }
 }
 
@@ -355,8 +389,6 @@ struct BigTile {
   static constexpr int kWLoads = kWBytes / 1024 / 4; // direct-to-LDS loads per wave per stage
   static constexpr int kYLoads = kYBytes / 1024 / 4;
 };
-
-__device__ __forceinline__ int wswz(int k) { return (k & 3) | ((k >> 1) & 4); }
 
 template <int BN, int BM>
 __global__ __launch_bounds__(256, 1) void query_gemm_big_kernel(
@@ -584,12 +616,18 @@ hipError_t launch_query_path(int n_heads, int64_t n_tokens, const uint16_t* q_la
   const int n_cols = n_heads * kQk;
   mark(ev, 0, stream);
   if (n_tokens <= kSmallM) {
-    // one block per CU (at most one per slice); a multiple of 8 so that every XCD has blocks
-    const int n_slices = n_cols / kSmallN;
-    const int grid = n_slices < 256 ? n_slices : 256;
+    // one block per CU (at most one per slice); slice counts are multiples of 8, so every XCD has
+    // blocks. Slices of 128 columns when they do not outnumber the CUs (one per block), else 64.
     mark(ev, 1, stream);
-    query_gemm_small_kernel<<<grid, 256, 0, stream>>>(q_latent, gamma, wq_b, rope_cs, static_cast<int>(n_tokens),
-                                                      n_cols, eps, inv_rms, q_out);
+    if (n_cols / SmallCfg<8>::kCols <= 256 && n_cols / SmallCfg<8>::kCols >= 128) {
+      query_gemm_small_kernel<8><<<n_cols / SmallCfg<8>::kCols, 256, 0, stream>>>(
+          q_latent, gamma, wq_b, rope_cs, static_cast<int>(n_tokens), n_cols, eps, inv_rms, q_out);
+    } else {
+      const int n_slices = n_cols / SmallCfg<4>::kCols;
+      const int grid = n_slices < 256 ? n_slices : 256;
+      query_gemm_small_kernel<4><<<grid, 256, 0, stream>>>(q_latent, gamma, wq_b, rope_cs,
+                                                           static_cast<int>(n_tokens), n_cols, eps, inv_rms, q_out);
+    }
   } else {
     char* ws = static_cast<char*>(workspace);
     uint16_t* y = reinterpret_cast<uint16_t*>(ws + lay.y_off);
