@@ -719,19 +719,20 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// 3. Merge and project out, per (head h, 16 sequences): the partials of each (sequence, h) over its
-//    runs are merged by their log-sum-exp weights (o_lat = sum_s e^(lse_s - M) o_s / sum_s
-//    e^(lse_s - M), lse = M + ln sum_s e^(lse_s - M)) into a bf16 o_lat tile in LDS (thread =
-//    sequence x 16 latent columns), then out[b,h,d] = bf16(sum_c o_lat[b,c] W_UV[h,d,c]) on MFMA
-//    (A: o_lat rows from LDS; B: W_UV rows 16 w .. 16 w + 15 for wave w, from VGPRs). A sequence
-//    with no rows gets out = 0, lse = -inf.
+// 3. Merge and project out, per (head h, group of 16 sequences); a block takes every gridDim.y-th
+//    group of its head, keeping the head's W_UV in registers across them. The partials of each
+//    (sequence, h) over its runs are merged by their log-sum-exp weights (o_lat = sum_s
+//    e^(lse_s - M) o_s / sum_s e^(lse_s - M), lse = M + ln sum_s e^(lse_s - M)) into a bf16 o_lat
+//    tile in LDS (thread = sequence x 16 latent columns), then out[b,h,d] = bf16(sum_c o_lat[b,c]
+//    W_UV[h,d,c]) on MFMA (A: o_lat rows from LDS; B: W_UV rows 16 w .. 16 w + 15 for wave w, from
+//    VGPRs). A sequence with no rows gets out = 0, lse = -inf.
 // ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(512) void combine_proj_kernel(
     const Plan* __restrict__ plan, const int64_t* __restrict__ cum, int batch, int n_heads,
     const float* __restrict__ part_o, const float* __restrict__ part_l, const uint16_t* __restrict__ wkv_b,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) uint16_t ol[16][kKvLora + 8];
-  const int h = blockIdx.x, b0 = blockIdx.y * 16;
+  const int h = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, grp = lane >> 4;
   const int64_t N = plan->total_tokens, G = plan->runs;
@@ -742,55 +743,61 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
   for (int ks = 0; ks < 16; ++ks) bw[ks] = as_bf16x8(ldg16(wrow + ks * 32));
 
   const int j = tid >> 5, c0 = (tid & 31) * 16;   // merge: sequence b0 + j, columns c0 .. c0 + 15
-  const int b = b0 + j;
-  float acc[16];
+  // groups of 16 sequences b0, b0 + 16 gridDim.y, ...: W_UV stays in registers across them
+  for (int b0 = blockIdx.y * 16; b0 < batch; b0 += gridDim.y * 16) {
+    const int b = b0 + j;
+    float acc[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  float M = -INFINITY, wsum = 0.f;
-  if (b < batch) {
-    const int64_t x0 = cum[b], x1 = cum[b + 1];
-    if (x1 > x0) {
-      const int64_t g0 = run_of(x0, N, G), g1 = run_of(x1 - 1, N, G);
-      for (int64_t g = g0; g <= g1; ++g) M = fmaxf(M, part_l[(g + b) * n_heads + h]);
-      for (int64_t g = g0; g <= g1; ++g) {
-        const int64_t slot = g + b;
-        const float w = __expf(part_l[slot * n_heads + h] - M);
-        wsum += w;
-        const float4* src = reinterpret_cast<const float4*>(part_o + (slot * n_heads + h) * kKvLora + c0);
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    float M = -INFINITY, wsum = 0.f;
+    if (b < batch) {
+      const int64_t x0 = cum[b], x1 = cum[b + 1];
+      if (x1 > x0) {
+        const int64_t g0 = run_of(x0, N, G), g1 = run_of(x1 - 1, N, G);
+        for (int64_t g = g0; g <= g1; ++g) M = fmaxf(M, part_l[(g + b) * n_heads + h]);
+        for (int64_t g = g0; g <= g1; ++g) {
+          const int64_t slot = g + b;
+          const float w = __expf(part_l[slot * n_heads + h] - M);
+          wsum += w;
+          const float4* src = reinterpret_cast<const float4*>(part_o + (slot * n_heads + h) * kKvLora + c0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 v = src[i];
-          acc[4 * i + 0] += w * v.x;
-          acc[4 * i + 1] += w * v.y;
-          acc[4 * i + 2] += w * v.z;
-          acc[4 * i + 3] += w * v.w;
+          for (int i = 0; i < 4; ++i) {
+            const float4 v = src[i];
+            acc[4 * i + 0] += w * v.x;
+            acc[4 * i + 1] += w * v.y;
+            acc[4 * i + 2] += w * v.z;
+            acc[4 * i + 3] += w * v.w;
+          }
         }
       }
+      if (lse && (tid & 31) == 0) lse[static_cast<int64_t>(b) * n_heads + h] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
     }
-    if (lse && (tid & 31) == 0) lse[static_cast<int64_t>(b) * n_heads + h] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
-  }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    if (b0 != static_cast<int>(blockIdx.y) * 16) __syncthreads();   // the previous group's reads of ol are done
 #pragma unroll
-  for (int i = 0; i < 16; i += 8) {
-    uint4 u;
-    u.x = pack_bf16x2(acc[i + 0] * inv, acc[i + 1] * inv);
-    u.y = pack_bf16x2(acc[i + 2] * inv, acc[i + 3] * inv);
-    u.z = pack_bf16x2(acc[i + 4] * inv, acc[i + 5] * inv);
-    u.w = pack_bf16x2(acc[i + 6] * inv, acc[i + 7] * inv);
-    *reinterpret_cast<uint4*>(&ol[j][c0 + i]) = u;
-  }
-  __syncthreads();
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 16; i += 8) {
+      uint4 u;
+      u.x = pack_bf16x2(acc[i + 0] * inv, acc[i + 1] * inv);
+      u.y = pack_bf16x2(acc[i + 2] * inv, acc[i + 3] * inv);
+      u.z = pack_bf16x2(acc[i + 4] * inv, acc[i + 5] * inv);
+      u.w = pack_bf16x2(acc[i + 6] * inv, acc[i + 7] * inv);
+      *reinterpret_cast<uint4*>(&ol[j][c0 + i]) = u;
+    }
+    __syncthreads();
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) o = mfma16x16x32(*reinterpret_cast<const bf16x8*>(&ol[r][ks * 32 + grp * 8]), bw[ks], o);
+    for (int ks = 0; ks < 16; ++ks) o = mfma16x16x32(*reinterpret_cast<const bf16x8*>(&ol[r][ks * 32 + grp * 8]), bw[ks], o);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int bb = b0 + grp * 4 + e;
-    if (bb < batch) out[(static_cast<int64_t>(bb) * n_heads + h) * kVDim + wave * 16 + r] = f32_to_bf16_bits(o[e]);
+    for (int e = 0; e < 4; ++e) {
+      const int bb = b0 + grp * 4 + e;
+      if (bb < batch) out[(static_cast<int64_t>(bb) * n_heads + h) * kVDim + wave * 16 + r] = f32_to_bf16_bits(o[e]);
+    }
   }
 }
 
 }  // namespace
+
+constexpr int kMergeBlocks = 512;
 
 DecodeLayout decode_layout(int n_heads, int batch, int64_t max_seqlen, int topk) {
   DecodeLayout L{};
@@ -858,8 +865,13 @@ hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16
                                                        0, plan, cum, runs, batch, n_heads, scale_log2, part_o, part_l);
   }
   mark(ev, 2, stream);
-  combine_proj_kernel<<<dim3(n_heads, (batch + 15) / 16), 512, 0, stream>>>(plan, cum, batch, n_heads, part_o, part_l,
-                                                                           wkv_b, out, lse);
+  {
+    // at most kMergeBlocks blocks, each with its head's W_UV in registers for as many sequence
+    // groups as that leaves to it
+    const int groups = (batch + 15) / 16, per_head = kMergeBlocks / n_heads;
+    combine_proj_kernel<<<dim3(n_heads, groups < per_head ? groups : per_head), 512, 0, stream>>>(
+        plan, cum, batch, n_heads, part_o, part_l, wkv_b, out, lse);
+  }
   mark(ev, 3, stream);
   return hipGetLastError();
 }
