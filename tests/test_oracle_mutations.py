@@ -55,6 +55,34 @@ MUTANTS = {
                                [(TN, "test_output_proj_width_flatten_order_and_library")]),
     "gain_ignored": ("y = np.asarray(gamma, dtype=np.float64) * (x * inv)", "y = (x * inv) + 0 * np.asarray(gamma)",
                      [(TA, "test_query_path_matches_torch_complex_route")]),
+    "lse_in_log2": ("return (p @ c) / l, (m + np.log(l))[:, 0]", "return (p @ c) / l, (m + np.log2(l))[:, 0]",
+                    [(TA, "test_decode_matches_torch_sdpa"), (TA, "test_decode_special_cases")]),
+    "combine_lse_without_max": ("lse = np.where(tot > 0, safe_M + np.log(np.where(tot > 0, tot, 1.0)), -np.inf)",
+                                "lse = np.where(tot > 0, np.log(np.where(tot > 0, tot, 1.0)), -np.inf)",
+                                [(TA, "test_split_partition_invariance")]),
+    "prefill_scale_dropped": ("s = scale * (k[: t + 1] @ q_h[r])", "s = (k[: t + 1] @ q_h[r])",
+                              [(TA, "test_prefill_first_row_future_rows_and_sdpa")]),
+    "prefill_rotary_key_dropped": ("k = np.concatenate([k_nope_h, k_pe], axis=1)",
+                                   "k = np.concatenate([k_nope_h, 0 * k_pe], axis=1)",
+                                   [(TA, "test_prefill_first_row_future_rows_and_sdpa"),
+                                    (TA, "test_prefill_row_equals_decode_over_prefix")]),
+    "expand_value_from_key_half": ("v = np.stack([c @ uv[h].T for h in heads], axis=1)",
+                                   "v = np.stack([c @ uk[h].T for h in heads], axis=1)",
+                                   [(TA, "test_prefill_row_equals_decode_over_prefix"),
+                                    (TA, "test_prefill_first_row_future_rows_and_sdpa")]),
+    "kv_rotary_key_not_rotated": ("pe = rope_rotate(a[:, KV_LORA:], np.asarray(rope_cs, np.float64))",
+                                  "pe = a[:, KV_LORA:] + 0 * np.asarray(rope_cs, np.float64)[:, :1, 0]",
+                                  [(TN, "test_kv_side_rotary_key")]),
+    "kv_norm_gain_ignored": ("lat, _ = rms_norm(a[:, :KV_LORA], kv_gamma, eps)",
+                             "lat, _ = rms_norm(a[:, :KV_LORA], np.ones(KV_LORA), eps)",
+                             [(TN, "test_kv_side_latent_norm_and_library")]),
+    "topk_first_position_unselectable": ("mask[idx[(idx >= 0) & (idx < L)]] = 0.0",
+                                         "mask[idx[(idx >= 1) & (idx < L)]] = 0.0",
+                                         [(TN, "test_topk_all_positions_is_dense_decode"),
+                                          (TN, "test_topk_special_cases")]),
+    "wo_not_transposed": ("return _maybe_round(x @ w.T, staged)",
+                          "return _maybe_round(x @ w.reshape(w.shape[1], w.shape[0]), staged)",
+                          [(TN, "test_output_proj_width_flatten_order_and_library")]),
 }
 
 
