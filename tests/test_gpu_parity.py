@@ -43,8 +43,9 @@ def _run_query(x, g, w, cs, H, with_inv=True):
     return host_bits(q), (inv.cpu().numpy() if with_inv else None)
 
 
-@pytest.mark.parametrize("H,n,with_inv", [(16, 1, True), (64, 1, True), (128, 5, False), (128, 64, True),
-                                          (64, 67, True), (32, 130, False), (128, 200, True)])
+@pytest.mark.parametrize("H,n,with_inv", [(16, 1, True), (64, 1, True), (128, 1, True), (128, 5, False),
+                                          (128, 32, True), (64, 32, False), (16, 32, True), (128, 33, True),
+                                          (128, 64, True), (64, 67, True), (32, 130, False), (128, 200, True)])
 def test_query_path_parity(H, n, with_inv):
     say(f"query_path H={H} n={n} inv={with_inv}")
     x, g, w, cs = _query_case(H, n, 0, 200 + H + n)
