@@ -393,33 +393,44 @@ __device__ __forceinline__ void issue_tile(const AttendCtx& c, const Segment& sg
 
 // Top-k mode: the tile's rows are the cache rows of the positions list_seg[32 t .. 32 t + 31] of
 // the sequence (read with scalar loads: the list is uniform across the wave and never changes
-// during the kernel). Rows past the segment get a position one past the descriptors' range
-// (max_seqlen rows from the sequence's first), so they read as zeros. kv_chunk[k] and pe_chunk are
-// the lane's byte offsets within its row.
+// during the kernel), fetched one issue ahead (TilePos) so that their latency is not paid at the
+// issue. Rows past the segment get a position one past the descriptors' range (max_seqlen rows
+// from the sequence's first), so they read as zeros. kv_chunk[k] and pe_chunk are the lane's byte
+// offsets within its row.
 typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
-__device__ __forceinline__ void issue_tile_gather(const AttendCtx& c, const Segment& sg, int t, const uint32_t* kv_chunk,
-                                                  uint32_t pe_chunk) {
+struct TilePos {
+  uint32_t kv[8];   // rows v + 4k of the tile (v = value wave)
+  uint32_t pe[8];   // rows 8v + j
+};
+__device__ __forceinline__ void load_tile_pos(const AttendCtx& c, const Segment& sg, int t, TilePos& p) {
   const int v = c.wave & 3;
   const int left = sg.n_rows - t * kTileTok;
   const uint32_t past = static_cast<uint32_t>(c.max_seqlen);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(sg.kv_seg, past * 1024u);
-  const __amdgpu_buffer_rsrc_t rp = make_rsrc(sg.pe_seg, past * 128u);
   const const_i32_ptr ti = (const_i32_ptr)(sg.list_seg + t * kTileTok);
-  const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)c.ring)) +
-                       (t % kStages) * kTileBytes;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int row = v + 4 * k;
-    const uint32_t pos = row < left ? static_cast<uint32_t>(ti[row]) : past;
-    dma16(rk, dst + row * 1024, pos * 1024u + kv_chunk[k]);
+    p.kv[k] = row < left ? static_cast<uint32_t>(ti[row]) : past;
   }
-  uint32_t ppos = past;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int row = 8 * v + j;
-    const uint32_t pos = row < left ? static_cast<uint32_t>(ti[row]) : past;
-    ppos = (c.lane >> 3) == j ? pos : ppos;
+    p.pe[j] = row < left ? static_cast<uint32_t>(ti[row]) : past;
   }
+}
+__device__ __forceinline__ void issue_tile_gather(const AttendCtx& c, const Segment& sg, int t, const uint32_t* kv_chunk,
+                                                  uint32_t pe_chunk, const TilePos& p) {
+  const int v = c.wave & 3;
+  const uint32_t past = static_cast<uint32_t>(c.max_seqlen);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(sg.kv_seg, past * 1024u);
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(sg.pe_seg, past * 128u);
+  const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)c.ring)) +
+                       (t % kStages) * kTileBytes;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) dma16(rk, dst + (v + 4 * k) * 1024, p.kv[k] * 1024u + kv_chunk[k]);
+  uint32_t ppos = past;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ppos = (c.lane >> 3) == j ? p.pe[j] : ppos;
   dma16(rp, dst + kKvBytes + v * 1024, ppos * 128u + pe_chunk);
 }
 
@@ -595,9 +606,14 @@ __device__ __forceinline__ void value_role(const AttendCtx& c) {
   }
   const int pe_row = 8 * w + (lane >> 3);
   const uint32_t pe_voff = static_cast<uint32_t>((kGather ? 0 : pe_row * 128) + (((lane & 7) ^ fp(pe_row)) << 4));
+  TilePos pos;   // top-k mode: positions of the next tile to issue
   auto issue = [&](const Segment& sg, int t) {
-    if (kGather) issue_tile_gather(c, sg, t, kv_voff, pe_voff);
-    else issue_tile(c, sg, t, kv_voff, pe_voff);
+    if (kGather) {
+      issue_tile_gather(c, sg, t, kv_voff, pe_voff, pos);
+      if (t + 1 < sg.n_tiles) load_tile_pos(c, sg, t + 1, pos);
+    } else {
+      issue_tile(c, sg, t, kv_voff, pe_voff);
+    }
   };
   // V^T: source row 4 grp + (r>>2) (+16), columns 16 (8 w + cb) + 4 (r&3) .. +3 at physical chunk
   // pair (8 w + cb) ^ (row & 7). P^T: head 16 hb + r, chunk grp.
@@ -612,6 +628,7 @@ __device__ __forceinline__ void value_role(const AttendCtx& c) {
   while (walk.next(c, sg)) {
     const int n_tiles = sg.n_tiles;
     int issued = 0;
+    if (kGather) load_tile_pos(c, sg, 0, pos);
     while (issued < kStages && issued < n_tiles) issue(sg, issued++);
 
     f32x4 o[8][4];   // O^T[16 (8 w + cb) + 4 grp + j][16 hb + r]
@@ -658,6 +675,9 @@ __device__ __forceinline__ void value_role(const AttendCtx& c) {
       // phase A: operand reads, then loads (bound by the load unit), while the score waves'
       // MFMAs own the pipes
       read_values(it);
+      // top-k mode: the operand reads are complete before the next tile's position loads go out,
+      // so that the waits for later LDS reads do not include those scalar loads
+      if (kGather) __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
       if (issued < n_tiles && issued <= it + 3) issue(sg, issued++);
       lds_barrier();
       // phase B: the value MFMAs of tile it beside the softmax of tile it+1
