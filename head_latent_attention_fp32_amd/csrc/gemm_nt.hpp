@@ -23,7 +23,8 @@ namespace gemm {
 
 constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kStageBytes = (kBM + kBN) * kBK * 2;              // 64 KB
-constexpr int kLoadsPerWave = kStageBytes / 1024 / 8;           // 8 loads of 1 KB per wave and step
+constexpr int kIssuers = 4;                                     // waves 0-3 issue the loads
+constexpr int kLoadsPerWave = kStageBytes / 1024 / kIssuers;    // 16 loads of 1 KB per issuing wave and step
 constexpr uint32_t kRsrcWord3 = 0x00020000u;                    // raw buffer, 32-bit data format
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -63,18 +64,22 @@ __device__ __forceinline__ void nt_tile(const uint16_t* __restrict__ w, int64_t 
   const int wm = wave >> 2, wn = wave & 3;
 
   // Loads: instruction d (0..63) of a step covers 8 rows x 128 B: d < 32 weight rows 8d.., else
-  // token rows 8(d-32)..; wave w issues d = w + 8e. Lane l: row 8d' + l/8, physical chunk l%8
+  // token rows 8(d-32)..; wave w < 4 issues d = w + 4e, waves 4-7 none. Waves w and w + 4 share a
+  // SIMD, so while one stalls issuing loads (the address unit takes a step's 64 KB at 64 B per
+  // clock) the other's MFMAs keep the matrix pipe busy. Lane l: row 8d' + l/8, physical chunk l%8
   // holding logical chunk (l%8) ^ swz(row).
+  const bool issuer = wave < kIssuers;
   uint32_t voff[kLoadsPerWave];
 #pragma unroll
   for (int e = 0; e < kLoadsPerWave; ++e) {
-    const int d = wave + 8 * e;
+    const int d = (wave & (kIssuers - 1)) + kIssuers * e;
     const int row = 8 * (d & 31) + (lane >> 3);
     voff[e] = static_cast<uint32_t>(row * K * 2 + (((lane & 7) ^ swz(row)) << 4));
   }
   const uint32_t st_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void_t*)stage));
   const int64_t w_left = w_rows - n0, x_left = x_rows - m0;
   auto issue = [&](int kt) {
+    if (!issuer) return;
     // descriptors rebuilt per step (scalar work): short-lived, they stay in SGPRs
     const __amdgpu_buffer_rsrc_t rw = rsrc(w + static_cast<int64_t>(n0) * K, static_cast<uint32_t>(w_left * K * 2));
     const __amdgpu_buffer_rsrc_t rx = rsrc(x + m0 * K, static_cast<uint32_t>(x_left * K * 2));
@@ -82,7 +87,7 @@ __device__ __forceinline__ void nt_tile(const uint16_t* __restrict__ w, int64_t 
     const uint32_t dst = st_lds + (kt & 1) * kStageBytes;
 #pragma unroll
     for (int e = 0; e < kLoadsPerWave; ++e) {
-      const int d = wave + 8 * e;
+      const int d = wave + kIssuers * e;
       if (d < 32) dma16(rw, dst + d * 1024, voff[e] + koff);
       else dma16(rx, dst + d * 1024, voff[e] + koff);
     }
@@ -112,7 +117,7 @@ __device__ __forceinline__ void nt_tile(const uint16_t* __restrict__ w, int64_t 
     for (int kt = 0; kt < n_kt; ++kt) {
       __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));   // vmcnt(0): this wave's loads of kt
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-      __builtin_amdgcn_s_barrier();                                // everyone's; stage kt-1 free
+      __builtin_amdgcn_s_barrier();                                // all loads of kt; stage kt-1 free
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
       if (kt + 1 < n_kt) issue(kt + 1);
       const uint8_t* st = stage + (kt & 1) * kStageBytes;
