@@ -6,6 +6,8 @@
 // steps of 64 through two LDS stages (64 KB each: 256 weight rows, then 256 token rows of 128 B)
 // filled by 16-byte direct-to-LDS buffer loads, the next step's loads in flight during this step's
 // MFMAs; one barrier per step. Rows past either operand's end read as zeros (descriptor range).
+// Only waves 0-3 (one per SIMD) issue the loads, so that on every SIMD one wave's MFMAs run while
+// the other waits for the address unit to take its loads.
 // Stage rows: 16-byte chunk c of row r at c ^ ((r >> 1) & 7), so every 128-bit operand read
 // (16 rows, 4 chunks) is free of LDS bank conflicts.
 // Per wave and k-step: 4 weight and 8 token operands (ds_read_b128), 32 MFMA 16x16x32.
