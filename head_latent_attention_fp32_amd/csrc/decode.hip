@@ -98,19 +98,53 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
     __syncthreads();   // the run count is known
     // Each thread writes the records of the runs that start in its own sequences: run g starts in
     // sequence b iff cum[b] <= g N / G < cum[b+1], i.e. ceil(cum[b] G / N) <= g < ceil(cum[b+1] G / N).
+    // run_start(g) = floor(g N / G) is stepped from run to run (quotient and remainder of N / G)
+    // rather than divided out per record.
     const int64_t N = total_runs[0], G = total_runs[1];
-    if (G > 0) {
+    if (G > 0 && per == 1) {
+      // at most one sequence per thread: thread i writes runs i, i + 256, ...; run g starts in the
+      // first sequence b whose inclusive prefix sum scan[b] exceeds run_start(g)
+      for (int64_t g = tid; g < G; g += 256) {
+        const int64_t q = run_start(g, N, G);
+        int lo_b = 0, hi_b = batch - 1;
+        while (lo_b < hi_b) {
+          const int mid = (lo_b + hi_b) >> 1;
+          if (scan[mid] > q) hi_b = mid;
+          else lo_b = mid + 1;
+        }
+        const int b = lo_b;
+        const int64_t first = b > 0 ? scan[b - 1] : 0;
+        RunStart rs;
+        rs.b = b;
+        rs.t0 = static_cast<int32_t>(q - first);
+        rs.next = scan[b];
+        rs.row_base = row_offset ? row_offset[b] : static_cast<int64_t>(b) * cache_rows_per_seq;
+        runs[g] = rs;
+      }
+    } else if (G > 0) {
+      const int64_t qN = N / G, rN = N % G;
       int64_t lo = chunk0;
       for (int b = b0; b < b1; ++b) {
         const int64_t hi = lo + min<int64_t>(max<int64_t>(seqlens[b], 0), max_seqlen);
         const int64_t row_base = row_offset ? row_offset[b] : static_cast<int64_t>(b) * cache_rows_per_seq;
-        for (int64_t g = (lo * G + N - 1) / N; g < (hi * G + N - 1) / N; ++g) {
-          RunStart rs;
-          rs.b = b;
-          rs.t0 = static_cast<int32_t>(run_start(g, N, G) - lo);
-          rs.next = hi;
-          rs.row_base = row_base;
-          runs[g] = rs;
+        int64_t g = (lo * G + N - 1) / N;           // first run starting at or after lo
+        if (g < G && hi > lo) {
+          int64_t q = g * N / G, rem = g * N - q * G;   // q = run_start(g)
+          while (g < G && q < hi) {                    // runs starting in [lo, hi)
+            RunStart rs;
+            rs.b = b;
+            rs.t0 = static_cast<int32_t>(q - lo);
+            rs.next = hi;
+            rs.row_base = row_base;
+            runs[g] = rs;
+            ++g;
+            q += qN;
+            rem += rN;
+            if (rem >= G) {
+              ++q;
+              rem -= G;
+            }
+          }
         }
         lo = hi;
       }
@@ -751,7 +785,11 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
     const Plan* __restrict__ plan, const int64_t* __restrict__ cum, int batch, int n_heads,
     const float* __restrict__ part_o, const float* __restrict__ part_l, const uint16_t* __restrict__ wkv_b,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) uint16_t ol[16][kKvLora + 8];
+  // one buffer for the parts' partial merges (fp32 [16][512]) and, after them, the bf16 o_lat tile
+  __shared__ __attribute__((aligned(16))) float4 mbuf[16 * kKvLora / 4];
+  __shared__ float pm_s[16][2];
+  float (*pa_s)[kKvLora] = reinterpret_cast<float (*)[kKvLora]>(mbuf);
+  uint16_t (*ol)[kKvLora + 8] = reinterpret_cast<uint16_t (*)[kKvLora + 8]>(mbuf);
   const int h = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, grp = lane >> 4;
@@ -762,20 +800,25 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) bw[ks] = as_bf16x8(ldg16(wrow + ks * 32));
 
-  const int j = tid >> 5, c0 = (tid & 31) * 16;   // merge: sequence b0 + j, columns c0 .. c0 + 15
+  const int j = tid >> 5, c0 = (tid & 31) * 16;   // thread group j (32 threads), columns c0 .. c0 + 15
   // groups of 16 sequences b0, b0 + 16 gridDim.y, ...: W_UV stays in registers across them
   for (int b0 = blockIdx.y * 16; b0 < batch; b0 += gridDim.y * 16) {
-    const int b = b0 + j;
+    // With fewer than 9 sequences in the group, each sequence's runs are shared by `parts` thread
+    // groups (runs part, part + parts, ...), whose partial merges are then merged through LDS.
+    const int nseq = min(16, batch - b0);
+    const int parts = nseq <= 1 ? 16 : nseq <= 2 ? 8 : nseq <= 4 ? 4 : nseq <= 8 ? 2 : 1;
+    const int js = j / parts, part = j % parts;   // sequence b0 + js
+    const int b = b0 + js;
     float acc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
     float M = -INFINITY, wsum = 0.f;
-    if (b < batch) {
+    if (js < nseq) {
       const int64_t x0 = cum[b], x1 = cum[b + 1];
       if (x1 > x0) {
-        const int64_t g0 = run_of(x0, N, G), g1 = run_of(x1 - 1, N, G);
-        for (int64_t g = g0; g <= g1; ++g) M = fmaxf(M, part_l[(g + b) * n_heads + h]);
-        for (int64_t g = g0; g <= g1; ++g) {
+        const int64_t g0 = run_of(x0, N, G) + part, g1 = run_of(x1 - 1, N, G);
+        for (int64_t g = g0; g <= g1; g += parts) M = fmaxf(M, part_l[(g + b) * n_heads + h]);
+        for (int64_t g = g0; g <= g1; g += parts) {
           const int64_t slot = g + b;
           const float w = __expf(part_l[slot * n_heads + h] - M);
           wsum += w;
@@ -790,18 +833,54 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
           }
         }
       }
-      if (lse && (tid & 31) == 0) lse[static_cast<int64_t>(b) * n_heads + h] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
     }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    if (b0 != static_cast<int>(blockIdx.y) * 16) __syncthreads();   // the previous group's reads of ol are done
+    if (parts > 1) {
+      // merge of the parts: thread group (js, 0) takes the others' (M, wsum, acc) from LDS
+      if (b0 != static_cast<int>(blockIdx.y) * 16) __syncthreads();   // previous group's o_lat read
+      pm_s[j][0] = M;
+      pm_s[j][1] = wsum;
 #pragma unroll
-    for (int i = 0; i < 16; i += 8) {
-      uint4 u;
-      u.x = pack_bf16x2(acc[i + 0] * inv, acc[i + 1] * inv);
-      u.y = pack_bf16x2(acc[i + 2] * inv, acc[i + 3] * inv);
-      u.z = pack_bf16x2(acc[i + 4] * inv, acc[i + 5] * inv);
-      u.w = pack_bf16x2(acc[i + 6] * inv, acc[i + 7] * inv);
-      *reinterpret_cast<uint4*>(&ol[j][c0 + i]) = u;
+      for (int i = 0; i < 16; i += 4)
+        *reinterpret_cast<float4*>(&pa_s[j][c0 + i]) = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
+      __syncthreads();
+      if (part == 0) {
+        float Mt = M;
+        for (int q = 1; q < parts; ++q) Mt = fmaxf(Mt, pm_s[j + q][0]);
+        const float a0 = M == -INFINITY ? 0.f : __expf(M - Mt);
+        wsum *= a0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] *= a0;
+        for (int q = 1; q < parts; ++q) {
+          const float Mq = pm_s[j + q][0];
+          const float aq = Mq == -INFINITY ? 0.f : __expf(Mq - Mt);
+          wsum += aq * pm_s[j + q][1];
+#pragma unroll
+          for (int i = 0; i < 16; i += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(&pa_s[j + q][c0 + i]);
+            acc[i] += aq * v.x;
+            acc[i + 1] += aq * v.y;
+            acc[i + 2] += aq * v.z;
+            acc[i + 3] += aq * v.w;
+          }
+        }
+        M = Mt;
+      }
+    }
+    if (js < nseq && part == 0 && lse && (tid & 31) == 0)
+      lse[static_cast<int64_t>(b) * n_heads + h] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    // the parts' partials, or the previous group's o_lat, are read before o_lat is written
+    if (parts > 1 || b0 != static_cast<int>(blockIdx.y) * 16) __syncthreads();
+    if (part == 0) {
+#pragma unroll
+      for (int i = 0; i < 16; i += 8) {
+        uint4 u;
+        u.x = pack_bf16x2(acc[i + 0] * inv, acc[i + 1] * inv);
+        u.y = pack_bf16x2(acc[i + 2] * inv, acc[i + 3] * inv);
+        u.z = pack_bf16x2(acc[i + 4] * inv, acc[i + 5] * inv);
+        u.w = pack_bf16x2(acc[i + 6] * inv, acc[i + 7] * inv);
+        *reinterpret_cast<uint4*>(&ol[js][c0 + i]) = u;
+      }
     }
     __syncthreads();
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
@@ -818,15 +897,26 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
 }  // namespace
 
 constexpr int kMergeBlocks = 512;
+constexpr int64_t kMinRunTokens = 64;
 
 DecodeLayout decode_layout(int n_heads, int batch, int64_t max_seqlen, int topk) {
   DecodeLayout L{};
-  L.min_unit_tokens = 256;
   // attended rows: at most max_seqlen per sequence, or topk in top-k mode (topk >= 0)
   const int64_t upper = static_cast<int64_t>(batch) * (topk >= 0 ? topk : max_seqlen);
-  int64_t units = (upper + L.min_unit_tokens - 1) / L.min_unit_tokens;
   // one block per compute unit: 256 CUs, shared by the head groups of a run
   const int64_t max_units = 256 / ((n_heads + 63) / 64);
+  // Runs of 256 tokens or more; shorter (whole tiles, down to kMinRunTokens) when the runs would
+  // not fill the chip, so that a short cache is not read by a few blocks one tile after another.
+  // Shorter runs mean more partials (H x 2 KB each) for the merge to read: a block's time grows
+  // with its run (about 0.9 us per tile of 32 tokens) and the merge's with the number of runs
+  // (H x 2 KB each at about 5 TB/s), which balance near 0.12 sqrt(tokens x H) tokens per run.
+  int64_t run_tokens = (upper + max_units - 1) / max_units;
+  const int64_t balance = static_cast<int64_t>(0.12 * std::sqrt(static_cast<double>(upper) * n_heads));
+  run_tokens = run_tokens > balance ? run_tokens : balance;
+  run_tokens = (run_tokens + 31) / 32 * 32;
+  run_tokens = run_tokens < kMinRunTokens ? kMinRunTokens : (run_tokens > 256 ? 256 : run_tokens);
+  L.min_unit_tokens = static_cast<int>(run_tokens);
+  int64_t units = (upper + L.min_unit_tokens - 1) / L.min_unit_tokens;
   units = units < 1 ? 1 : (units > max_units ? max_units : units);
   L.units = static_cast<int>(units);
   const size_t B = static_cast<size_t>(batch), H = static_cast<size_t>(n_heads);
