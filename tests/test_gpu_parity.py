@@ -92,6 +92,12 @@ DECODE_SMALL = [
     (16, [1], "padded"), (64, [31], "padded"), (64, [32], "padded"), (64, [33], "padded"),
     (128, [1000], "padded"), (32, [0, 5, 300], "padded"), (128, [257, 1, 0, 64, 512], "padded"),
     (64, [3, 700, 45, 0, 1, 96], "packed"), (128, [2049, 17], "packed"), (16, [0, 0], "padded"),
+    # short caches: runs shorter than 256 tokens, a sequence's runs merged by several thread groups
+    (128, [4096], "padded"),
+    (128, [(37 * i) % 500 + 1 for i in range(20)], "packed"),
+    # 72 sequences over 4 merge blocks per head: a block's second group holds 8 sequences
+    (128, [(53 * i) % 300 for i in range(72)], "packed"),
+    (64, [(29 * i) % 400 + 33 for i in range(40)], "padded"),
 ]
 
 
