@@ -249,13 +249,14 @@ __global__ __launch_bounds__(256) void topk_compact_kernel(const int32_t* __rest
 //                        adds O^T[c][h] += sum_t tile[t][c] P^T[t][h] (A operand:
 //                        ds_read_b64_tr_b16, the transposing LDS read, of tile columns; B operand:
 //                        ds_read_b128 of P).
-//    The iteration of tile t has two phases, each closed by a barrier. Phase A: the score waves
-//    compute S(t+1) with the MFMA pipes to themselves while the value waves issue the loads of tile
-//    t+3 (bound by the load unit). Phase B: the score waves' softmax of tile t+1 runs beside the
-//    value waves' MFMAs of tile t. The barrier that closes phase B hands P(t+1), its rescale factors
-//    and flags (double-buffered by tile parity) to the value waves. A head whose reference moved has its accumulators rescaled before the value
-//    MFMAs of that tile, on a path outside the loop, so that inside it accumulators are only ever
-//    touched by MFMAs.
+//    One barrier per tile. Iteration j: the score waves run the MFMAs of S(j+1) with the softmax
+//    of tile j (its scores held in registers since the previous iteration) interleaved between
+//    them, so that the matrix pipe of each SIMD works on the scores while its vector ALU works on
+//    the exponentials; the value waves run the MFMAs of tile j-1 against P(j-1), read tile j's V^T
+//    into registers and issue the loads of tile j+3 into the stage tile j-1 held (so three tiles
+//    are in flight). P and the rescale factors are double-buffered by tile parity. A head block
+//    with a rescale factor other than 1 (its reference moved) has its accumulators rescaled before
+//    the value MFMAs of that tile, outside the MFMA chain.
 //    P^T comes out of the S^T accumulators with lane l holding tokens 4(l/16)+{0..3} and
 //    16+4(l/16)+{0..3} of head l%16 -- its k-group of the P.V product -- and V^T is read in the
 //    same token order.
@@ -358,9 +359,8 @@ struct AttendCtx {
   float* part_l;
   uint8_t* ring;
   uint8_t* pbuf;
-  uint8_t* xbuf;
   float (*alpha_s)[kBlockHeads];
-  int (*flag_s)[4];
+  float* l_s;
   int wave, lane;
 };
 
@@ -408,16 +408,17 @@ struct SegmentWalk {
 // score waves' critical path -- scores, then softmax -- must not stall behind the load queue):
 // value wave v fills latent rows v + 4k (k < 8) -- physical chunk `lane` holds logical chunk
 // lane ^ fk(row) -- and the rotary rows 8v .. 8v+7 (physical chunk lane%8 of row 8v + lane/8 holds
-// logical chunk (lane%8) ^ fp(row)). The descriptors start at the tile's first row and end at the
-// segment's last row; kv_voff[k] is the byte offset of lane's chunk of row v + 4k.
+// logical chunk (lane%8) ^ fp(row)). The descriptors start at the tile's first row and cover its
+// rows up to the segment's last (none for a tile past the segment: it loads zeros and reads no
+// memory); kv_voff[k] is the byte offset of lane's chunk of row v + 4k.
 __device__ __forceinline__ void issue_tile(const AttendCtx& c, const Segment& sg, int t, const uint32_t* kv_voff,
                                            uint32_t pe_voff) {
   const int v = c.wave & 3;
-  const uint32_t rows_left = static_cast<uint32_t>(sg.n_rows - t * kTileTok);
-  const __amdgpu_buffer_rsrc_t rk =
-      make_rsrc(sg.kv_seg + static_cast<int64_t>(t) * kTileTok * kKvLora, rows_left * 1024u);
-  const __amdgpu_buffer_rsrc_t rp =
-      make_rsrc(sg.pe_seg + static_cast<int64_t>(t) * kTileTok * kRope, rows_left * 128u);
+  const int left = sg.n_rows - t * kTileTok;
+  const uint32_t rows = static_cast<uint32_t>(left <= 0 ? 0 : (left < kTileTok ? left : kTileTok));
+  const int64_t row0 = left <= 0 ? 0 : static_cast<int64_t>(t) * kTileTok;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(sg.kv_seg + row0 * kKvLora, rows * 1024u);
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(sg.pe_seg + row0 * kRope, rows * 128u);
   const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)c.ring)) +
                        (t % kStages) * kTileBytes;
 #pragma unroll
@@ -468,30 +469,28 @@ __device__ __forceinline__ void issue_tile_gather(const AttendCtx& c, const Segm
   dma16(rp, dst + kKvBytes + v * 1024, ppos * 128u + pe_chunk);
 }
 
-// Score waves 0-3. Wave w = (kh, hh) = (w & 1, w >> 1) holds the query of the 32 heads of half hh
-// over k half kh -- latent k-steps [8 kh, 8 kh + 8) and rotary k-step 16 + kh -- and computes the
-// partial S^T of those heads for all 32 tokens of a tile (each tile operand it reads feeds two
-// MFMAs). Partners w and w^1 then swap the partials of each other's 16 heads through LDS, so that
-// wave w ends with the full S^T of heads 16w .. 16w+15, runs their softmax and writes P to LDS.
+// Score waves 0-3. Wave w holds the query of heads 16w .. 16w+15 (absorbed latent part, 16
+// k-steps, and rotary part, 2 k-steps; B operands, k-group grp of head 16 w + r per lane) and
+// computes S^T[t][h] for all 32 tokens of a tile over the full 576 features (A operand: ds_read_b128
+// of tile rows). Iteration j (one barrier each) runs the MFMAs of tile j+1 and, interleaved with
+// them, the softmax of tile j, whose scores the previous iteration left in registers: per head a
+// reference m (log2 units, scale folded in) that moves only when a tile's maximum exceeds it by
+// more than 8, so that p = 2^(s - m) <= 2^8; P goes to LDS as bf16 with the head's rescale factor.
 // They issue no loads: a tile is complete once the value waves, which wait for their own loads of
 // it, reach the next barrier.
 __device__ __forceinline__ void score_role(const AttendCtx& c) {
   const int w = c.wave, lane = c.lane, r = lane & 15, grp = lane >> 4;
-  const int kh = w & 1, hh = w >> 1, partner = w ^ 1;
   // LDS byte offsets. Latent k-step ks = 4a + k: row 16 tb + r, logical chunk 4 ks + grp at
   // physical 16 a + 4 (k ^ (fk>>2)) + (grp ^ (fk&3)); a and tb go into immediates. Rotary k-step
-  // 16 + kh: row 16 tb + r, chunk 4 kh + grp at (4 kh + grp) ^ fp(r).
+  // 16 + e: row 16 tb + r, chunk 4 e + grp at (4 e + grp) ^ fp(r).
   const int sf = fk(r);
   int s_off[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) s_off[k] = r * 1024 + 64 * (k ^ (sf >> 2)) + 16 * (grp ^ (sf & 3));
-  const int e_off = kKvBytes + r * 128 + 16 * ((4 * kh + grp) ^ fp(r));
+  int e_off[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) e_off[e] = kKvBytes + r * 128 + 16 * ((4 * e + grp) ^ fp(r));
   const int p_wr = (grp * kBlockHeads + w * 16 + r) * 16;
-  // Partial exchange: token half 0 through xbuf[receiver][lane]; token half 1 through the P buffer
-  // of the tile (idle until the softmax), at the receiver's own P slots: only the receiver writes
-  // there afterwards, and only after reading.
-  const int x_send0 = partner * 1024 + lane * 16, x_recv0 = w * 1024 + lane * 16;
-  const int x_send1 = (grp * kBlockHeads + partner * 16 + r) * 16;
   const int head = c.head0 + w * 16 + r;
   const bool real = head < c.n_heads;
 
@@ -499,135 +498,102 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
   Segment sg;
   while (walk.next(c, sg)) {
     const int n_tiles = sg.n_tiles;
-    // B operands: qf[hb][j] = head 32 hh + 16 hb + r, k-group grp of k-step 8 kh + j (j < 8) or of
-    // rotary k-step 16 + kh (j = 8).
-    bf16x8 qf[2][9];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int hd = c.head0 + hh * 32 + hb * 16 + r;
-      const bool rl = hd < c.n_heads;
-      const int hq = rl ? hd : 0;
-      const uint16_t* ql = c.q_lat + (static_cast<int64_t>(sg.b) * c.n_heads + hq) * kKvLora + kh * 256 + grp * 8;
-      const uint16_t* qp = c.q + (static_cast<int64_t>(sg.b) * c.n_heads + hq) * kQk + kNope + kh * 32 + grp * 8;
+    bf16x8 qf[18];
+    {
+      const int hq = real ? head : 0;
+      const uint16_t* ql = c.q_lat + (static_cast<int64_t>(sg.b) * c.n_heads + hq) * kKvLora + grp * 8;
+      const uint16_t* qp = c.q + (static_cast<int64_t>(sg.b) * c.n_heads + hq) * kQk + kNope + grp * 8;
       const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qf[hb][j] = as_bf16x8(rl ? ldg16(ql + j * 32) : z);
-      qf[hb][8] = as_bf16x8(rl ? ldg16(qp) : z);
+      for (int j = 0; j < 16; ++j) qf[j] = as_bf16x8(real ? ldg16(ql + j * 32) : z);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) qf[16 + e] = as_bf16x8(real ? ldg16(qp + e * 32) : z);
     }
-
-    f32x4 acc[2][2];   // partial S^T [token half tb][head block hb]
-    f32x4 s[2];        // full S^T of this wave's heads, token halves 0 and 1
-    auto scores = [&](int t) {
+    // S^T of tile t: acc[tb] holds tokens 16 tb + 4 grp + {0..3} of head 16 w + r.
+    auto scores = [&](int t, f32x4 (&acc)[2]) {
       const uint8_t* tile = c.ring + (t % kStages) * kTileBytes;
-      auto rd = [&](int tb, int j) {
-        const int ks = 8 * kh + j;
-        return j < 8 ? lds_b128(tile + tb * 16384 + (ks >> 2) * 256 + s_off[ks & 3])
-                     : lds_b128(tile + tb * 2048 + e_off);
+      auto rd = [&](int tb, int ks) {
+        return ks < 16 ? lds_b128(tile + tb * 16384 + (ks >> 2) * 256 + s_off[ks & 3])
+                       : lds_b128(tile + tb * 2048 + e_off[ks - 16]);
       };
+      // four accumulator chains (token half x k-step parity), summed at the end
+      f32x4 a2[2][2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) a2[tb][0] = a2[tb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        a2[0][ks & 1] = mfma16x16x32(rd(0, ks), qf[ks], a2[0][ks & 1]);
+        a2[1][ks & 1] = mfma16x16x32(rd(1, ks), qf[ks], a2[1][ks & 1]);
+      }
+      acc[0] = a2[0][0] + a2[0][1];
+      acc[1] = a2[1][0] + a2[1][1];
+    };
+    float m_ref = -INFINITY, lsum = 0.f;   // of head 16 w + r, log2 units; lsum over this lane's tokens
+    // Softmax of tile t from its scores, without branches; rows at or past the segment end count as
+    // -inf. The rescale factor is exactly 1 unless the reference moved (the first tile of a segment
+    // always moves it, from -inf).
+    auto softmax = [&](int t, const f32x4 (&s)[2]) {
+      const int valid = sg.n_rows - t * kTileTok - 4 * grp;
+      float x[8];
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) acc[tb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      constexpr int kAhead = 9;   // every operand is read up front
-      bf16x8 fa[kAhead][2];
-#pragma unroll
-      for (int j = 0; j < kAhead; ++j) {
-        fa[j][0] = rd(0, j);
-        fa[j][1] = rd(1, j);
-      }
-#pragma unroll
-      for (int j = 0; j < 9; ++j) {
-        const bf16x8 a0 = fa[j % kAhead][0], a1 = fa[j % kAhead][1];
-        if (j + kAhead < 9) {
-          fa[j % kAhead][0] = rd(0, j + kAhead);
-          fa[j % kAhead][1] = rd(1, j + kAhead);
-        }
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          acc[0][hb] = mfma16x16x32(a0, qf[hb][j], acc[0][hb]);
-          acc[1][hb] = mfma16x16x32(a1, qf[hb][j], acc[1][hb]);
-        }
-      }
-    };
-    auto send = [&](int par) {
-      const f32x4 v0 = kh ? acc[0][0] : acc[0][1];
-      const f32x4 v1 = kh ? acc[1][0] : acc[1][1];
-      *reinterpret_cast<f32x4*>(c.xbuf + x_send0) = v0;
-      *reinterpret_cast<f32x4*>(c.pbuf + par * kPBytes + x_send1) = v1;
-    };
-    // Full scores of tile t (after the exchange barrier); rows at or past the segment end -inf.
-    auto receive = [&](int t, int par) {
-      const f32x4 u0 = *reinterpret_cast<const f32x4*>(c.xbuf + x_recv0);
-      const f32x4 u1 = *reinterpret_cast<const f32x4*>(c.pbuf + par * kPBytes + p_wr);
-      s[0] = (kh ? acc[0][1] : acc[0][0]) + u0;
-      s[1] = (kh ? acc[1][1] : acc[1][0]) + u1;
-      const int valid = sg.n_rows - t * kTileTok - 4 * grp;
-      if (sg.n_rows - t * kTileTok < kTileTok) {
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (tb * 16 + j >= valid) s[tb][j] = -INFINITY;
-      }
-    };
-    auto tile_max = [&]() {
-      const float m = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                            fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-      return max_over_rows(m) * c.scale_log2;
-    };
-    float m_ref, lsum = 0.f;   // of head 16 w + r, log2 units; lsum over this lane's tokens
-    auto write_p = [&](int par) {
+        for (int j = 0; j < 4; ++j) x[tb * 4 + j] = tb * 16 + j < valid ? s[tb][j] : -INFINITY;
+      const float m = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      const float mx = max_over_rows(m) * c.scale_log2;
+      const bool up = mx > m_ref + 8.f;
+      const float m_new = up ? mx : m_ref;
+      const float alpha = fast_exp2(m_ref - m_new);
+      m_ref = m_new;
       float p[8];
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(x[i] * c.scale_log2 - m_ref);
+      lsum = lsum * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+      *reinterpret_cast<bf16x8*>(c.pbuf + (t & 1) * kPBytes + p_wr) = bf16x8_from_f32(p);
+      c.alpha_s[t & 1][w * 16 + r] = alpha;
+    };
+    // Iteration j: the scores of tile j+1 (of a stale stage past the last tile: computed, never
+    // used) and the softmax of tile j in one basic block, so that the softmax's vector instructions
+    // can fill the gaps between MFMAs: eight operand reads go out first, then each pair of MFMAs
+    // is followed by the next two reads.
+    auto step = [&](int j, const f32x4 (&cur)[2], f32x4 (&next)[2]) {
+      lds_barrier();   // tile j+1 landed; P(j-1) consumed by the value waves
+      scores(j + 1, next);
+      softmax(j, cur);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) p[tb * 4 + j] = fast_exp2(s[tb][j] * c.scale_log2 - m_ref);
-      lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      *reinterpret_cast<bf16x8*>(c.pbuf + par * kPBytes + p_wr) = bf16x8_from_f32(p);
+      for (int i = 0; i < 14; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     };
 
-    // Tile 0: its maximum is the first reference; no rescale for it.
+    f32x4 sa[2], sb[2];
     lds_barrier();   // tile 0 landed
-    scores(0);
-    send(0);
-    lds_barrier();   // partials of tile 0 exchanged
-    receive(0, 0);
-    m_ref = tile_max();
-    write_p(0);
-    c.flag_s[0][w] = 0;
-    for (int it = 0; it < n_tiles; ++it) {
-      lds_barrier();   // tile it+1 landed, P(it) published
-      // phase A: the scores of tile it+1 own the MFMA pipes (the value waves issue loads)
-      if (it + 1 < n_tiles) {
-        scores(it + 1);
-        send((it + 1) & 1);
-      }
-      lds_barrier();
-      // phase B: the softmax of tile it+1 beside the value MFMAs of tile it
-      if (it + 1 < n_tiles) {
-        receive(it + 1, (it + 1) & 1);
-        const float mx = tile_max();
-        const bool up = mx > m_ref + 8.f;
-        const float m_new = up ? mx : m_ref;
-        const float alpha = fast_exp2(m_ref - m_new);
-        m_ref = m_new;
-        lsum *= alpha;
-        write_p((it + 1) & 1);
-        c.alpha_s[(it + 1) & 1][w * 16 + r] = alpha;
-        c.flag_s[(it + 1) & 1][w] = __any(up) ? 1 : 0;
-      }
+    scores(0, sa);
+    // unrolled by two so that the scores of consecutive tiles alternate between sa and sb
+    for (int j = 0; j < n_tiles; j += 2) {
+      step(j, sa, sb);
+      if (j + 1 < n_tiles) step(j + 1, sb, sa);
     }
-    // Final normalisation: publish l of every head through alpha_s.
+    lds_barrier();   // P of the last tile published
     const float ltot = sum_over_rows(lsum);
-    lds_barrier();
-    c.alpha_s[0][w * 16 + r] = ltot;
-    if (grp == 0 && real) c.part_l[(c.g + sg.b) * c.n_heads + head] = (m_ref + __log2f(ltot)) * kLn2;
-    lds_barrier();
-    lds_barrier();   // alpha_s, P and the ring are reused by the next segment
+    if (grp == 0) {
+      c.l_s[w * 16 + r] = ltot;
+      if (real) c.part_l[(c.g + sg.b) * c.n_heads + head] = (m_ref + __log2f(ltot)) * kLn2;
+    }
+    lds_barrier();   // l published
   }
 }
 
-// Value waves 4-7: O^T += V^T P^T for latent columns [128 w, 128 w + 128) of all 64 heads.
+// Value waves 4-7: O^T += V^T P^T for latent columns [128 w, 128 w + 128) of all 64 heads, one
+// tile behind the score waves. Iteration j: P^T and the rescale factors of tile j-1 from LDS (a
+// head block whose reference moved has its accumulators scaled first, outside the MFMA chain),
+// then, in one basic block, the MFMAs of tile j-1 (V^T from registers, read in the previous
+// iteration) with the loads of tile j+3 (into the stage tile j-1 held; in dense mode also past the
+// segment's end, as zero-length loads, so that the block has no branch) and the transposing reads
+// of tile j's V^T placed between them.
 template <bool kGather>
 __device__ __forceinline__ void value_role(const AttendCtx& c) {
   constexpr int L = 9;   // loads per tile
@@ -662,68 +628,100 @@ __device__ __forceinline__ void value_role(const AttendCtx& c) {
   while (walk.next(c, sg)) {
     const int n_tiles = sg.n_tiles;
     int issued = 0;
-    if (kGather) load_tile_pos(c, sg, 0, pos);
-    while (issued < kStages && issued < n_tiles) issue(sg, issued++);
+    if (kGather) {
+      load_tile_pos(c, sg, 0, pos);
+      while (issued < kStages && issued < n_tiles) issue(sg, issued++);
+    } else {
+#pragma unroll
+      for (int t = 0; t < kStages; ++t) issue(sg, issued++);
+    }
 
     f32x4 o[8][4];   // O^T[16 (8 w + cb) + 4 grp + j][16 hb + r]
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) o[cb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // O^T += V^T P^T for tile t, in two steps: read_values (phase A: P^T, V^T and the rescale flags
-    // of tile t into registers, beside the score waves' LDS reads) and values (phase B: a head whose
-    // reference moved at tile t has its accumulators -- tiles < t -- scaled, then the MFMAs).
-    bf16x8 pf[4], vf[8];
-    int4 fl;
-    auto read_values = [&](int t) {
+    auto read_v = [&](int t, bf16x8 (&vf)[8]) {
       const uint8_t* tile = c.ring + (t % kStages) * kTileBytes;
-      const uint8_t* pb = c.pbuf + (t & 1) * kPBytes + p_rd;
-      fl = *reinterpret_cast<const int4*>(&c.flag_s[t & 1][0]);
-#pragma unroll
-      for (int hb = 0; hb < 4; ++hb) pf[hb] = lds_b128(pb + hb * 256);
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb) vf[cb] = lds_vt(tile + v_off[cb]);
     };
-    auto values = [&](int t) {
-      if ((fl.x | fl.y | fl.z | fl.w) != 0) {
+    // P^T of tile t and its rescale factors; then the accumulators of heads whose reference moved
+    // scaled (those of tile 0 are still zero)
+    auto read_p = [&](int t, bf16x8 (&pf)[4], float (&a)[4]) {
+      const uint8_t* pb = c.pbuf + (t & 1) * kPBytes + p_rd;
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) {
-          const float a = c.alpha_s[t & 1][hb * 16 + r];
+      for (int hb = 0; hb < 4; ++hb) {
+        pf[hb] = lds_b128(pb + hb * 256);
+        a[hb] = c.alpha_s[t & 1][hb * 16 + r];
+      }
+    };
+    auto rescale = [&](int t, const float (&a)[4]) {
 #pragma unroll
-          for (int cb = 0; cb < 8; ++cb) o[cb][hb] *= a;
+      for (int hb = 0; hb < 4; ++hb) {
+        if (t > 0 && __any(a[hb] != 1.f)) {
+#pragma unroll
+          for (int cb = 0; cb < 8; ++cb) o[cb][hb] *= a[hb];
         }
       }
+    };
+    auto mfmas = [&](const bf16x8 (&vf)[8], const bf16x8 (&pf)[4]) {
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) o[cb][hb] = mfma16x16x32(vf[cb], pf[hb], o[cb][hb]);
     };
+    // Iteration 1 <= j <= n_tiles: tile j+1 landed, barrier (for j = n_tiles: P of the last tile
+    // published), values of tile j-1, the V^T of tile j and the loads of tile j+3 (for j = n_tiles
+    // a stale stage is read and, in dense mode, zero-length loads go out: neither is used).
+    auto step = [&](int j, const bf16x8 (&prev)[8], bf16x8 (&cur)[8]) {
+      if (j + 1 < n_tiles) wait_tiles<L>(issued - 2 - j);
+      lds_barrier();
+      bf16x8 pf[4];
+      float a[4];
+      read_p(j - 1, pf, a);
+      if (kGather) {
+        rescale(j - 1, a);
+        mfmas(prev, pf);
+        read_v(j, cur);
+        // the operand reads are complete before the next tile's position loads go out, so that
+        // the waits for later LDS reads do not include those scalar loads
+        __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+        if (issued < n_tiles && issued <= j + 3) issue(sg, issued++);
+      } else {
+        // the loads go out while P^T is read (the MFMAs may run beside them), then two MFMAs per
+        // transposing read
+        issue(sg, issued++);
+        rescale(j - 1, a);
+        mfmas(prev, pf);
+        read_v(j, cur);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 14; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+    };
 
+    bf16x8 va[8], vb[8];
     wait_tiles<L>(issued - 1);
     lds_barrier();   // tile 0 landed
-    lds_barrier();   // partials of tile 0 exchanged
-    for (int it = 0; it < n_tiles; ++it) {
-      // tile it+1 landed, P(it) published, the stage of tile it-1 free for tile it+3
-      if (it + 1 < n_tiles) wait_tiles<L>(issued - 2 - it);
-      lds_barrier();
-      // phase A: operand reads, then loads (bound by the load unit), while the score waves'
-      // MFMAs own the pipes
-      read_values(it);
-      // top-k mode: the operand reads are complete before the next tile's position loads go out,
-      // so that the waits for later LDS reads do not include those scalar loads
-      if (kGather) __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
-      if (issued < n_tiles && issued <= it + 3) issue(sg, issued++);
-      lds_barrier();
-      // phase B: the value MFMAs of tile it beside the softmax of tile it+1
-      values(it);
+    if (n_tiles > 1) wait_tiles<L>(issued - 2);
+    lds_barrier();   // tile 1 landed
+    read_v(0, va);
+    // unrolled by two so that the V^T of consecutive tiles alternates between va and vb
+    for (int j = 1; j <= n_tiles; j += 2) {
+      step(j, va, vb);
+      if (j + 1 <= n_tiles) step(j + 1, vb, va);
     }
-    lds_barrier();
-    lds_barrier();
+    lds_barrier();   // l published
     const int64_t slot = c.g + sg.b;
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
       if (c.head0 + hb * 16 < c.n_heads) {
-        const float inv = 1.f / c.alpha_s[0][hb * 16 + r];
+        const float inv = 1.f / c.l_s[hb * 16 + r];
         float* po = c.part_o + (slot * c.n_heads + c.head0 + hb * 16 + r) * kKvLora + w * 128 + grp * 4;
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) {
@@ -732,7 +730,6 @@ __device__ __forceinline__ void value_role(const AttendCtx& c) {
         }
       }
     }
-    lds_barrier();   // alpha_s, P and the ring are reused by the next segment
   }
 }
 
@@ -755,9 +752,8 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(
 
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages * kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t pbuf[2 * kPBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t xbuf[4 * 1024];
   __shared__ float alpha_s[2][kBlockHeads];
-  __shared__ __attribute__((aligned(16))) int flag_s[2][4];
+  __shared__ float l_s[kBlockHeads];
 
   AttendCtx c;
   c.q_lat = q_lat; c.q = q; c.kv = kv; c.pe = pe; c.row_offset = row_offset; c.max_seqlen = max_seqlen;
@@ -765,7 +761,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(
   c.cum = cum; c.runs = runs; c.batch = batch; c.n_heads = n_heads; c.head0 = hg * kBlockHeads;
   c.g = g; c.start = run_start(g, N, G); c.end = run_start(g + 1, N, G);
   c.scale_log2 = scale_log2; c.part_o = part_o; c.part_l = part_l;
-  c.ring = ring; c.pbuf = pbuf; c.xbuf = xbuf; c.alpha_s = alpha_s; c.flag_s = flag_s;
+  c.ring = ring; c.pbuf = pbuf; c.alpha_s = alpha_s; c.l_s = l_s;
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: wave-derived values live in SGPRs
   c.lane = threadIdx.x & 63;
   if (c.wave < 4) score_role(c);
