@@ -630,10 +630,10 @@ __device__ __forceinline__ void value_role(const AttendCtx& c) {
     int issued = 0;
     if (kGather) {
       load_tile_pos(c, sg, 0, pos);
-      while (issued < kStages && issued < n_tiles) issue(sg, issued++);
+      while (issued < 2 && issued < n_tiles) issue(sg, issued++);
     } else {
-#pragma unroll
-      for (int t = 0; t < kStages; ++t) issue(sg, issued++);
+      issue(sg, issued++);
+      issue(sg, issued++);
     }
 
     f32x4 o[8][4];   // O^T[16 (8 w + cb) + 4 grp + j][16 hb + r]
@@ -708,6 +708,14 @@ __device__ __forceinline__ void value_role(const AttendCtx& c) {
     bf16x8 va[8], vb[8];
     wait_tiles<L>(issued - 1);
     lds_barrier();   // tile 0 landed
+    // tiles 2 and 3 only now: at a launch every block asks for its first tiles at once, and the
+    // first tile lands sooner when fewer are queued behind it
+    if (kGather) {
+      while (issued < kStages && issued < n_tiles) issue(sg, issued++);
+    } else {
+      issue(sg, issued++);
+      issue(sg, issued++);
+    }
     if (n_tiles > 1) wait_tiles<L>(issued - 2);
     lds_barrier();   // tile 1 landed
     read_v(0, va);
