@@ -913,9 +913,9 @@ DecodeLayout decode_layout(int n_heads, int batch, int64_t max_seqlen, int topk)
   // not fill the chip, so that a short cache is not read by a few blocks one tile after another.
   // Shorter runs mean more partials (H x 2 KB each) for the merge to read: a block's time grows
   // with its run (about 0.9 us per tile of 32 tokens) and the merge's with the number of runs
-  // (H x 2 KB each at about 5 TB/s), which balance near 0.12 sqrt(tokens x H) tokens per run.
+  // (H x 2 KB each at about 5 TB/s), which balance near 0.085 sqrt(tokens x H) tokens per run.
   int64_t run_tokens = (upper + max_units - 1) / max_units;
-  const int64_t balance = static_cast<int64_t>(0.12 * std::sqrt(static_cast<double>(upper) * n_heads));
+  const int64_t balance = static_cast<int64_t>(0.085 * std::sqrt(static_cast<double>(upper) * n_heads));
   run_tokens = run_tokens > balance ? run_tokens : balance;
   run_tokens = (run_tokens + 31) / 32 * 32;
   run_tokens = run_tokens < kMinRunTokens ? kMinRunTokens : (run_tokens > 256 ? 256 : run_tokens);
