@@ -11,8 +11,8 @@
 //   2. attend        split-KV attention: the tokens of all sequences, back to back, are cut into
 //                    equal runs; a workgroup streams its run's kv/pe rows through LDS 32 at a
 //                    time, computes S^T = [kv|pe] . [q_lat|q_pe]^T and O^T += kv^T . P^T on MFMA
-//                    with an fp32 online softmax, and writes one normalised partial (o, lse) per
-//                    sequence it touches.
+//                    with an fp32 online softmax, and writes one normalised partial per sequence
+//                    it touches: o as fp16 with a power-of-two factor per 128 columns, and lse.
 //   3. combine_proj  log-sum-exp merge of the partials of each (sequence, head) -> o_lat (bf16, LDS)
 //                    and lse, then out = bf16(o_lat . W_UV^T) per head (MFMA).
 #include "mla_common.hpp"
@@ -355,7 +355,8 @@ struct AttendCtx {
   int batch, n_heads, head0;
   int64_t g, start, end;
   float scale_log2;
-  float* part_o;
+  uint16_t* part_o;
+  float* part_s;
   float* part_l;
   uint8_t* ring;
   uint8_t* pbuf;
@@ -725,17 +726,32 @@ __device__ __forceinline__ void value_role(const AttendCtx& c) {
       if (j + 1 <= n_tiles) step(j + 1, vb, va);
     }
     lds_barrier();   // l published
+    // The normalised partial of each head, as fp16 times a power of two that brings the largest
+    // magnitude among this wave's 128 columns into [2^14, 2^15); the inverse factor goes to part_s.
     const int64_t slot = c.g + sg.b;
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
+      const float inv = 1.f / c.l_s[hb * 16 + r];
+      float m = 0.f;
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) {
+        o[cb][hb] *= inv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(o[cb][hb][j]));
+      }
+      m = max_over_rows(m);   // over the head's four lane groups
+      int e = static_cast<int>((__float_as_uint(m) >> 23) & 0xff) - 127;
+      e = e < -110 ? -110 : (e > 127 ? 127 : e);
+      const float sc = __uint_as_float(static_cast<uint32_t>(127 + 14 - e) << 23);
       if (c.head0 + hb * 16 < c.n_heads) {
-        const float inv = 1.f / c.l_s[hb * 16 + r];
-        float* po = c.part_o + (slot * c.n_heads + c.head0 + hb * 16 + r) * kKvLora + w * 128 + grp * 4;
+        const int64_t row = slot * c.n_heads + c.head0 + hb * 16 + r;
+        uint16_t* po = c.part_o + row * kKvLora + w * 128 + grp * 4;
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) {
-          const f32x4 v = o[cb][hb] * inv;
-          *reinterpret_cast<float4*>(po + cb * 16) = make_float4(v[0], v[1], v[2], v[3]);
+          const f32x4 v = o[cb][hb] * sc;
+          *reinterpret_cast<uint2*>(po + cb * 16) = make_uint2(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]));
         }
+        if (grp == 0) c.part_s[row * 4 + w] = __uint_as_float(static_cast<uint32_t>(127 - 14 + e) << 23);
       }
     }
   }
@@ -747,7 +763,8 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(
     const uint16_t* __restrict__ pe, const int64_t* __restrict__ row_offset, int64_t max_seqlen,
     const int32_t* __restrict__ list, int list_pitch,
     const Plan* __restrict__ plan, const int64_t* __restrict__ cum, const RunStart* __restrict__ runs, int batch,
-    int n_heads, float scale_log2, float* __restrict__ part_o, float* __restrict__ part_l) {
+    int n_heads, float scale_log2, uint16_t* __restrict__ part_o, float* __restrict__ part_s,
+    float* __restrict__ part_l) {
   // The blocks of the head groups of one run share blockIdx mod 8 -- the same XCD and its L2 --
   // and are dispatched next to each other, so the tiles one of them pulls from HBM are L2 hits for
   // the others.
@@ -768,7 +785,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(
   c.list = kGather ? list : nullptr; c.list_pitch = list_pitch;
   c.cum = cum; c.runs = runs; c.batch = batch; c.n_heads = n_heads; c.head0 = hg * kBlockHeads;
   c.g = g; c.start = run_start(g, N, G); c.end = run_start(g + 1, N, G);
-  c.scale_log2 = scale_log2; c.part_o = part_o; c.part_l = part_l;
+  c.scale_log2 = scale_log2; c.part_o = part_o; c.part_s = part_s; c.part_l = part_l;
   c.ring = ring; c.pbuf = pbuf; c.alpha_s = alpha_s; c.l_s = l_s;
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: wave-derived values live in SGPRs
   c.lane = threadIdx.x & 63;
@@ -785,9 +802,10 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(
 //    W_UV[h,d,c]) on MFMA (A: o_lat rows from LDS; B: W_UV rows 16 w .. 16 w + 15 for wave w, from
 //    VGPRs). A sequence with no rows gets out = 0, lse = -inf.
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(512) void combine_proj_kernel(
+__global__ __launch_bounds__(512, 4) void combine_proj_kernel(
     const Plan* __restrict__ plan, const int64_t* __restrict__ cum, int batch, int n_heads,
-    const float* __restrict__ part_o, const float* __restrict__ part_l, const uint16_t* __restrict__ wkv_b,
+    const uint16_t* __restrict__ part_o, const float* __restrict__ part_s, const float* __restrict__ part_l,
+    const uint16_t* __restrict__ wkv_b,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
   // one buffer for the parts' partial merges (fp32 [16][512]) and, after them, the bf16 o_lat tile
   __shared__ __attribute__((aligned(16))) float4 mbuf[16 * kKvLora / 4];
@@ -826,14 +844,20 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
           const int64_t slot = g + b;
           const float w = __expf(part_l[slot * n_heads + h] - M);
           wsum += w;
-          const float4* src = reinterpret_cast<const float4*>(part_o + (slot * n_heads + h) * kKvLora + c0);
+          // fp16 partial times the inverse of its power-of-two factor (columns c0.. lie in the
+          // 128-column slice c0 / 128 of one attention wave)
+          const float ws = w * part_s[(slot * n_heads + h) * 4 + (c0 >> 7)];
+          const uint4* src = reinterpret_cast<const uint4*>(part_o + (slot * n_heads + h) * kKvLora + c0);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float4 v = src[i];
-            acc[4 * i + 0] += w * v.x;
-            acc[4 * i + 1] += w * v.y;
-            acc[4 * i + 2] += w * v.z;
-            acc[4 * i + 3] += w * v.w;
+          for (int i = 0; i < 2; ++i) {
+            const uint4 v = src[i];
+            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const f32x2 f = unpack_f16x2(u[k]);
+              acc[8 * i + 2 * k] += ws * f[0];
+              acc[8 * i + 2 * k + 1] += ws * f[1];
+            }
           }
         }
       }
@@ -911,9 +935,9 @@ DecodeLayout decode_layout(int n_heads, int batch, int64_t max_seqlen, int topk)
   const int64_t max_units = 256 / ((n_heads + 63) / 64);
   // Runs of 256 tokens or more; shorter (whole tiles, down to kMinRunTokens) when the runs would
   // not fill the chip, so that a short cache is not read by a few blocks one tile after another.
-  // Shorter runs mean more partials (H x 2 KB each) for the merge to read: a block's time grows
+  // Shorter runs mean more partials (H x 1 KB each) for the merge to read: a block's time grows
   // with its run (about 0.9 us per tile of 32 tokens) and the merge's with the number of runs
-  // (H x 2 KB each at about 5 TB/s), which balance near 0.085 sqrt(tokens x H) tokens per run.
+  // (H x 1 KB each at about 5 TB/s), which balance near 0.085 sqrt(tokens x H) tokens per run.
   int64_t run_tokens = (upper + max_units - 1) / max_units;
   const int64_t balance = static_cast<int64_t>(0.085 * std::sqrt(static_cast<double>(upper) * n_heads));
   run_tokens = run_tokens > balance ? run_tokens : balance;
@@ -930,7 +954,8 @@ DecodeLayout decode_layout(int n_heads, int batch, int64_t max_seqlen, int topk)
   L.cum_off = off;    off = align_up(off + (B + 1) * sizeof(int64_t));
   L.runs_off = off;   off = align_up(off + static_cast<size_t>(L.units) * sizeof(RunStart));
   L.qlat_off = off;   off = align_up(off + B * H * kKvLora * sizeof(uint16_t));
-  L.part_o_off = off; off = align_up(off + slots * H * kKvLora * sizeof(float));
+  L.part_o_off = off; off = align_up(off + slots * H * kKvLora * sizeof(uint16_t));
+  L.part_s_off = off; off = align_up(off + slots * H * 4 * sizeof(float));
   L.part_l_off = off; off = align_up(off + slots * H * sizeof(float));
   L.list_off = L.count_off = 0;
   if (topk >= 0) {
@@ -953,7 +978,8 @@ hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16
   int64_t* cum = reinterpret_cast<int64_t*>(ws + lay.cum_off);
   RunStart* runs = reinterpret_cast<RunStart*>(ws + lay.runs_off);
   uint16_t* q_lat = reinterpret_cast<uint16_t*>(ws + lay.qlat_off);
-  float* part_o = reinterpret_cast<float*>(ws + lay.part_o_off);
+  uint16_t* part_o = reinterpret_cast<uint16_t*>(ws + lay.part_o_off);
+  float* part_s = reinterpret_cast<float*>(ws + lay.part_s_off);
   float* part_l = reinterpret_cast<float*>(ws + lay.part_l_off);
   const float scale_log2 = scale * kLog2e;
 
@@ -973,10 +999,10 @@ hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16
     const int blocks = (lay.units + 7) / 8 * 8 * n_groups;
     if (sparse)
       attend_kernel<true><<<blocks, 512, 0, stream>>>(q_lat, q, kv_cache, pe_cache, row_offset, max_seqlen, list, topk,
-                                                      plan, cum, runs, batch, n_heads, scale_log2, part_o, part_l);
+                                                      plan, cum, runs, batch, n_heads, scale_log2, part_o, part_s, part_l);
     else
       attend_kernel<false><<<blocks, 512, 0, stream>>>(q_lat, q, kv_cache, pe_cache, row_offset, max_seqlen, nullptr,
-                                                       0, plan, cum, runs, batch, n_heads, scale_log2, part_o, part_l);
+                                                       0, plan, cum, runs, batch, n_heads, scale_log2, part_o, part_s, part_l);
   }
   mark(ev, 2, stream);
   {
@@ -984,7 +1010,7 @@ hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16
     // groups as that leaves to it
     const int groups = (batch + 15) / 16, per_head = kMergeBlocks / n_heads;
     combine_proj_kernel<<<dim3(n_heads, groups < per_head ? groups : per_head), 512, 0, stream>>>(
-        plan, cum, batch, n_heads, part_o, part_l, wkv_b, out, lse);
+        plan, cum, batch, n_heads, part_o, part_s, part_l, wkv_b, out, lse);
   }
   mark(ev, 3, stream);
   return hipGetLastError();

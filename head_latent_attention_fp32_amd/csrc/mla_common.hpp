@@ -77,6 +77,10 @@ __device__ __forceinline__ f32x4 mfma16x16x32_f16(f16x8 a, f16x8 b, f32x4 c) {
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), f16x2));
 }
+// One packed f16 pair -> two fp32 (exact).
+__device__ __forceinline__ f32x2 unpack_f16x2(uint32_t u) {
+  return __builtin_convertvector(__builtin_bit_cast(f16x2, u), f32x2);
+}
 
 __device__ __forceinline__ f16x8 f16x8_from_f32(const float* v) {
   uint4 u;
