@@ -45,28 +45,88 @@ struct RunStart {
 __device__ __forceinline__ int64_t run_of(int64_t x, int64_t N, int64_t G) { return ((x + 1) * G - 1) / N; }
 
 // ---------------------------------------------------------------------------------------------
-// 1. q_lat[b,h,c] = bf16(sum_d q[b,h,d] W_UK[h,d,c]); block (h, 64-column slice of c).
-//    W_UK[h] rows are stored with c contiguous, so the slice is transposed into LDS ([c][d]) to
-//    give the MFMA B operand eight consecutive d per lane. Block (0, 8) builds the plan.
+// 1. q_lat[b,h,c] = bf16(sum_d q[b,h,d] W_UK[h,d,c]); block (h, 1 + 64-column slice of c).
+//    W_UK[h] rows are stored with c contiguous; the slice goes to LDS as it is and the transposing
+//    LDS read gives the MFMA B operand eight consecutive d per lane. Block (0, 0), dispatched
+//    first, builds the plan.
 // ---------------------------------------------------------------------------------------------
+constexpr int kWrPitch = 64 * 2 + 16;   // bytes per W_UK row of a 64-column slice in LDS
+
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+
 __global__ __launch_bounds__(256) void absorb_plan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ wkv_b, int batch, int n_heads,
     uint16_t* __restrict__ q_lat, const int32_t* __restrict__ seqlens, int64_t max_seqlen,
     int units, int min_unit_tokens, Plan* __restrict__ plan, int64_t* __restrict__ cum,
     const int64_t* __restrict__ row_offset, int64_t cache_rows_per_seq, RunStart* __restrict__ runs) {
   const int tid = threadIdx.x;
-  const int h = blockIdx.x;
-  const int c0 = blockIdx.y * 64;
+  const int lane = tid & 63, wave = tid >> 6;
 
-  __shared__ uint16_t wt[64][kNope + 8];
+  __shared__ __attribute__((aligned(16))) uint8_t wr[kNope * kWrPitch];
   __shared__ int64_t scan[256];
+  __shared__ int64_t rowb_s[256];
+  __shared__ int64_t wsum_s[4];
   __shared__ int64_t total_runs[2];
 
-  if (blockIdx.y == kKvLora / 64) {
+  if (blockIdx.y == 0) {
     // the plan, in a block of its own beside the absorb blocks
     if (blockIdx.x != 0) return;
-    // cum[b] = sum_{b' < b} clamp(L_b', 0, max_seqlen); each thread owns a contiguous chunk.
     const int per = (batch + 255) / 256;
+    if (per == 1) {
+      // One sequence per thread: its clamped length and first cache row are loaded together, the
+      // inclusive prefix sums taken within each wave by shuffles and across the four waves
+      // through LDS (cum[b] = sum_{b' < b} clamp(L_b', 0, max_seqlen)).
+      int64_t len = 0, rb = 0;
+      if (tid < batch) {
+        len = min<int64_t>(max<int64_t>(seqlens[tid], 0), max_seqlen);
+        rb = row_offset ? row_offset[tid] : static_cast<int64_t>(tid) * cache_rows_per_seq;
+      }
+      rowb_s[tid] = rb;
+      int64_t v = len;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int64_t t = __shfl_up(v, off, 64);
+        if (lane >= off) v += t;
+      }
+      if (lane == 63) wsum_s[wave] = v;
+      __syncthreads();
+      for (int w2 = 0; w2 < wave; ++w2) v += wsum_s[w2];
+      scan[tid] = v;
+      if (tid < batch) cum[tid] = v - len;
+      if (tid == 255) {
+        const int64_t N = v;
+        cum[batch] = N;
+        int64_t G = (N + min_unit_tokens - 1) / min_unit_tokens;
+        G = min<int64_t>(G, units);
+        plan->total_tokens = N;
+        plan->runs = static_cast<int32_t>(N > 0 ? max<int64_t>(G, 1) : 0);
+        plan->pad = 0;
+        total_runs[0] = N;
+        total_runs[1] = N > 0 ? max<int64_t>(G, 1) : 0;
+      }
+      __syncthreads();   // prefix sums, first rows and the run count are known
+      // thread i writes runs i, i + 256, ...: run g starts in the first sequence b whose inclusive
+      // prefix sum exceeds run_start(g)
+      const int64_t N = total_runs[0], G = total_runs[1];
+      for (int64_t g = tid; g < G; g += 256) {
+        const int64_t x = run_start(g, N, G);
+        int lo_b = 0, hi_b = batch - 1;
+        while (lo_b < hi_b) {
+          const int mid = (lo_b + hi_b) >> 1;
+          if (scan[mid] > x) hi_b = mid;
+          else lo_b = mid + 1;
+        }
+        const int b = lo_b;
+        RunStart rs;
+        rs.b = b;
+        rs.t0 = static_cast<int32_t>(x - (b > 0 ? scan[b - 1] : 0));
+        rs.next = scan[b];
+        rs.row_base = rowb_s[b];
+        runs[g] = rs;
+      }
+      return;
+    }
+    // More than 256 sequences: each thread owns a contiguous chunk of them.
     const int b0 = min(batch, tid * per), b1 = min(batch, b0 + per);
     int64_t s = 0;
     for (int b = b0; b < b1; ++b) s += min<int64_t>(max<int64_t>(seqlens[b], 0), max_seqlen);
@@ -101,27 +161,7 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
     // run_start(g) = floor(g N / G) is stepped from run to run (quotient and remainder of N / G)
     // rather than divided out per record.
     const int64_t N = total_runs[0], G = total_runs[1];
-    if (G > 0 && per == 1) {
-      // at most one sequence per thread: thread i writes runs i, i + 256, ...; run g starts in the
-      // first sequence b whose inclusive prefix sum scan[b] exceeds run_start(g)
-      for (int64_t g = tid; g < G; g += 256) {
-        const int64_t q = run_start(g, N, G);
-        int lo_b = 0, hi_b = batch - 1;
-        while (lo_b < hi_b) {
-          const int mid = (lo_b + hi_b) >> 1;
-          if (scan[mid] > q) hi_b = mid;
-          else lo_b = mid + 1;
-        }
-        const int b = lo_b;
-        const int64_t first = b > 0 ? scan[b - 1] : 0;
-        RunStart rs;
-        rs.b = b;
-        rs.t0 = static_cast<int32_t>(q - first);
-        rs.next = scan[b];
-        rs.row_base = row_offset ? row_offset[b] : static_cast<int64_t>(b) * cache_rows_per_seq;
-        runs[g] = rs;
-      }
-    } else if (G > 0) {
+    if (G > 0) {
       const int64_t qN = N / G, rN = N % G;
       int64_t lo = chunk0;
       for (int b = b0; b < b1; ++b) {
@@ -129,19 +169,19 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
         const int64_t row_base = row_offset ? row_offset[b] : static_cast<int64_t>(b) * cache_rows_per_seq;
         int64_t g = (lo * G + N - 1) / N;           // first run starting at or after lo
         if (g < G && hi > lo) {
-          int64_t q = g * N / G, rem = g * N - q * G;   // q = run_start(g)
-          while (g < G && q < hi) {                    // runs starting in [lo, hi)
+          int64_t x = g * N / G, rem = g * N - x * G;   // x = run_start(g)
+          while (g < G && x < hi) {                    // runs starting in [lo, hi)
             RunStart rs;
             rs.b = b;
-            rs.t0 = static_cast<int32_t>(q - lo);
+            rs.t0 = static_cast<int32_t>(x - lo);
             rs.next = hi;
             rs.row_base = row_base;
             runs[g] = rs;
             ++g;
-            q += qN;
+            x += qN;
             rem += rN;
             if (rem >= G) {
-              ++q;
+              ++x;
               rem -= G;
             }
           }
@@ -152,47 +192,61 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
     return;
   }
 
-  const int lane = tid & 63, wave = tid >> 6;
+  // Block (h, 1 + slice): columns 64 slice .. +63 for every query. The queries go in groups of
+  // 16, loaded two groups ahead of their products; the first two before the weight slice.
+  const int h = blockIdx.x;
+  const int c0 = (blockIdx.y - 1) * 64;
   const int r = lane & 15, grp = lane >> 4;
-  // the first 16 queries' content part, loaded ahead of the weight slice
-  uint4 qa[4];
-  {
-    const uint16_t* qrow = q + (static_cast<int64_t>(min(r, batch - 1)) * n_heads + h) * kQk;
+  constexpr int kAhead = 2;
+  uint4 qa[kAhead][4];
+  auto load_q = [&](int b0, uint4 (&dst)[4]) {
+    const uint16_t* qrow = q + (static_cast<int64_t>(min(b0 + r, batch - 1)) * n_heads + h) * kQk;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qa[ks] = ldg16(qrow + ks * 32 + grp * 8);
-  }
+    for (int ks = 0; ks < 4; ++ks) dst[ks] = ldg16(qrow + ks * 32 + grp * 8);
+  };
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i)
+    if (16 * i < batch) load_q(16 * i, qa[i]);
 
-  // Transposed W_UK[h][0:128][c0:c0+64] -> wt[c][d].
+  // W_UK[h][0:128][c0:c0+64], row-major in LDS (rows kWrPitch bytes apart)
   const uint16_t* wk = wkv_b + static_cast<int64_t>(h) * kKvRows * kKvLora + c0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int idx = tid + 256 * i;
     const int d = idx >> 3, ch = idx & 7;
-    const uint4 v = ldg16(wk + static_cast<int64_t>(d) * kKvLora + ch * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) wt[ch * 8 + e][d] = u4_elem(v, e);
+    *reinterpret_cast<uint4*>(wr + d * kWrPitch + ch * 16) = ldg16(wk + static_cast<int64_t>(d) * kKvLora + ch * 8);
   }
   __syncthreads();
 
+  // B operand of k-step ks: column c = 16 wave + r, rows d = 32 ks + 8 grp .. +7, by two
+  // transposing reads (rows +0..3 and +4..7 of the 16-column block)
   bf16x8 bw[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    bw[ks] = *reinterpret_cast<const bf16x8*>(&wt[wave * 16 + r][ks * 32 + grp * 8]);
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint8_t* p = wr + (32 * ks + 8 * grp + (r >> 2)) * kWrPitch + (16 * wave + 4 * (r & 3)) * 2;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p + 4 * kWrPitch));
+    bw[ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
 
-  for (int b0 = 0; b0 < batch; b0 += 16) {
-    const int b = b0 + r;
+  // q_lat^T = W_UK^T q^T for 16 columns x 16 queries: lane (r, grp) ends with columns
+  // 16 wave + 4 grp .. +3 of query b0 + r, stored as one 8-byte write
+  auto product = [&](int b0, const uint4 (&a)[4]) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const uint16_t* qrow = q + (static_cast<int64_t>(min(b, batch - 1)) * n_heads + h) * kQk;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 a = as_bf16x8(b0 == 0 ? qa[ks] : ldg16(qrow + ks * 32 + grp * 8));
-      acc = mfma16x16x32(a, bw[ks], acc);
-    }
+    for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(bw[ks], as_bf16x8(a[ks]), acc);
+    if (b0 + r < batch)
+      *reinterpret_cast<uint2*>(q_lat + (static_cast<int64_t>(b0 + r) * n_heads + h) * kKvLora + c0 + wave * 16 + grp * 4) =
+          make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+  };
+  for (int b0 = 0; b0 < batch; b0 += 16 * kAhead) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int bb = b0 + grp * 4 + j;
-      if (bb < batch)
-        q_lat[(static_cast<int64_t>(bb) * n_heads + h) * kKvLora + c0 + wave * 16 + r] = f32_to_bf16_bits(acc[j]);
+    for (int i = 0; i < kAhead; ++i) {
+      const int b = b0 + 16 * i;
+      if (b < batch) {
+        product(b, qa[i]);
+        if (b + 16 * kAhead < batch) load_q(b + 16 * kAhead, qa[i]);
+      }
     }
   }
 }
@@ -305,7 +359,6 @@ __device__ __forceinline__ void wait_tiles(int tiles_after) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((ext_vector_type(4))) short i16x4;
 
 // Raw buffer descriptor over [base, base + bytes) built from wave-uniform values (so that it
 // lives in SGPRs); loads beyond the range return zeros.
@@ -990,7 +1043,7 @@ hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16
   mark(ev, 0, stream);
   if (sparse) topk_compact_kernel<<<batch, 256, 0, stream>>>(topk_indices, topk, seqlens, max_seqlen, list, counts);
   // the run plan covers the attended rows: L_b per sequence, or the count of its top-k positions
-  absorb_plan_kernel<<<dim3(n_heads, kKvLora / 64 + 1), 256, 0, stream>>>(
+  absorb_plan_kernel<<<dim3(n_heads, 1 + kKvLora / 64), 256, 0, stream>>>(
       q, wkv_b, batch, n_heads, q_lat, sparse ? counts : seqlens, sparse ? topk : max_seqlen, lay.units,
       lay.min_unit_tokens, plan, cum, row_offset, max_seqlen, runs);
   mark(ev, 1, stream);
