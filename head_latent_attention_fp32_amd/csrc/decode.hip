@@ -570,50 +570,76 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
         return ks < 16 ? lds_b128(tile + tb * 16384 + (ks >> 2) * 256 + s_off[ks & 3])
                        : lds_b128(tile + tb * 2048 + e_off[ks - 16]);
       };
-      // four accumulator chains (token half x k-step parity), summed at the end
-      f32x4 a2[2][2];
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) a2[tb][0] = a2[tb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
-        a2[0][ks & 1] = mfma16x16x32(rd(0, ks), qf[ks], a2[0][ks & 1]);
-        a2[1][ks & 1] = mfma16x16x32(rd(1, ks), qf[ks], a2[1][ks & 1]);
+        acc[0] = mfma16x16x32(rd(0, ks), qf[ks], acc[0]);
+        acc[1] = mfma16x16x32(rd(1, ks), qf[ks], acc[1]);
       }
-      acc[0] = a2[0][0] + a2[0][1];
-      acc[1] = a2[1][0] + a2[1][1];
     };
     float m_ref = -INFINITY, lsum = 0.f;   // of head 16 w + r, log2 units; lsum over this lane's tokens
-    // Softmax of tile t from its scores, without branches; rows at or past the segment end count as
-    // -inf. The rescale factor is exactly 1 unless the reference moved (the first tile of a segment
-    // always moves it, from -inf).
-    auto softmax = [&](int t, const f32x4 (&s)[2]) {
+    // Softmax of tile t from its scores, in two parts. The common part assumes the reference stays
+    // (rescale factor exactly 1): P = 2^(s - m) and the sums, with no cross-lane step, and reports
+    // whether any of the lane's scores exceeds the reference by more than 8. If one does anywhere
+    // in the wave (rare after the first tile of a segment, which always moves the reference from
+    // -inf), the full part, on a branch of its own, takes each head's maximum, moves the references
+    // that must move and redoes P, the sums and the factors. kMask: rows at or past the segment
+    // end count as -inf (only the last tile of a segment can have such rows).
+    float lsum_prev = 0.f;
+    bool above = false;
+    auto softmax_common = [&](int t, const f32x4 (&s)[2], bool mask) {
       const int valid = sg.n_rows - t * kTileTok - 4 * grp;
-      float x[8];
+      const float thr = m_ref + 8.f;
+      float p[8], y[8];
+      float ymax = -INFINITY;
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) x[tb * 4 + j] = tb * 16 + j < valid ? s[tb][j] : -INFINITY;
-      const float m = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      const float mx = max_over_rows(m) * c.scale_log2;
+        for (int j = 0; j < 4; ++j) {
+          const float v = s[tb][j] * c.scale_log2;
+          y[tb * 4 + j] = (!mask || tb * 16 + j < valid) ? v : -INFINITY;
+        }
+      ymax = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])), fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(y[i] - m_ref);
+      lsum_prev = lsum;
+      lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      *reinterpret_cast<bf16x8*>(c.pbuf + (t & 1) * kPBytes + p_wr) = bf16x8_from_f32(p);
+      c.alpha_s[t & 1][w * 16 + r] = 1.f;
+      above = ymax > thr;
+    };
+    auto softmax_full = [&](int t, const f32x4 (&s)[2], bool mask) {
+      const int valid = sg.n_rows - t * kTileTok - 4 * grp;
+      float y[8];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float v = s[tb][j] * c.scale_log2;
+          y[tb * 4 + j] = (!mask || tb * 16 + j < valid) ? v : -INFINITY;
+        }
+      const float m = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])), fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+      const float mx = max_over_rows(m);
       const bool up = mx > m_ref + 8.f;
       const float m_new = up ? mx : m_ref;
       const float alpha = fast_exp2(m_ref - m_new);
       m_ref = m_new;
       float p[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(x[i] * c.scale_log2 - m_ref);
-      lsum = lsum * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(y[i] - m_ref);
+      lsum = lsum_prev * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
       *reinterpret_cast<bf16x8*>(c.pbuf + (t & 1) * kPBytes + p_wr) = bf16x8_from_f32(p);
       c.alpha_s[t & 1][w * 16 + r] = alpha;
     };
     // Iteration j: the scores of tile j+1 (of a stale stage past the last tile: computed, never
-    // used) and the softmax of tile j in one basic block, so that the softmax's vector instructions
-    // can fill the gaps between MFMAs: eight operand reads go out first, then each pair of MFMAs
-    // is followed by the next two reads.
-    auto step = [&](int j, const f32x4 (&cur)[2], f32x4 (&next)[2]) {
+    // used) and the common softmax part of tile j in one basic block, so that the softmax's vector
+    // instructions can fill the gaps between MFMAs: eight operand reads go out first, then each
+    // pair of MFMAs is followed by the next two reads.
+    auto step = [&](int j, const f32x4 (&cur)[2], f32x4 (&next)[2], bool mask) {
       lds_barrier();   // tile j+1 landed; P(j-1) consumed by the value waves
       scores(j + 1, next);
-      softmax(j, cur);
+      softmax_common(j, cur, mask);
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
       for (int i = 0; i < 14; ++i) {
@@ -621,15 +647,24 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      if (__any(above)) softmax_full(j, cur, mask);
     };
 
     f32x4 sa[2], sb[2];
     lds_barrier();   // tile 0 landed
     scores(0, sa);
-    // unrolled by two so that the scores of consecutive tiles alternate between sa and sb
-    for (int j = 0; j < n_tiles; j += 2) {
-      step(j, sa, sb);
-      if (j + 1 < n_tiles) step(j + 1, sb, sa);
+    // Unrolled by two so that the scores of consecutive tiles alternate between sa and sb; the
+    // last tile of the segment takes the masked softmax.
+    int j = 0;
+    for (; j + 2 < n_tiles; j += 2) {
+      step(j, sa, sb, false);
+      step(j + 1, sb, sa, false);
+    }
+    if (n_tiles - j == 2) {
+      step(j, sa, sb, false);
+      step(j + 1, sb, sa, true);
+    } else {
+      step(j, sa, sb, true);
     }
     lds_barrier();   // P of the last tile published
     const float ltot = sum_over_rows(lsum);
