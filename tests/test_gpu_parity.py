@@ -112,6 +112,25 @@ def test_decode_parity_small(H, lens, layout):
     _check_decode(case, q, d, out, lse)
 
 
+@pytest.mark.parametrize("shift", [16, -20])
+def test_decode_partials_outside_fp16_range(shift):
+    """The split partials are kept as fp16 times a power of two per 128 columns: a cache scaled by
+    2^shift, with the query's content part scaled by 2^-shift (the same scores), gives outputs
+    2^shift times larger -- for shift 16 past fp16's largest finite value, for -20 inside its
+    subnormal range -- which must still meet the bar."""
+    say(f"decode with the cache scaled by 2^{shift}")
+    case = S.DecodeCase("t", 340 + (shift > 0), 128, np.array([3000, 700, 1], np.int32), layout="packed")
+    d = S.decode_inputs(case, seed=4, with_q_latent=False)
+    q = S.decode_query(case, seed=4)
+    f = 2.0 ** shift
+    d["kv_cache"] = bits_of(O.bf16_decode(d["kv_cache"]) * f)
+    qv = O.bf16_decode(q)
+    qv[..., :128] *= 1.0 / f
+    q = bits_of(qv)
+    out, lse = _run_decode(case, q, d)
+    _check_decode(case, q, d, out, lse)
+
+
 def test_decode_lengths_are_clamped():
     say("decode clamped lengths")
     case = S.DecodeCase("t", 330, 64, np.array([40, 40, 40], np.int32), max_seqlen=40)
