@@ -893,7 +893,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(
 __global__ __launch_bounds__(512, 4) void combine_proj_kernel(
     const Plan* __restrict__ plan, const int64_t* __restrict__ cum, int batch, int n_heads,
     const uint16_t* __restrict__ part_o, const float* __restrict__ part_s, const float* __restrict__ part_l,
-    const uint16_t* __restrict__ wkv_b,
+    const uint16_t* __restrict__ wkv_b, int dsplit,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
   // one buffer for the parts' partial merges (fp32 [16][512]) and, after them, the bf16 o_lat tile
   __shared__ __attribute__((aligned(16))) float4 mbuf[16 * kKvLora / 4];
@@ -904,15 +904,22 @@ __global__ __launch_bounds__(512, 4) void combine_proj_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, grp = lane >> 4;
   const int64_t N = plan->total_tokens, G = plan->runs;
+  // blockIdx.y = group slot gy x output part dp: the block produces outputs d0 .. d0 + 128 / dsplit
+  // of its head, from the first 8 / dsplit waves
+  const int gy = blockIdx.y / dsplit, dp = blockIdx.y % dsplit, ngy = gridDim.y / dsplit;
+  const int d0 = dp * (kVDim / dsplit);
+  const bool proj = wave < 8 / dsplit;
 
-  const uint16_t* wrow = wkv_b + (static_cast<int64_t>(h) * kKvRows + kNope + wave * 16 + r) * kKvLora + grp * 8;
+  const uint16_t* wrow = wkv_b + (static_cast<int64_t>(h) * kKvRows + kNope + d0 + wave * 16 + r) * kKvLora + grp * 8;
   bf16x8 bw[16];
+  if (proj) {
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) bw[ks] = as_bf16x8(ldg16(wrow + ks * 32));
+    for (int ks = 0; ks < 16; ++ks) bw[ks] = as_bf16x8(ldg16(wrow + ks * 32));
+  }
 
   const int j = tid >> 5, c0 = (tid & 31) * 16;   // thread group j (32 threads), columns c0 .. c0 + 15
   // groups of 16 sequences b0, b0 + 16 gridDim.y, ...: W_UV stays in registers across them
-  for (int b0 = blockIdx.y * 16; b0 < batch; b0 += gridDim.y * 16) {
+  for (int b0 = gy * 16; b0 < batch; b0 += ngy * 16) {
     // With fewer than 9 sequences in the group, each sequence's runs are shared by `parts` thread
     // groups (runs part, part + parts, ...), whose partial merges are then merged through LDS.
     const int nseq = min(16, batch - b0);
@@ -952,7 +959,7 @@ __global__ __launch_bounds__(512, 4) void combine_proj_kernel(
     }
     if (parts > 1) {
       // merge of the parts: thread group (js, 0) takes the others' (M, wsum, acc) from LDS
-      if (b0 != static_cast<int>(blockIdx.y) * 16) __syncthreads();   // previous group's o_lat read
+      if (b0 != gy * 16) __syncthreads();   // previous group's o_lat read
       pm_s[j][0] = M;
       pm_s[j][1] = wsum;
 #pragma unroll
@@ -982,11 +989,11 @@ __global__ __launch_bounds__(512, 4) void combine_proj_kernel(
         M = Mt;
       }
     }
-    if (js < nseq && part == 0 && lse && (tid & 31) == 0)
+    if (js < nseq && part == 0 && lse && dp == 0 && (tid & 31) == 0)
       lse[static_cast<int64_t>(b) * n_heads + h] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
     // the parts' partials, or the previous group's o_lat, are read before o_lat is written
-    if (parts > 1 || b0 != static_cast<int>(blockIdx.y) * 16) __syncthreads();
+    if (parts > 1 || b0 != gy * 16) __syncthreads();
     if (part == 0) {
 #pragma unroll
       for (int i = 0; i < 16; i += 8) {
@@ -999,13 +1006,15 @@ __global__ __launch_bounds__(512, 4) void combine_proj_kernel(
       }
     }
     __syncthreads();
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    if (proj) {
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) o = mfma16x16x32(*reinterpret_cast<const bf16x8*>(&ol[r][ks * 32 + grp * 8]), bw[ks], o);
+      for (int ks = 0; ks < 16; ++ks) o = mfma16x16x32(*reinterpret_cast<const bf16x8*>(&ol[r][ks * 32 + grp * 8]), bw[ks], o);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int bb = b0 + grp * 4 + e;
-      if (bb < batch) out[(static_cast<int64_t>(bb) * n_heads + h) * kVDim + wave * 16 + r] = f32_to_bf16_bits(o[e]);
+      for (int e = 0; e < 4; ++e) {
+        const int bb = b0 + grp * 4 + e;
+        if (bb < batch) out[(static_cast<int64_t>(bb) * n_heads + h) * kVDim + d0 + wave * 16 + r] = f32_to_bf16_bits(o[e]);
+      }
     }
   }
 }
@@ -1094,11 +1103,14 @@ hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16
   }
   mark(ev, 2, stream);
   {
-    // at most kMergeBlocks blocks, each with its head's W_UV in registers for as many sequence
-    // groups as that leaves to it
+    // At most kMergeBlocks blocks, each with its head's W_UV in registers for as many sequence
+    // groups as that leaves to it. A single group (16 sequences or fewer, whose partials are few)
+    // is merged by up to four blocks per head, each projecting a quarter of the outputs with a
+    // quarter of W_UV, so that W_UV is read by more compute units.
     const int groups = (batch + 15) / 16, per_head = kMergeBlocks / n_heads;
-    combine_proj_kernel<<<dim3(n_heads, groups < per_head ? groups : per_head), 512, 0, stream>>>(
-        plan, cum, batch, n_heads, part_o, part_s, part_l, wkv_b, out, lse);
+    const int dsplit = groups == 1 ? (per_head >= 4 ? 4 : (per_head >= 2 ? 2 : 1)) : 1;
+    combine_proj_kernel<<<dim3(n_heads, (groups < per_head ? groups : per_head) * dsplit), 512, 0, stream>>>(
+        plan, cum, batch, n_heads, part_o, part_s, part_l, wkv_b, dsplit, out, lse);
   }
   mark(ev, 3, stream);
   return hipGetLastError();
