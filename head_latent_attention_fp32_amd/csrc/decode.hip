@@ -298,7 +298,8 @@ __global__ __launch_bounds__(256) void topk_compact_kernel(const int32_t* __rest
 //                        sum_k tile[t][k] q[h][k] on MFMA (A operand: ds_read_b128 of tile rows),
 //                        then the softmax: per head a reference m (log2 units, scale folded in)
 //                        that moves only when a tile's maximum exceeds it by more than 8, so
-//                        p = 2^(s - m) <= 2^8, written to LDS as bf16;
+//                        p = 2^(s - m) <= 2^8, written to LDS as bf16 (a common part keeps the
+//                        reference; a full part on a branch of its own moves it);
 //      value waves 4-7   wave 4+w owns latent columns [128 w, 128 w + 128) of all 64 heads and
 //                        adds O^T[c][h] += sum_t tile[t][c] P^T[t][h] (A operand:
 //                        ds_read_b64_tr_b16, the transposing LDS read, of tile columns; B operand:
