@@ -10,6 +10,7 @@ from oracle import mla_oracle as O
 import tests.test_oracle_attention as TA
 import tests.test_oracle_codec_norms as TC
 import tests.test_oracle_next as TN
+import tests.test_oracle_tolerance as TT
 
 MUTANTS = {
     "rope_sign": ("ra = a * c - b * s", "ra = a * c + b * s",
@@ -83,6 +84,20 @@ MUTANTS = {
     "wo_not_transposed": ("return _maybe_round(x @ w.T, staged)",
                           "return _maybe_round(x @ w.reshape(w.shape[1], w.shape[0]), staged)",
                           [(TN, "test_output_proj_width_flatten_order_and_library")]),
+    "decode_magnitude_scale_dropped": ("return scale * np.max(np.abs(q_lat) @ c.T", "return np.max(np.abs(q_lat) @ c.T",
+                                       [(TT, "test_decode_magnitude_hand_case"),
+                                        (TT, "test_decode_magnitude_scaling_sign_and_zero_query")]),
+    "decode_magnitude_signed_terms": ("np.max(np.abs(q_lat) @ c.T + np.abs(q[:, NOPE:]) @ pe.T, axis=1)",
+                                      "np.max(q_lat @ c.T + q[:, NOPE:] @ pe.T, axis=1)",
+                                      [(TT, "test_decode_magnitude_hand_case"),
+                                       (TT, "test_decode_magnitude_scaling_sign_and_zero_query")]),
+    "prefill_magnitude_scale_dropped": ("mag[j, i] = scale * np.max(", "mag[j, i] = np.max(",
+                                        [(TT, "test_prefill_magnitude_hand_case_and_causal_range"),
+                                         (TT, "test_prefill_magnitude_scaling_sign_future_rows_and_zero_query")]),
+    "prefill_magnitude_sees_next_key": ("np.max(k[: off + r + 1] @ np.abs(q[r, h]))",
+                                        "np.max(k[: off + r + 2] @ np.abs(q[r, h]))",
+                                        [(TT, "test_prefill_magnitude_hand_case_and_causal_range"),
+                                         (TT, "test_prefill_magnitude_scaling_sign_future_rows_and_zero_query")]),
 }
 
 
