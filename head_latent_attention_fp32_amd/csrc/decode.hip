@@ -52,8 +52,6 @@ __device__ __forceinline__ int64_t run_of(int64_t x, int64_t N, int64_t G) { ret
 // ---------------------------------------------------------------------------------------------
 constexpr int kWrPitch = 64 * 2 + 16;   // bytes per W_UK row of a 64-column slice in LDS
 
-typedef __attribute__((ext_vector_type(4))) short i16x4;
-
 __global__ __launch_bounds__(256) void absorb_plan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ wkv_b, int batch, int n_heads,
     uint16_t* __restrict__ q_lat, const int32_t* __restrict__ seqlens, int64_t max_seqlen,
@@ -330,24 +328,9 @@ constexpr int kTileBytes = kKvBytes + kPeBytes;            // 36864
 constexpr int kStages = 4;                                 // tiles in the LDS ring
 constexpr int kBlockHeads = 64;                            // heads of one workgroup
 constexpr int kPBytes = kTileTok / 8 * kBlockHeads * 16;   // one P buffer
-constexpr uint32_t kRsrcWord3 = 0x00020000u;               // raw buffer, 32-bit data format
 
 __device__ __forceinline__ int fk(int row) { return 2 * (row & 7); }
 __device__ __forceinline__ int fp(int row) { return (row >> 1) & 7; }
-
-// Workgroup barrier that orders LDS accesses only. __syncthreads() also orders global memory,
-// which waits for every vector-memory load in flight -- here, the next tiles' loads.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  // s_waitcnt vmcnt(N); expcnt and lgkmcnt left unconstrained
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // Wait until at most `tiles_after` tiles of this wave's loads (L per tile) are still in flight
 // (one tile is the steady state of the loops).
@@ -357,30 +340,6 @@ __device__ __forceinline__ void wait_tiles(int tiles_after) {
   else if (tiles_after >= 3) wait_vm<3 * L>();
   else if (tiles_after == 2) wait_vm<2 * L>();
   else wait_vm<0>();
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Raw buffer descriptor over [base, base + bytes) built from wave-uniform values (so that it
-// lives in SGPRs); loads beyond the range return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
-  void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)),
-                                           kRsrcWord3);
-}
-
-// 16-byte direct-to-LDS buffer load: lane l's 16 bytes at rsrc + voff land at LDS byte address
-// lds_addr + 16 l. Issued from an asm block: the compiler cannot tell which ring stage such a load
-// writes and would otherwise wait for every load in flight before any LDS read. Completion is
-// tracked with explicit vmcnt waits and barriers. The block writes no registers.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr, uint32_t voff) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
-               : "memory");
 }
 
 __device__ __forceinline__ bf16x8 lds_b128(const uint8_t* p) { return *reinterpret_cast<const bf16x8*>(p); }

@@ -27,27 +27,6 @@ constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kStageBytes = (kBM + kBN) * kBK * 2;              // 64 KB
 constexpr int kIssuers = 4;                                     // waves 0-3 issue the loads
 constexpr int kLoadsPerWave = kStageBytes / 1024 / kIssuers;    // 16 loads of 1 KB per issuing wave and step
-constexpr uint32_t kRsrcWord3 = 0x00020000u;                    // raw buffer, 32-bit data format
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
-  void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)),
-                                           kRsrcWord3);
-}
-
-// 16-byte direct-to-LDS buffer load (lane l's bytes land at lds_addr + 16 l); completion is tracked
-// with an explicit vmcnt wait. The asm block writes no registers.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t voff) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(r), "{m0}"(lds_addr)
-               : "memory");
-}
-
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 // One block tile: features [n0, n0 + 256) of W (w_rows rows in all), tokens [m0, m0 + 256) of X
@@ -78,13 +57,18 @@ __device__ __forceinline__ void nt_tile(const uint16_t* __restrict__ w, int64_t 
     const int row = 8 * (d & 31) + (lane >> 3);
     voff[e] = static_cast<uint32_t>(row * K * 2 + (((lane & 7) ^ swz(row)) << 4));
   }
-  const uint32_t st_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void_t*)stage));
+  const uint32_t st_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)stage));
+  // Descriptor ranges: the rows this tile reads (at most 256 of each operand; rows past an operand's
+  // end read as zeros), so that the 32-bit byte ranges stay below 4 GiB for any operand size
+  // (256 rows x K x 2 B; K <= 16384 here).
   const int64_t w_left = w_rows - n0, x_left = x_rows - m0;
+  const uint32_t w_bytes = static_cast<uint32_t>((w_left < kBN ? w_left : kBN) * K * 2);
+  const uint32_t x_bytes = static_cast<uint32_t>((x_left < kBM ? x_left : kBM) * K * 2);
   auto issue = [&](int kt) {
     if (!issuer) return;
     // descriptors rebuilt per step (scalar work): short-lived, they stay in SGPRs
-    const __amdgpu_buffer_rsrc_t rw = rsrc(w + static_cast<int64_t>(n0) * K, static_cast<uint32_t>(w_left * K * 2));
-    const __amdgpu_buffer_rsrc_t rx = rsrc(x + m0 * K, static_cast<uint32_t>(x_left * K * 2));
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + static_cast<int64_t>(n0) * K, w_bytes);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + m0 * K, x_bytes);
     const uint32_t koff = static_cast<uint32_t>(k_begin + kt * kBK) * 2u;
     const uint32_t dst = st_lds + (kt & 1) * kStageBytes;
 #pragma unroll

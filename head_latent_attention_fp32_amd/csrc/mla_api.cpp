@@ -33,6 +33,17 @@ constexpr int64_t kMaxTokens = int64_t(65535) * 128;
 constexpr int64_t kMaxOutElems = (int64_t(1) << 31) - 1;
 // The longest top-k list of one sequence (a list of one sequence's positions).
 constexpr int32_t kMaxTopk = 1 << 21;
+// Prefill: at most 2^23 key positions over the batch (batch x kv_len), so that the expansion's and
+// the attention's grids fit their 32-bit block counts with room to spare, and every workspace index
+// stays far inside int64.
+constexpr int64_t kMaxPrefillTokens = int64_t(1) << 23;
+constexpr int32_t kMaxPrefillBatch = 65535;
+
+mla_status_t check_prefill_sizes(int32_t batch, int32_t q_len, int32_t kv_len) {
+  if (batch < 0 || batch > kMaxPrefillBatch || q_len < 0 || kv_len < q_len) return MLA_ERR_SHAPE;
+  if (static_cast<int64_t>(batch) * kv_len > kMaxPrefillTokens) return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
 
 }  // namespace
 
@@ -174,7 +185,7 @@ mla_status_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t batch, i
   mla_status_t st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (!bytes) return MLA_ERR_INVALID_ARG;
-  if (batch < 0 || batch > 65535 || seqlen < 0) return MLA_ERR_SHAPE;
+  if ((st = check_prefill_sizes(batch, 0, seqlen)) != MLA_OK) return st;
   *bytes = (batch == 0 || seqlen == 0) ? 0 : mla::prefill_layout(dims->n_heads, batch, seqlen).total;
   return MLA_OK;
 }
@@ -185,7 +196,7 @@ mla_status_t mla_prefill_ex(const mla_dims_t* dims, int32_t batch, int32_t seqle
                             hipEvent_t* stage_events) {
   mla_status_t st = check_dims(dims);
   if (st != MLA_OK) return st;
-  if (batch < 0 || batch > 65535 || seqlen < 0) return MLA_ERR_SHAPE;
+  if ((st = check_prefill_sizes(batch, seqlen, seqlen)) != MLA_OK) return st;
   if (batch == 0 || seqlen == 0) return MLA_OK;
   if (!q || !kv_latent || !k_pe || !wkv_b || !workspace || !out) return MLA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(kv_latent) || !aligned16(k_pe) || !aligned16(wkv_b) || !aligned16(workspace) ||
@@ -204,7 +215,7 @@ mla_status_t mla_prefill_with_prefix_ex(const mla_dims_t* dims, int32_t batch, i
                                         float* lse, hipStream_t stream, hipEvent_t* stage_events) {
   mla_status_t st = check_dims(dims);
   if (st != MLA_OK) return st;
-  if (batch < 0 || batch > 65535 || q_len < 0 || kv_len < q_len) return MLA_ERR_SHAPE;
+  if ((st = check_prefill_sizes(batch, q_len, kv_len)) != MLA_OK) return st;
   if (batch == 0 || q_len == 0) return MLA_OK;
   if (!q || !kv_latent || !k_pe || !wkv_b || !workspace || !out) return MLA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(kv_latent) || !aligned16(k_pe) || !aligned16(wkv_b) || !aligned16(workspace) ||

@@ -121,4 +121,53 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// ---------------------------------------------------------------------------------------------
+// Buffer loads straight into LDS, and the barriers around them.
+// ---------------------------------------------------------------------------------------------
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+
+// LDS byte address of a __shared__ object (the M0 operand of a direct-to-LDS load).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)p));
+}
+
+// Raw buffer descriptor over [base, base + bytes) built from wave-uniform values (so that it
+// lives in SGPRs); loads beyond the range return zeros. Callers size `bytes` to what the loads
+// that use the descriptor may reach, so that it never wraps.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)),
+                                           kRsrcWord3);
+}
+
+// 16-byte direct-to-LDS buffer load: lane l's 16 bytes at rsrc + voff land at LDS byte address
+// lds_addr + 16 l. Issued from an asm block: the compiler cannot tell which LDS stage such a load
+// writes and would otherwise wait for every load in flight before any LDS read. Completion is
+// tracked with explicit vmcnt waits and barriers. The block writes no registers.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
+}
+
+// Workgroup barrier that orders LDS accesses only. __syncthreads() also orders global memory,
+// which waits for every vector-memory load in flight -- the next stages' loads among them.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// s_waitcnt vmcnt(N); expcnt and lgkmcnt left unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 }  // namespace mla

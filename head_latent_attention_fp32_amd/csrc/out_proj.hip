@@ -27,33 +27,6 @@ namespace mla {
 
 namespace {
 
-constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
-  void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)),
-                                           kRsrcWord3);
-}
-
-// 16-byte direct-to-LDS buffer load (lane l's bytes land at lds_addr + 16 l; loads outside the
-// descriptor's range return zeros); completion is tracked with explicit vmcnt waits.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr, uint32_t voff) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
-               : "memory");
-}
-
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // ---------------------------------------------------------------------------------------------
 // Small token counts.
 // ---------------------------------------------------------------------------------------------

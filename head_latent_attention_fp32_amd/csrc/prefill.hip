@@ -142,33 +142,6 @@ constexpr int kKnBytes = kPK * kNope * 2;   // 16384
 constexpr int kKpBytes = kPK * kRope * 2;   // 8192
 constexpr int kVtBytes = kVDim * kPK * 2;   // 16384
 constexpr int kStage = kKnBytes + kKpBytes + kVtBytes;   // 40960
-constexpr uint32_t kRsrcWord3 = 0x00020000u;
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
-  void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)),
-                                           kRsrcWord3);
-}
-
-// 16-byte direct-to-LDS buffer load (lane l's bytes land at lds_addr + 16 l; loads outside the
-// descriptor's range return zeros); completion is tracked with explicit vmcnt waits.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr, uint32_t voff) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
-               : "memory");
-}
-
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 __device__ __forceinline__ bf16x8 lds_b128(const uint8_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ __forceinline__ int swz_kn(int row) { return 2 * (row & 7); }
@@ -231,10 +204,12 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
   auto issue = [&](int kt) {
     const int k0 = kt * kPK;
     const uint32_t dst = st_lds + (kt & 1) * kStage;
-    const auto rk = make_rsrc(kn + static_cast<int64_t>(k0) * kNope, static_cast<uint32_t>(t_pad - k0) * 256u);
-    const int rows_pe = kv_len - k0;
+    // each descriptor covers this tile's rows only (a whole tile of the padded k_nope and V^T; the
+    // rotary key up to the last position), so that its 32-bit byte range never wraps
+    const auto rk = make_rsrc(kn + static_cast<int64_t>(k0) * kNope, static_cast<uint32_t>(kKnBytes));
+    const int rows_pe = min(kv_len - k0, kPK);
     const auto rp = make_rsrc(pe + static_cast<int64_t>(k0) * kRope, static_cast<uint32_t>(rows_pe) * 128u);
-    const auto rv = make_rsrc(vh + static_cast<int64_t>(k0) * kVDim, static_cast<uint32_t>(kVDim * (t_pad - k0)) * 2u);
+    const auto rv = make_rsrc(vh + static_cast<int64_t>(k0) * kVDim, static_cast<uint32_t>(kVtBytes));
 #pragma unroll
     for (int e = 0; e < 4; ++e) dma16(rk, dst + (wave + 4 * e) * 1024, kn_off[e]);
 #pragma unroll

@@ -108,7 +108,6 @@ __global__ __launch_bounds__(256) void normalize_kernel(const uint16_t* __restri
 constexpr int kSmallM = 32;          // largest token count of the small kernel
 constexpr int kWaveK = kQLora / 4;   // 384
 constexpr int kSteps = kWaveK / 32;  // 12 k-steps per slice
-constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
 
 template <int NB>
 struct SmallCfg {
@@ -122,32 +121,6 @@ struct SmallCfg {
   static constexpr bool kOneSlice = NB == 8;                   // one slice per block, reduction in the ring
   static constexpr int kLdsBytes = kOneSlice ? kRingBytes : kRingBytes + kRedBytes;
 };
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((ext_vector_type(4))) short i16x4;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
-  void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)),
-                                           kRsrcWord3);
-}
-
-// 16-byte direct-to-LDS buffer load (lane l's bytes land at lds_addr + 16 l); completion is tracked
-// with explicit vmcnt waits. The asm block writes no registers.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr, uint32_t voff) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
-               : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // Slice t of XCD x's list: x, x + 8, x + 16, ...
 __device__ __forceinline__ int slice_of(int x, int t) { return x + 8 * t; }

@@ -131,7 +131,8 @@ mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, const uint16_t* q
                         hipStream_t stream);
 
 /* Bytes of device workspace mla_prefill needs (holds the expanded per-head k_nope and values).
- * Host-only; no HIP call. */
+ * Host-only; no HIP call. batch in [0, 65535] and batch * seqlen <= 2^23 key positions, else
+ * MLA_ERR_SHAPE (the same limits hold for mla_prefill and, with kv_len, mla_prefill_with_prefix). */
 mla_status_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t seqlen, size_t* bytes);
 
 /* Non-absorbed causal prefill ("Kimi-K2 · value_states", mla-prefill excerpt), start position 0:
@@ -144,7 +145,8 @@ mla_status_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t batch, i
  *   wkv_b      bf16 [n_heads*256, 512]
  *   workspace  >= mla_prefill_workspace_size bytes
  *   out        bf16 [batch, seqlen, n_heads, 128]
- *   lse        fp32 [batch, n_heads, seqlen] or NULL */
+ *   lse        fp32 [batch, n_heads, seqlen] or NULL
+ * batch > 65535 or batch * seqlen > 2^23 -> MLA_ERR_SHAPE. */
 mla_status_t mla_prefill(const mla_dims_t* dims, int32_t batch, int32_t seqlen, const uint16_t* q,
                          const uint16_t* kv_latent, const uint16_t* k_pe, const uint16_t* wkv_b,
                          void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
@@ -186,7 +188,7 @@ mla_status_t mla_decode_sparse(const mla_dims_t* dims, int32_t batch, const uint
  *   workspace  >= mla_prefill_workspace_size(dims, batch, kv_len) bytes
  *   out        bf16 [batch, q_len, n_heads, 128]
  *   lse        fp32 [batch, n_heads, q_len] or NULL
- * kv_len < q_len -> MLA_ERR_SHAPE; q_len = 0 enqueues nothing. */
+ * kv_len < q_len, batch > 65535 or batch * kv_len > 2^23 -> MLA_ERR_SHAPE; q_len = 0 enqueues nothing. */
 mla_status_t mla_prefill_with_prefix(const mla_dims_t* dims, int32_t batch, int32_t q_len, int32_t kv_len,
                                      const uint16_t* q, const uint16_t* kv_latent, const uint16_t* k_pe,
                                      const uint16_t* wkv_b, void* workspace, size_t workspace_bytes,

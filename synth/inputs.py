@@ -329,3 +329,16 @@ def topk_indices(lengths: np.ndarray, k: int, seed: int, case_id: int) -> np.nda
         if n > 0:
             out[b, :n] = _rng(seed, case_id, T_TOPK, b).choice(L, size=n, replace=False)
     return out
+
+
+def device_normal_bf16(shape, seed: int, case_id: int, tensor: int = T_Q_LATENT, std: float = 1.0):
+    """N(0, std^2) bf16 drawn directly on the GPU (torch's seeded Philox generator on cuda:0), for
+    inputs too large to draw on the host (several GB). Rows needed by a CPU check are copied back
+    from the returned tensor; the stream is keyed by (seed, case id, tensor id) like the host ones."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed((int(seed) * 1_000_003 + int(case_id)) * 101 + int(tensor))
+    x = torch.randn(tuple(shape), generator=g, device="cuda", dtype=torch.float32)
+    if std != 1.0:
+        x *= std
+    return x.to(torch.bfloat16)

@@ -140,6 +140,15 @@ def test_prefill_validation_and_workspace():
     assert pf(ctypes.byref(d), 1, 4096, FAKE, None, FAKE, FAKE, FAKE, need, FAKE, None, None) == 1
     assert pf(ctypes.byref(d), 1, 4096, FAKE, FAKE, MIS, FAKE, FAKE, need, FAKE, None, None) == 4
     assert pf(ctypes.byref(d), 1, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, need - 256, FAKE, None, None) == 5
+    # at most 2^23 key positions over the batch, at most 65535 sequences (the 32-bit grids and byte
+    # ranges of the expansion and attention stay far from wrapping)
+    big = 1 << 23
+    assert lib.mla_prefill_workspace_size(ctypes.byref(d), 1, big, ctypes.byref(n)) == 0
+    assert lib.mla_prefill_workspace_size(ctypes.byref(d), 1, big + 1, ctypes.byref(n)) == 3
+    assert lib.mla_prefill_workspace_size(ctypes.byref(d), 2, big // 2 + 1, ctypes.byref(n)) == 3
+    assert lib.mla_prefill_workspace_size(ctypes.byref(d), 65536, 1, ctypes.byref(n)) == 3
+    assert pf(ctypes.byref(d), 1, big + 1, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 62, FAKE, None, None) == 3
+    assert pf(ctypes.byref(d), 4, big // 4 + 64, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 62, FAKE, None, None) == 3
 
 
 def test_prefill_with_prefix_validation():
@@ -158,6 +167,8 @@ def test_prefill_with_prefix_validation():
     assert pf(*args(lat=None)) == 1
     assert pf(*args(lse=MIS)) == 4
     assert pf(*args(wsb=need - 1)) == 5
+    assert pf(*args(kv_len=(1 << 23) + 1, wsb=1 << 62)) == 3   # more than 2^23 key positions
+    assert pf(*args(batch=3, kv_len=(1 << 23) // 3 + 1, wsb=1 << 62)) == 3
 
 
 def test_kv_append_validation():

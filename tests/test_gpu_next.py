@@ -231,6 +231,20 @@ def test_decode_sparse_parity(H, lens, k, layout):
     _check_sparse(case, q, d, topk, out, lse, list(range(case.batch)))
 
 
+@pytest.mark.parametrize("H,B", [(16, 300), (64, 1000)])
+def test_decode_sparse_many_sequences(H, B):
+    """More than 256 sequences in top-k mode: the run plan's chunked branch over the compacted
+    counts; every 7th sequence is empty and lists are padded with -1 past the sequence."""
+    lens = [0 if i % 7 == 0 else (89 * i + 5) % 311 for i in range(B)]
+    say(f"decode_sparse H={H} B={B} k=64")
+    case = S.DecodeCase("t", 960 + H + B, H, np.array(lens, np.int32), layout="packed")
+    d = S.decode_inputs(case, seed=12, with_q_latent=False)
+    q = S.decode_query(case, seed=12)
+    topk = S.topk_indices(case.lengths, 64, seed=12, case_id=case.case_id)
+    out, lse = _run_sparse(case, q, d, topk)
+    _check_sparse(case, q, d, topk, out, lse, list(range(B)))
+
+
 def test_decode_sparse_empty_lists_and_full_lists():
     case = S.DecodeCase("t", 950, 64, np.array([0, 50, 7], np.int32), max_seqlen=50)
     d = S.decode_inputs(case, seed=10, with_q_latent=False)

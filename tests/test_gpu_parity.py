@@ -56,6 +56,33 @@ def test_query_path_parity(H, n, with_inv):
         assert_f32_parity(inv, invo, "inv_rms")
 
 
+@pytest.mark.slow
+def test_query_path_past_4gib_of_activations():
+    """16 heads over 1,398,200 tokens: the normalised activations span 4.3 GB, so one 256-token
+    tile of the product (the first) starts more than 4 GiB of activation rows before the end. Its
+    buffer descriptor covers only the rows the tile reads; were it sized to every row left, its
+    32-bit byte range would wrap and rows 99.. of the tile would read as zeros ("DeepSeek-V3.2-Exp
+    · Query heads", in/out shapes: every token's 1536 latent features become its query heads).
+    The inputs are drawn on the device (seeded) and the tile's rows, plus the last tile's, copied
+    back for the oracle."""
+    H, n = 16, 1_398_200
+    say(f"query_path H={H} n={n} (activations past 4 GiB)")
+    x = S.device_normal_bf16((n, S.Q_LORA), seed=7, case_id=250)
+    w = S.query_weights(H, 7, 250)
+    pos = np.arange(n) % 131072
+    cs = S.rope_table(pos)
+    inv = torch.empty(n, dtype=torch.float32, device="cuda")
+    q, _ = binding.query_path(x, dev(w["gamma"]), dev_bf16(w["wq_b"]), dev(cs), H, inv_rms=inv)
+    torch.cuda.synchronize()
+    rows = np.r_[0:256, n - 300:n]
+    xr = host_bits(x[torch.from_numpy(rows).cuda()])
+    qg = host_bits(q[torch.from_numpy(rows).cuda()])
+    del q, x
+    qo, invo = O.query_path(xr, w["gamma"], w["wq_b"], cs[rows], H)
+    assert_bf16_parity(qg, qo, "q_out rows of the first and last tiles")
+    assert_f32_parity(inv.cpu().numpy()[rows], invo, "inv_rms")
+
+
 # ----------------------------------------------------------------------------------- decode
 def _run_decode(case, q_bits, d, with_lse=True):
     B, H = case.batch, case.n_heads
@@ -108,6 +135,27 @@ def test_decode_parity_small(H, lens, layout):
                         max_seqlen=max(max(lens), 1))
     d = S.decode_inputs(case, seed=1, with_q_latent=False)
     q = S.decode_query(case, seed=1)
+    out, lse = _run_decode(case, q, d)
+    _check_decode(case, q, d, out, lse)
+
+
+def _many_lengths(B, mod, zero_every):
+    return [0 if i % zero_every == 0 else (97 * i + 13) % mod for i in range(B)]
+
+
+@pytest.mark.parametrize("H,B,layout", [(16, 300, "packed"), (64, 300, "padded"), (16, 1000, "padded"),
+                                        (64, 1000, "packed")])
+def test_decode_parity_many_sequences(H, B, layout):
+    """More than 256 sequences: the run plan takes its chunked branch (each plan thread owns a
+    contiguous chunk of sequences, prefix sums across the chunks, run start records stepped within
+    them). Short ragged caches with every 7th sequence empty, so that runs cross many sequence
+    boundaries and some runs start right after empty sequences ("DeepSeek-V3.2-Exp · Attention
+    update", mla-decode: each sequence attends exactly its own rows kv_cache[b, :end_pos])."""
+    lens = _many_lengths(B, 301 if B == 300 else 257, 7)
+    say(f"decode H={H} B={B} layout={layout} sum L={sum(lens)}")
+    case = S.DecodeCase("t", 360 + H + B, H, np.array(lens, np.int32), layout=layout, max_seqlen=max(lens))
+    d = S.decode_inputs(case, seed=5, with_q_latent=False)
+    q = S.decode_query(case, seed=5)
     out, lse = _run_decode(case, q, d)
     _check_decode(case, q, d, out, lse)
 
@@ -225,6 +273,32 @@ def test_prefill_parity_small(H, B, T):
         assert_bf16_parity(out[b], oo, f"out[b={b}]")
         mag = O.prefill_score_magnitude(qv, d["kv_latent"][b], d["k_pe"][b], d["wkv_b"], SCALE)
         assert_f32_parity(lse[b], lo, f"lse[b={b}]", magnitude=mag)
+
+
+@pytest.mark.slow
+def test_prefill_expansion_past_4gib_of_latent():
+    """1025 sequences of 4096 positions at 16 heads: 4,198,400 latent rows (4.3 GB). The expansion
+    tile at row 4096 (sequence 1, positions 0..255) starts exactly 4 GiB of latent rows before the
+    end, where a descriptor sized to every row left would wrap to an empty range. Sequence 1 is
+    checked on its first 256 rows and on rows near its end ("Kimi-K2 · value_states", mla-prefill:
+    kv_b_proj expands every position's latent). Inputs drawn on the device (seeded)."""
+    H, B, T = 16, 1025, 4096
+    say(f"prefill H={H} B={B} T={T} (latent past 4 GiB)")
+    w = S.kv_weights(H, 8, 451)
+    lat = S.device_normal_bf16((B, T, S.KV_LORA), seed=8, case_id=451, tensor=S.T_KV_LAT)
+    kpe = S.device_normal_bf16((B, T, S.ROPE), seed=8, case_id=451, tensor=S.T_K_PE)
+    q = S.device_normal_bf16((B, T, H, S.QK_DIM), seed=8, case_id=451, tensor=S.T_Q)
+    out, _ = binding.prefill(q, lat, kpe, dev_bf16(w))
+    torch.cuda.synchronize()
+    rows = [0, 1, 63, 64, 100, 200, 255, 256, 4000, 4095]
+    heads = [0, 9, 15]
+    b = 1
+    og = host_bits(out[b])[rows][:, heads]
+    del out
+    qb = O.bf16_decode(host_bits(q[b]))
+    latb, kpeb = host_bits(lat[b]), host_bits(kpe[b])
+    oo, _ = O.prefill_causal(qb, latb, kpeb, w, SCALE, heads=heads, rows=rows, round_output=False)
+    assert_bf16_parity(og, oo, "out of sequence 1")
 
 
 @pytest.mark.slow
