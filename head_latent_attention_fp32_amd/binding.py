@@ -63,10 +63,11 @@ def _lib():
         lib.mla_output_proj.argtypes = [dp, _I64, _I32, _P, _P, _P, _SZ, _P, _P]
         lib.mla_prefill_with_prefix.argtypes = [dp, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]
         lib.mla_kv_append.argtypes = [dp, _I32, _I32, _P, _P, _P, _P, _P, _I64, _P, _P, _P]
+        lib.mla_decode_noalloc.argtypes = [dp, _I32, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _P]
         for f in ("mla_dims_default", "mla_query_path_workspace_size", "mla_query_path", "mla_decode_workspace_size",
                   "mla_decode", "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_with_prefix",
                   "mla_kv_append", "mla_decode_sparse_workspace_size", "mla_decode_sparse",
-                  "mla_output_proj_workspace_size", "mla_output_proj"):
+                  "mla_output_proj_workspace_size", "mla_output_proj", "mla_decode_noalloc"):
             getattr(lib, f).restype = ctypes.c_int
         lib.mla_status_string.argtypes = [ctypes.c_int]
         lib.mla_status_string.restype = ctypes.c_char_p
@@ -208,6 +209,44 @@ def decode(q: torch.Tensor, wkv_b: torch.Tensor, kv_cache: torch.Tensor, pe_cach
     _check(_lib().mla_decode(ctypes.byref(d), B, _ptr(q), _ptr(wkv_b), _ptr(kv_cache), _ptr(pe_cache),
                              _ptr(cache_row_offset), _ptr(cache_seqlens), int(max_seqlen), _ptr(workspace),
                              workspace.numel(), _ptr(out), _ptr(lse), _stream()), "mla_decode")
+    return out, lse
+
+
+DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def decode_noalloc(q: torch.Tensor, wkv_b: torch.Tensor, kv_cache: torch.Tensor, pe_cache: torch.Tensor,
+                   cache_seqlens: torch.Tensor, max_seqlen: int, cache_row_offset: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   d: Optional[MlaDims] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """mla_decode_noalloc: decode as decode() does, with the library's fixed device scratch in place of
+    a workspace (at most DECODE_NOALLOC_SCRATCH_BYTES of it; larger batches raise). The library
+    allocates nothing; `out` is allocated here only when not given."""
+    _need(q, "q", torch.bfloat16)
+    if q.dim() != 3 or q.shape[2] != QK:
+        raise ValueError("q must be [B, H, 192]")
+    B, H = int(q.shape[0]), int(q.shape[1])
+    d = d or dims(H)
+    _need(wkv_b, "wkv_b", torch.bfloat16, (H * (NOPE + V_DIM), KV_LORA))
+    _need(kv_cache, "kv_cache", torch.bfloat16)
+    _need(pe_cache, "pe_cache", torch.bfloat16)
+    if kv_cache.shape[-1] != KV_LORA or pe_cache.shape[-1] != ROPE:
+        raise ValueError("kv_cache rows must be 512 wide and pe_cache rows 64 wide")
+    if kv_cache.numel() // KV_LORA != pe_cache.numel() // ROPE:
+        raise ValueError("kv_cache and pe_cache must hold the same number of rows")
+    _need(cache_seqlens, "cache_seqlens", torch.int32, (B,))
+    if cache_row_offset is not None:
+        _need(cache_row_offset, "cache_row_offset", torch.int64, (B,))
+    elif kv_cache.numel() // KV_LORA < B * max_seqlen:
+        raise ValueError("padded caches (no row offsets) need batch * max_seqlen rows")
+    if out is None:
+        out = torch.empty((B, H, V_DIM), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (B, H, V_DIM))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, H))
+    _check(_lib().mla_decode_noalloc(ctypes.byref(d), B, _ptr(q), _ptr(wkv_b), _ptr(kv_cache), _ptr(pe_cache),
+                                     _ptr(cache_row_offset), _ptr(cache_seqlens), int(max_seqlen), _ptr(out),
+                                     _ptr(lse), _stream()), "mla_decode_noalloc")
     return out, lse
 
 

@@ -15,6 +15,9 @@
 //                    it touches: o as fp16 with a power-of-two factor per 128 columns, and lse.
 //   3. combine_proj  log-sum-exp merge of the partials of each (sequence, head) -> o_lat (bf16, LDS)
 //                    and lse, then out = bf16(o_lat . W_UV^T) per head (MFMA).
+#include <atomic>
+#include <mutex>
+
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
@@ -564,8 +567,9 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) p[i] = fast_exp2(y[i] - m_ref);
       lsum_prev = lsum;
-      lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      *reinterpret_cast<bf16x8*>(c.pbuf + (t & 1) * kPBytes + p_wr) = bf16x8_from_f32(p);
+      const bf16x8 pb = bf16x8_from_f32(p);
+      lsum += sum_bf16x8(pb);   // the sum of the rounded weights the value MFMAs see
+      *reinterpret_cast<bf16x8*>(c.pbuf + (t & 1) * kPBytes + p_wr) = pb;
       c.alpha_s[t & 1][w * 16 + r] = 1.f;
       above = ymax > thr;
     };
@@ -588,8 +592,9 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
       float p[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) p[i] = fast_exp2(y[i] - m_ref);
-      lsum = lsum_prev * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
-      *reinterpret_cast<bf16x8*>(c.pbuf + (t & 1) * kPBytes + p_wr) = bf16x8_from_f32(p);
+      const bf16x8 pb = bf16x8_from_f32(p);
+      lsum = lsum_prev * alpha + sum_bf16x8(pb);
+      *reinterpret_cast<bf16x8*>(c.pbuf + (t & 1) * kPBytes + p_wr) = pb;
       c.alpha_s[t & 1][w * 16 + r] = alpha;
     };
     // Iteration j: the scores of tile j+1 (of a stale stage past the last tile: computed, never
@@ -845,21 +850,24 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(
 // 3. Merge and project out, per (head h, group of 16 sequences); a block takes every gridDim.y-th
 //    group of its head, keeping the head's W_UV in registers across them. The partials of each
 //    (sequence, h) over its runs are merged by their log-sum-exp weights (o_lat = sum_s
-//    e^(lse_s - M) o_s / sum_s e^(lse_s - M), lse = M + ln sum_s e^(lse_s - M)) into a bf16 o_lat
-//    tile in LDS (thread = sequence x 16 latent columns), then out[b,h,d] = bf16(sum_c o_lat[b,c]
-//    W_UV[h,d,c]) on MFMA (A: o_lat rows from LDS; B: W_UV rows 16 w .. 16 w + 15 for wave w, from
-//    VGPRs). A sequence with no rows gets out = 0, lse = -inf.
+//    e^(lse_s - M) o_s / sum_s e^(lse_s - M), lse = M + ln sum_s e^(lse_s - M)) into an o_lat
+//    tile in LDS (thread = sequence x 16 latent columns), kept as two bf16 tiles, the rounded
+//    value and its residual, then out[b,h,d] = bf16(sum_c o_lat[b,c] W_UV[h,d,c]) on MFMA, one
+//    product per tile into the same accumulator (A: o_lat rows from LDS; B: W_UV rows 16 w ..
+//    16 w + 15 for wave w, from VGPRs). A sequence with no rows gets out = 0, lse = -inf.
 // ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(512, 4) void combine_proj_kernel(
     const Plan* __restrict__ plan, const int64_t* __restrict__ cum, int batch, int n_heads,
     const uint16_t* __restrict__ part_o, const float* __restrict__ part_s, const float* __restrict__ part_l,
     const uint16_t* __restrict__ wkv_b, int dsplit,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
-  // one buffer for the parts' partial merges (fp32 [16][512]) and, after them, the bf16 o_lat tile
-  __shared__ __attribute__((aligned(16))) float4 mbuf[16 * kKvLora / 4];
+  // one buffer for the parts' partial merges (fp32 [16][512]) and, after them, the o_lat tile as
+  // two bf16 tiles, the rounded value and its rounding residual ([2][16][512 + 8])
+  __shared__ __attribute__((aligned(16))) float4 mbuf[2 * 16 * (kKvLora + 8) * 2 / 16];
   __shared__ float pm_s[16][2];
   float (*pa_s)[kKvLora] = reinterpret_cast<float (*)[kKvLora]>(mbuf);
   uint16_t (*ol)[kKvLora + 8] = reinterpret_cast<uint16_t (*)[kKvLora + 8]>(mbuf);
+  uint16_t (*ol_lo)[kKvLora + 8] = ol + 16;
   const int h = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, grp = lane >> 4;
@@ -955,21 +963,27 @@ __global__ __launch_bounds__(512, 4) void combine_proj_kernel(
     // the parts' partials, or the previous group's o_lat, are read before o_lat is written
     if (parts > 1 || b0 != gy * 16) __syncthreads();
     if (part == 0) {
+      // o_lat = hi + lo, both bf16: the product through W_UV sees o_lat to about 16 bits
 #pragma unroll
       for (int i = 0; i < 16; i += 8) {
-        uint4 u;
-        u.x = pack_bf16x2(acc[i + 0] * inv, acc[i + 1] * inv);
-        u.y = pack_bf16x2(acc[i + 2] * inv, acc[i + 3] * inv);
-        u.z = pack_bf16x2(acc[i + 4] * inv, acc[i + 5] * inv);
-        u.w = pack_bf16x2(acc[i + 6] * inv, acc[i + 7] * inv);
-        *reinterpret_cast<uint4*>(&ol[js][c0 + i]) = u;
+        float v[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          v[e] = acc[i + e] * inv;
+          lo[e] = v[e] - round_bf16(v[e]);
+        }
+        *reinterpret_cast<bf16x8*>(&ol[js][c0 + i]) = bf16x8_from_f32(v);
+        *reinterpret_cast<bf16x8*>(&ol_lo[js][c0 + i]) = bf16x8_from_f32(lo);
       }
     }
     __syncthreads();
     if (proj) {
       f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) o = mfma16x16x32(*reinterpret_cast<const bf16x8*>(&ol[r][ks * 32 + grp * 8]), bw[ks], o);
+      for (int ks = 0; ks < 16; ++ks) {
+        o = mfma16x16x32(*reinterpret_cast<const bf16x8*>(&ol[r][ks * 32 + grp * 8]), bw[ks], o);
+        o = mfma16x16x32(*reinterpret_cast<const bf16x8*>(&ol_lo[r][ks * 32 + grp * 8]), bw[ks], o);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int bb = b0 + grp * 4 + e;
@@ -1074,6 +1088,40 @@ hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16
   }
   mark(ev, 3, stream);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Fixed scratch for decode without a caller workspace. Every GPU the library runs on holds its own
+// copy of this array for the life of the process. In host code `scratch` names a host-side stand-in,
+// not device memory: the array's device address is looked up per device with hipGetSymbolAddress
+// (with that device current) and only that address is handed to kernels.
+// ---------------------------------------------------------------------------------------------
+namespace {
+__device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 }  // namespace mla

@@ -129,6 +129,31 @@ mla_status_t mla_decode_ex(const mla_dims_t* dims, int32_t batch, const uint16_t
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+static_assert(MLA_DECODE_NOALLOC_SCRATCH_BYTES == mla::kDecodeScratchBytes, "scratch size of mla.h and the library");
+
+mla_status_t mla_decode_noalloc(const mla_dims_t* dims, int32_t batch, const uint16_t* q, const uint16_t* wkv_b,
+                                const uint16_t* kv_cache, const uint16_t* pe_cache, const int64_t* cache_row_offset,
+                                const int32_t* cache_seqlens, int64_t max_seqlen, uint16_t* out, float* lse,
+                                hipStream_t stream) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || batch > kMaxBatch || max_seqlen < 0 || max_seqlen > kMaxSeqlen) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!q || !wkv_b || !kv_cache || !pe_cache || !cache_seqlens || !out) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(wkv_b) || !aligned16(kv_cache) || !aligned16(pe_cache) ||
+      !aligned16(cache_seqlens) || !aligned16(out) || (cache_row_offset && !aligned16(cache_row_offset)) ||
+      (lse && !aligned16(lse)))
+    return MLA_ERR_ALIGNMENT;
+  const mla::DecodeLayout lay = mla::decode_layout(dims->n_heads, batch, max_seqlen);
+  if (lay.total > mla::kDecodeScratchBytes) return MLA_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  if (mla::decode_scratch(&scratch) != hipSuccess) return MLA_ERR_HIP;
+  hipError_t e = mla::launch_decode(dims->n_heads, batch, q, wkv_b, kv_cache, pe_cache, cache_row_offset,
+                                    cache_seqlens, max_seqlen, nullptr, -1, scratch, lay, out, lse,
+                                    dims->softmax_scale, stream, nullptr);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 mla_status_t mla_decode_sparse_workspace_size(const mla_dims_t* dims, int32_t batch, int64_t max_seqlen,
                                               int32_t topk, size_t* bytes) {
   mla_status_t st = check_dims(dims);

@@ -47,6 +47,11 @@ hipError_t launch_query_path(int n_heads, int64_t n_tokens, const uint16_t* q_la
                              void* workspace, const QueryLayout& lay, float eps, hipStream_t stream,
                              hipEvent_t* ev);
 
+// Decode on a fixed device array instead of a caller workspace (for callers that cannot allocate):
+// its size, and the array's device address on the current device (looked up once per device).
+constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
+hipError_t decode_scratch(void** ptr);
+
 // topk < 0: dense decode; else top-k mode over int32 [batch, topk] positions topk_indices.
 hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16_t* wkv_b,
                          const uint16_t* kv_cache, const uint16_t* pe_cache, const int64_t* row_offset,

@@ -130,6 +130,23 @@ mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, const uint16_t* q
                         void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
                         hipStream_t stream);
 
+/* mla_decode without a workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same arguments,
+ * computation and results as mla_decode; the scratch memory mla_decode takes from `workspace`
+ * (run plan, absorbed queries, split partials) comes instead from a fixed device array of
+ * MLA_DECODE_NOALLOC_SCRATCH_BYTES inside the library, of which every GPU the library runs on holds
+ * its own copy until the process ends (its address is looked up on the first call on a device).
+ * The call allocates and frees nothing. A batch whose mla_decode_workspace_size exceeds that size
+ * returns MLA_ERR_WORKSPACE with nothing enqueued (at 128 heads: up to 128 sequences of any length
+ * up to 2^21). Every call on one GPU uses the same array and leaves its contents behind (nothing in
+ * it has to start at zero): calls that overlap on one GPU -- on different streams, or from
+ * different threads without ordering -- race and give undefined results. */
+#define MLA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+mla_status_t mla_decode_noalloc(const mla_dims_t* dims, int32_t batch, const uint16_t* q, const uint16_t* wkv_b,
+                                const uint16_t* kv_cache, const uint16_t* pe_cache, const int64_t* cache_row_offset,
+                                const int32_t* cache_seqlens, int64_t max_seqlen, uint16_t* out, float* lse,
+                                hipStream_t stream);
+
 /* Bytes of device workspace mla_prefill needs (holds the expanded per-head k_nope and values).
  * Host-only; no HIP call. batch in [0, 65535] and batch * seqlen <= 2^23 key positions, else
  * MLA_ERR_SHAPE (the same limits hold for mla_prefill and, with kv_len, mla_prefill_with_prefix). */

@@ -190,6 +190,29 @@ def test_kv_append_validation():
     assert ap(*args(dims=ctypes.byref(d2))) == 2
 
 
+def test_decode_noalloc_validation():
+    """mla_decode_noalloc validates like mla_decode and rejects, before any HIP call, a batch whose
+    scratch (mla_decode_workspace_size) exceeds the library's fixed array."""
+    lib = _lib()
+    d = _dims()
+    f = lib.mla_decode_noalloc
+    args = lambda **kw: [kw.get(k, v) for k, v in [
+        ("dims", ctypes.byref(d)), ("batch", 4096), ("q", FAKE), ("w", FAKE), ("kv", FAKE), ("pe", FAKE),
+        ("off", None), ("lens", FAKE), ("max_seqlen", 4096), ("out", FAKE), ("lse", None), ("stream", None)]]
+    n = ctypes.c_size_t(0)
+    assert lib.mla_decode_workspace_size(ctypes.byref(d), 4096, 4096, ctypes.byref(n)) == 0
+    assert n.value > binding.DECODE_NOALLOC_SCRATCH_BYTES
+    assert f(*args()) == 5                                   # scratch too small for this batch
+    assert f(*args(batch=0, q=None)) == 0                    # nothing to do
+    assert f(*args(batch=-1)) == 3
+    assert f(*args(max_seqlen=(1 << 21) + 1)) == 3
+    assert f(*args(out=None)) == 1
+    assert f(*args(lens=MIS)) == 4
+    d2 = _dims()
+    d2.n_heads = 96
+    assert f(*args(dims=ctypes.byref(d2))) == 2
+
+
 def test_decode_sparse_validation():
     lib = _lib()
     d = _dims()
