@@ -567,9 +567,8 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) p[i] = fast_exp2(y[i] - m_ref);
       lsum_prev = lsum;
-      const bf16x8 pb = bf16x8_from_f32(p);
-      lsum += sum_bf16x8(pb);   // the sum of the rounded weights the value MFMAs see
-      *reinterpret_cast<bf16x8*>(c.pbuf + (t & 1) * kPBytes + p_wr) = pb;
+      lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      *reinterpret_cast<bf16x8*>(c.pbuf + (t & 1) * kPBytes + p_wr) = bf16x8_from_f32(p);
       c.alpha_s[t & 1][w * 16 + r] = 1.f;
       above = ymax > thr;
     };
@@ -592,9 +591,8 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
       float p[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) p[i] = fast_exp2(y[i] - m_ref);
-      const bf16x8 pb = bf16x8_from_f32(p);
-      lsum = lsum_prev * alpha + sum_bf16x8(pb);
-      *reinterpret_cast<bf16x8*>(c.pbuf + (t & 1) * kPBytes + p_wr) = pb;
+      lsum = lsum_prev * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+      *reinterpret_cast<bf16x8*>(c.pbuf + (t & 1) * kPBytes + p_wr) = bf16x8_from_f32(p);
       c.alpha_s[t & 1][w * 16 + r] = alpha;
     };
     // Iteration j: the scores of tile j+1 (of a stale stage past the last tile: computed, never
@@ -632,11 +630,9 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
       step(j, sa, sb, true);
     }
     lds_barrier();   // P of the last tile published
+    // the log-sum-exp from the fp32 weights (the value waves normalise by their rounded sum)
     const float ltot = sum_over_rows(lsum);
-    if (grp == 0) {
-      c.l_s[w * 16 + r] = ltot;
-      if (real) c.part_l[(c.g + sg.b) * c.n_heads + head] = (m_ref + __log2f(ltot)) * kLn2;
-    }
+    if (grp == 0 && real) c.part_l[(c.g + sg.b) * c.n_heads + head] = (m_ref + __log2f(ltot)) * kLn2;
     lds_barrier();   // l published
   }
 }
@@ -695,6 +691,16 @@ __device__ __forceinline__ void value_role(const AttendCtx& c) {
     for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) o[cb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Running sum of the bf16 weights of heads 16 w + r (this wave's head block w) over this lane's
+    // k-group: exactly the weights the value MFMAs multiply, so that normalising by their total
+    // leaves the rounding of P no effect on the weights' sum (the log-sum-exp the score waves keep
+    // comes from the fp32 weights).
+    float lr = 0.f;
+    auto sum_mine = [&](int t) {
+      const bf16x8 pm = lds_b128(c.pbuf + (t & 1) * kPBytes + p_rd + w * 256);
+      const float am = c.alpha_s[t & 1][w * 16 + r];
+      lr = lr * am + sum_bf16x8(pm);
+    };
     auto read_v = [&](int t, bf16x8 (&vf)[8]) {
       const uint8_t* tile = c.ring + (t % kStages) * kTileBytes;
 #pragma unroll
@@ -737,6 +743,7 @@ __device__ __forceinline__ void value_role(const AttendCtx& c) {
       if (kGather) {
         rescale(j - 1, a);
         mfmas(prev, pf);
+        sum_mine(j - 1);
         read_v(j, cur);
         // the operand reads are complete before the next tile's position loads go out, so that
         // the waits for later LDS reads do not include those scalar loads
@@ -748,6 +755,7 @@ __device__ __forceinline__ void value_role(const AttendCtx& c) {
         issue(sg, issued++);
         rescale(j - 1, a);
         mfmas(prev, pf);
+        sum_mine(j - 1);
         read_v(j, cur);
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 #pragma unroll
@@ -777,6 +785,10 @@ __device__ __forceinline__ void value_role(const AttendCtx& c) {
     for (int j = 1; j <= n_tiles; j += 2) {
       step(j, va, vb);
       if (j + 1 <= n_tiles) step(j + 1, vb, va);
+    }
+    {
+      const float lt = sum_over_rows(lr);   // over the head's four k-groups
+      if (grp == 0) c.l_s[w * 16 + r] = lt;
     }
     lds_barrier();   // l published
     // The normalised partial of each head, as fp16 times a power of two that brings the largest

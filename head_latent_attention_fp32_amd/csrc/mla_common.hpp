@@ -66,8 +66,8 @@ __device__ __forceinline__ bf16x8 bf16x8_from_f32(const float* v) {
 }
 
 // Sum, in fp32, of the eight bf16 values of v (v_dot2 against ones, two chains): softmax weights
-// that enter an MFMA rounded to bf16 are normalised by the sum of exactly those rounded values, so
-// that their rounding perturbs the weights' shape but never their total.
+// that enter an MFMA rounded to bf16 can be normalised by the sum of exactly those rounded values,
+// so that their rounding perturbs the weights' shape but not their total.
 __device__ __forceinline__ float sum_bf16x8(bf16x8 v) {
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
   float s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, 0.f, false);
@@ -101,16 +101,6 @@ __device__ __forceinline__ f16x8 f16x8_from_f32(const float* v) {
   u.z = pack_f16x2(v[4], v[5]);
   u.w = pack_f16x2(v[6], v[7]);
   return __builtin_bit_cast(f16x8, u);
-}
-
-// Sum, in fp32, of the eight f16 values of v (as sum_bf16x8, for weights rounded to f16).
-__device__ __forceinline__ float sum_f16x8(f16x8 v) {
-  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-  float s0 = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 0, 1), one, 0.f, false);
-  float s1 = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 2, 3), one, 0.f, false);
-  s0 = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 4, 5), one, s0, false);
-  s1 = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 6, 7), one, s1, false);
-  return s0 + s1;
 }
 
 // Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48): the k-groups

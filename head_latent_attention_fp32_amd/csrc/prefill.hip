@@ -295,11 +295,13 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) p[kb * 4 + j] = fast_exp2(s[qh][kb][j] * scale_log2 - m_new);
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; e += 4) ps += (p[e] + p[e + 1]) + (p[e + 2] + p[e + 3]);
+      lsum[qh] = lsum[qh] * alpha[qh] + ps;
       // k-group order of the 32-key groups: keys 4 grp + j (block 2g) then 16 + 4 grp + j (block 2g+1)
       pb[qh][0] = f16x8_from_f32(p);
       pb[qh][1] = f16x8_from_f32(p + 8);
-      // the sum of the f16 weights the P.V MFMAs see
-      lsum[qh] = lsum[qh] * alpha[qh] + (sum_f16x8(pb[qh][0]) + sum_f16x8(pb[qh][1]));
     }
     if (__any(any_up)) {
 #pragma unroll
