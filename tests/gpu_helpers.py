@@ -1,10 +1,13 @@
 """Shared helpers of the GPU parity tests: host<->device transfers and the parity bars.
 
 Parity bars:
-  * bf16 outputs: max|gpu - oracle| <= 2e-2 * RMS(oracle), by default per output vector (the last
-    axis: one head's 128 outputs, one head's 192 query features, one cache row, one token's wo
-    output), against the oracle's value before its final bf16 rounding; the whole-tensor ratio is
-    printed beside it;
+  * bf16 outputs: max|err| <= 2e-2 * RMS(oracle), by default per output vector (the last axis: one
+    head's 128 outputs, one head's 192 query features, one cache row, one token's wo output),
+    against the oracle's value o before its final bf16 rounding. A bf16 output carries the rounding
+    of its own last step, which for an element several times its vector's RMS alone approaches the
+    bar, so err is how much farther the GPU's output lies from o than the correctly rounded value
+    bf16(o) does: err = |gpu - o| - |bf16(o) - o| (0 for a correctly rounded output). The plain
+    ratio max|gpu - o| / RMS and the whole-tensor ratio are printed beside it;
   * fp32 intermediates (inv_rms, lse): relative error <= 1e-4 against max(|value|, 1, magnitude),
     where `magnitude` (lse only) is the oracle's sum of the absolute terms of the score dot
     products (decode_score_magnitude / prefill_score_magnitude); the ratio against max(|value|, 1)
@@ -43,34 +46,42 @@ def bits_of(vals: np.ndarray) -> np.ndarray:
 
 
 def assert_bf16_parity(gpu_bits: np.ndarray, oracle_vals: np.ndarray, what: str, per_vector: bool = True) -> float:
-    """max|gpu - oracle| <= 2e-2 * RMS(oracle).
+    """max|err| <= 2e-2 * RMS(oracle), err = |gpu - o| - |bf16(o) - o|.
 
-    `oracle_vals` is the oracle's staged value BEFORE its final bf16 rounding: the GPU output is
-    itself the rounding of its own accumulator, and comparing two independently rounded values
-    would charge one bf16 quantum twice. With per_vector (the default) the RMS is taken over each
-    output vector -- the last axis: one head's 128 output features, or one head's 192 query
-    features -- since attention outputs of different rows have different scales (early prefill
-    rows are single values, later rows averages); the whole-tensor ratio is reported too."""
+    `oracle_vals` is the oracle's staged value o BEFORE its final bf16 rounding. The GPU output is
+    a bf16 value, so it cannot come closer to o than bf16(o), the correctly rounded value; err is
+    the distance beyond that (0 when the GPU returns bf16(o); about twice the GPU's own error before
+    its rounding when that error moves it to the other bf16 neighbour). Charging the output's own
+    rounding as well would let the bar fail on a correctly rounded exact result: an element 5 RMS
+    large rounds by up to 5 * 2^-8 = 1.95e-2 RMS. With per_vector (the default) the RMS is taken
+    over each output vector -- the last axis: one head's 128 output features, or one head's 192
+    query features -- since attention outputs of different rows have different scales (early
+    prefill rows are single values, later rows averages). The plain ratio max|gpu - o| / RMS and
+    the whole-tensor ratio are printed too."""
     g = O.bf16_decode(gpu_bits)
     o = np.asarray(oracle_vals, np.float64)
     assert g.shape == o.shape, (what, g.shape, o.shape)
     assert np.all(np.isfinite(g)), f"{what}: non-finite GPU values"
     if not o.size:
         return 0.0
-    err = np.abs(g - o)
+    plain = np.abs(g - o)
+    err = np.maximum(plain - np.abs(O.bf16_decode(O.bf16_encode(o)) - o), 0.0)
     rms_all = float(np.sqrt(np.mean(o * o)))
-    whole = float(err.max()) / max(rms_all, 1e-30)
+    whole = float(plain.max()) / max(rms_all, 1e-30)
     if per_vector:
         rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True))
         vec_err = err.max(axis=-1, keepdims=True)
         ok = (vec_err <= BF16_TOL * rms) | ((rms == 0) & (vec_err == 0))
         ratio = float(np.max(vec_err / np.maximum(rms, 1e-30)))
-        say(f"  {what}: max per-vector |err|/rms = {ratio:.3e} (whole tensor {whole:.3e})")
+        plain_ratio = float(np.max(plain.max(axis=-1, keepdims=True) / np.maximum(rms, 1e-30)))
+        say(f"  {what}: max per-vector err/rms = {ratio:.3e} (plain |gpu - oracle|/rms {plain_ratio:.3e}, "
+            f"whole tensor {whole:.3e})")
         assert ok.all(), f"{what}: {int((~ok).sum())} vectors exceed {BF16_TOL} x their RMS (worst {ratio:.3e})"
         return ratio
-    say(f"  {what}: max|err|/rms = {whole:.3e}")
-    assert whole <= BF16_TOL, f"{what}: max|err| / rms {whole} > {BF16_TOL}"
-    return whole
+    ratio = float(err.max()) / max(rms_all, 1e-30)
+    say(f"  {what}: max err/rms = {ratio:.3e} (plain {whole:.3e})")
+    assert ratio <= BF16_TOL, f"{what}: max err / rms {ratio} > {BF16_TOL}"
+    return ratio
 
 
 def assert_f32_parity(gpu: np.ndarray, oracle: np.ndarray, what: str, rtol: float = F32_RTOL,
