@@ -184,21 +184,29 @@ def param_counts(n_heads: int, q_lora: int = Q_LORA) -> dict:
 # Query path: RMSNorm -> wq_b -> split -> RoPE on the rotary part
 # ---------------------------------------------------------------------------------------------
 def query_path(q_latent_bits, gamma, wq_b_bits, rope_cs, n_heads: int, eps: float = 1e-6,
-               staged: bool = True) -> Tuple[np.ndarray, np.ndarray]:
+               staged: bool = True, round_output: bool = True) -> Tuple[np.ndarray, np.ndarray]:
     """[QH] q^C = c^Q W_UQ, q^pe = c^Q W_QR, Q^R_t = RoPE(Q^pe_t, R_t), Q = [Q^C; Q^R], with
     c^Q = q_norm(q latent) ([QN], [AU] RMSNorm; [QH] query excerpt: qr = q_norm(.), q = wq_b(qr)).
 
     q_latent_bits: bf16 [n, 1536]; gamma fp32 [1536]; wq_b_bits bf16 [1536, H*192];
-    rope_cs fp32 [n, 32, 2]. Returns (q [n, H, 192] fp64 -- bf16-valued when staged,
-    inv_rms [n]). Token-major layout [n, H, 192] as the query code's view.
+    rope_cs fp32 [n, 32, 2]. Returns (q [n, H, 192] fp64 -- bf16-valued when staged and
+    round_output, inv_rms [n]). Token-major layout [n, H, 192] as the query code's view.
+    staged and not round_output: every feature before its last rounding -- the content features
+    are the Linear output before its bf16 rounding (their last), the rotary features the rotation
+    of the bf16 Linear output before the rotated values are rounded.
     """
     x = bf16_decode(q_latent_bits)
     y, inv_rms = rms_norm(x, gamma, eps)
     y = _maybe_round(y, staged)                         # RMSNorm output stored in the input dtype
     w = bf16_decode(wq_b_bits)
-    q = _maybe_round(y @ w, staged)                    # bf16 Linear output
+    lin = y @ w
+    q = _maybe_round(lin, staged)                       # bf16 Linear output
     q = q.reshape(q.shape[0], n_heads, QK)
     rot = rope_rotate(q[:, :, NOPE:], np.asarray(rope_cs, np.float64)[:, None, :, :])
+    if staged and not round_output:
+        q = lin.reshape(q.shape).copy()
+        q[:, :, NOPE:] = rot
+        return q, inv_rms
     q[:, :, NOPE:] = _maybe_round(rot, staged)          # rotated q_pe stored in bf16
     return q, inv_rms
 

@@ -145,6 +145,14 @@ def test_query_path_staged_points_are_bf16_and_close_to_exact():
     qe, _ = O.query_path(x, g, w, cs, 2, staged=False)
     assert np.array_equal(O.bf16_round(qs), qs)
     assert np.max(np.abs(qs - qe)) <= 2e-2 * np.sqrt(np.mean(qe ** 2))
+    # before the last rounding: the content features are the exact Linear output (the RMSNorm
+    # output rounded first), so they round to the staged values; the rotary features round to them
+    # too, and differ from the exact path's only through the rounding of the Linear output
+    qu, _ = O.query_path(x, g, w, cs, 2, staged=True, round_output=False)
+    assert np.array_equal(O.bf16_round(qu), qs)
+    assert not np.array_equal(qu[:, :, :128], qs[:, :, :128])
+    lin = (O.bf16_round(O.rms_norm(O.bf16_decode(x), g)[0]) @ O.bf16_decode(w)).reshape(6, 2, 192)
+    np.testing.assert_allclose(qu[:, :, :128], lin[:, :, :128], rtol=1e-12, atol=1e-14)
 
 
 # ------------------------------------------------------------------------------ decode
