@@ -1,30 +1,43 @@
 """Benchmark of the MLA hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N] [--no-prefill] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads 3,0,1,4] [--no-prefill]
+                    [--no-next] [--no-cpu] [--no-peaks]
 
-A step is one pass of the decode hot path over one batch of the DeepSeek-V3.2-shaped decode
-workload (32 sequences x 4096 cached tokens, 128 heads): mla_query_path on the 32 new tokens, then
-mla_decode (absorb, split-KV attention, log-sum-exp combine, value projection). Inputs are
-synthetic (seeded) and resident in HBM before the timed region; four copies of every input are
-rotated so that the 256 MB Infinity Cache cannot hold the working set between steps.
+A step is one pass of the decode hot path over one batch of a decode workload: mla_query_path on
+the batch's new tokens, then mla_decode (absorb, split-KV attention, log-sum-exp combine, value
+projection). Inputs are synthetic (seeded) and resident in HBM before the timed region; workloads
+whose inputs fit the 256 MB Infinity Cache rotate copies of every input so that a step never finds
+the previous step's data there.
+
+The headline is the first workload of --workloads (default: the ragged batch, 128 sequences of
+256..32768 cached tokens at 128 heads, the largest decode configuration); the other decode
+workloads (Kimi-K2 B = 1 x 1000 at 64 heads, DeepSeek-V3.2 32 x 4096, 8 x 131072 with spikes) are
+measured in the same run and reported under "decode_workloads".
 
 The printed JSON line carries:
-  value       whole-job decode throughput, cache-token.heads/s = H * sum(L_b) / step time
+  value       whole-job decode throughput of the headline workload, cache-token.heads/s =
+              H * sum(L_b) / step time
   roofline    the split-KV attention kernel (the dominant kernel): algorithmic bytes per launch
               (1152 B per cached token: 512 latent + 64 rotary bf16) / its mean duration, timed with
-              HIP events recorded on its own stream around that kernel, against 8 TB/s; `traffic`
-              is the HBM bytes per launch measured by rocprofv3 (FETCH_SIZE + WRITE_SIZE, scaled by a
+              HIP events recorded on its own stream around that kernel, against 8 TB/s, and against
+              the stream-read rate measured in the same process (`peaks`); `traffic` is the HBM
+              bytes per launch measured by rocprofv3 (FETCH_SIZE + WRITE_SIZE, scaled by a
               copy-kernel calibration) as committed under profiles/, or null when the kernel source
-              has changed since (checked by hash) or for another workload
+              has changed since (checked by hash)
+  peaks       achievable rates measured in this process: a plain streaming read of 4 GiB and a loop
+              of independent bf16 MFMAs on every SIMD
+  decode_workloads  the same record (step, stages, attention roofline, oracle baseline) for every
+              decode workload
   prefill     the DeepSeek-V3.2-shaped prefill (T = 4096, 128 heads): query path + expansion +
-              causal attention, TFLOP/s of algorithmic flops against 2.5 PFLOP/s bf16
-  cpu_baseline the CPU oracle on a bounded sample of the same workload (whole sequences, one at a
-              time, for about half of --cpu-budget seconds)
+              causal attention, TFLOP/s of algorithmic flops against 2.5 PFLOP/s bf16, with an
+              oracle sample
+  cpu_baseline the CPU oracle on a bounded sample of the headline workload (whole sequences, one at
+              a time), with the host's CPU model, core count and NumPy's BLAS
   next_rows   the steps next to the path, each with its time, roofline fraction and an oracle
-              sample: mla_kv_append (32 decode / 4096 prefill tokens), mla_decode_sparse (the decode
-              workload with 2048 of 4096 positions per sequence), mla_prefill_with_prefix (the last
-              2048 of the 4096 prefill positions over the first 2048), mla_output_proj (wo 7168 x
-              16384 after 32 and 4096 tokens)
+              sample: mla_kv_append (32 decode / 4096 prefill tokens), mla_decode_sparse (the
+              32 x 4096 workload with 2048 of 4096 positions per sequence), mla_prefill_with_prefix
+              (the last 2048 of the 4096 prefill positions over the first 2048), mla_output_proj (wo
+              7168 x 16384 after 32 and 4096 tokens)
 
     python bench.py --copy-calibration MIB   only runs a plain device copy of MIB MiB (for scaling
                                              the rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
@@ -54,8 +67,9 @@ def log(*a):
 
 
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_kernel_hbm_traffic_dsv32_b32_l4096.txt")
+PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SRC = os.path.join(ROOT, "head_latent_attention_fp32_amd", "csrc", "decode.hip")
+PEAKS_LIB = os.path.join(ROOT, "head_latent_attention_fp32_amd", "libmla_peaks.so")
 
 
 class HipEvents:
@@ -83,14 +97,17 @@ def to_dev_bf16(torch, bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def decode_bench(args, torch, binding, S):
-    case = S.workload(args.workload)
+def decode_bench(args, torch, binding, S, workload):
+    case = S.workload(workload)
     B, H = case.batch, case.n_heads
     log(f"[bench] generating {case.name} (B={B}, H={H}, sum L={int(case.lengths.sum())})")
     d = S.decode_inputs(case, seed=0)
     L = binding.lib()
     dims = binding.dims(H)
-    n_copies = args.copies
+    # copies rotated so that the inputs of the steps in flight never fit the 256 MB Infinity Cache
+    # together: enough copies for about 1 GB, at most --copies (one when a single copy is larger)
+    one = sum(int(d[k].nbytes) for k in ("q_latent", "wq_b", "wkv_b", "kv_cache", "pe_cache"))
+    n_copies = int(max(1, min(args.copies, -(-(1 << 30) // one))))
     sets = []
     base = {
         "q_latent": to_dev_bf16(torch, d["q_latent"]), "gamma": torch.from_numpy(d["gamma"]).cuda(),
@@ -168,7 +185,7 @@ def decode_bench(args, torch, binding, S):
     alg_query = 1536 * H * 192 * 2 + B * 1536 * 2 + B * H * 192 * 2
     decode_ms = ms - float(stage_q.sum()) * (ms / float(stage_q.sum() + stage_d.sum()))
     res = {
-        "case": case, "ms": ms, "tokens": tokens, "H": H, "B": B,
+        "case": case, "ms": ms, "tokens": tokens, "H": H, "B": B, "copies": n_copies,
         "value": H * tokens / (ms * 1e-3),
         "attn_ms": attn_ms,
         "event_pair_ms": pair_ms,
@@ -434,18 +451,57 @@ def next_rows_bench(args, torch, binding, S, dec_d, pre_inputs):
     return rows
 
 
-def measured_traffic():
+def measured_traffic(workload_name):
     """HBM bytes per launch of the attention kernel on this workload, from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary -- None when decode.hip changed since it was taken."""
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary profiles/attend_kernel_hbm_traffic_<workload>.txt --
+    None when there is none or decode.hip changed since it was taken."""
     import hashlib
     try:
-        fields = dict(l.split(":", 1) for l in open(TRAFFIC_FILE).read().splitlines() if ":" in l)
+        path = os.path.join(PROFILES, f"attend_kernel_hbm_traffic_{workload_name}.txt")
+        fields = dict(l.split(":", 1) for l in open(path).read().splitlines() if ":" in l)
         src = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
         if fields.get("decode_hip_sha256", "").strip() != src:
             return None
         return float(fields["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def measure_peaks(torch):
+    """Achievable rates on this GPU, measured in this process: a plain streaming read of 4 GiB (the
+    HBM read rate a kernel can reach) and a loop of independent bf16 16x16x32 MFMAs on every SIMD
+    (the matrix rate at the clock the chip holds under it). Each is the median of 7 launches timed
+    with events on the stream they run on."""
+    lib = ctypes.CDLL(PEAKS_LIB)
+    lib.mla_peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mla_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def timed(launch, reps=7):
+        for _ in range(3):
+            assert launch() == 0
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            assert launch() == 0
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    ms_read = timed(lambda: lib.mla_peak_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream))
+    del buf
+    blocks, iters = 1024, 20000
+    ms_mfma = timed(lambda: lib.mla_peak_mfma(blocks, iters, sink.data_ptr(), stream))
+    flops = blocks * 4 * iters * 8 * 16384
+    return {"stream_read_gbps": nbytes / (ms_read * 1e-3) / 1e9, "stream_read_bytes": nbytes,
+            "mfma_bf16_tflops": flops / (ms_mfma * 1e-3) / 1e12,
+            "note": "plain 4 GiB streaming read (16-byte loads, 2048 blocks) and 8 independent 16x16x32 bf16 "
+                    "MFMA chains per wave, 1024 blocks of 4 waves; median of 7 launches"}
 
 
 def copy_calibration(torch, mib):
@@ -458,6 +514,30 @@ def copy_calibration(torch, mib):
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def host_description():
+    """The host the oracle runs on: CPU model, cores it may use, and NumPy's BLAS build."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
+    blas = None
+    try:
+        import threadpoolctl
+        for i in threadpoolctl.threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer')} threads, " \
+                       f"{i.get('architecture')})"
+                break
+    except Exception:  # pragma: no cover
+        pass
+    return {"cpu_model": model, "cores_available": len(os.sched_getaffinity(0)),
+            "numpy": np.__version__, "numpy_blas": blas}
 
 
 def cpu_baseline(case, d, budget_s):
@@ -497,7 +577,46 @@ def cpu_baseline(case, d, budget_s):
         ctl.unregister() if hasattr(ctl, "unregister") else None
     return {"value": H * tokens / dt, "unit": "cache-token·heads/s", "cores": int(used), "kind": "oracle",
             "sample": f"{n_seq} sequences ({passes} pass(es) over the {case.batch} of {case.name}; query path + "
-                      f"absorbed decode, fp64 NumPy, one sequence at a time), {dt:.1f} s"}
+                      f"absorbed decode, fp64 NumPy, one sequence at a time), {dt:.1f} s",
+            "host": host_description()}
+
+
+def decode_record(res, cpu, peaks):
+    """The per-workload record: step, stages, the attention kernel's roofline and the oracle."""
+    case = res["case"]
+    achieved = res["attn_gbps"]
+    roof = {"bound": "hbm", "kernel": "split-KV attention (mla_decode stage 2)",
+            "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": measured_traffic(case.name),
+            "bytes_per_launch": res["alg_cache"],
+            "attn_us": (res["attn_ms"] - res["event_pair_ms"]) * 1e3,
+            "attn_us_between_events": res["attn_ms"] * 1e3,
+            "event_pair_us": res["event_pair_ms"] * 1e3,
+            "duration_note": "mean span between the events that bracket the kernel in the timed loop, "
+                             "less the mean span of two events recorded back to back after a step "
+                             "(what a pair of events adds by itself)"}
+    if peaks:
+        roof["frac_of_measured_read_peak"] = achieved / peaks["stream_read_gbps"]
+    return {"workload": case.name, "batch": res["B"], "heads": res["H"], "cached_tokens": res["tokens"],
+            "value": res["value"], "unit": "cache-token·heads/s", "ms_per_step": res["ms"],
+            "input_copies_rotated": res["copies"],
+            "hbm_gbps": res["step_gbps"], "decode_hbm_gbps": res["decode_gbps"],
+            "stages_ms": res["stages_ms"], "roofline": roof, "cpu_baseline": cpu}
+
+
+def prefill_cpu_baseline(p, budget):
+    """The oracle on a sample of the prefill workload: one head's expansion of the 4096 keys and
+    the causal attention of that head's last query row over them."""
+    from oracle import mla_oracle as O
+    T = p["kv_latent"].shape[1]
+    qh = np.random.default_rng(0).standard_normal((T, 1, 192))
+    c = _cpu_timed(lambda: O.prefill_causal(qh, p["kv_latent"][0], p["k_pe"][0], p["wkv_b"][:256], 192 ** -0.5,
+                                            heads=[0], rows=[T - 1]), budget,
+                   2.0 * T * 512 * 256 + 640.0 * T, "FLOP/s")
+    c["sample"] = ("one head's expansion of the 4096 latent rows (k_nope and values) and its last query row's "
+                   "causal attention over them (fp64 NumPy), repeated")
+    c["host"] = host_description()
+    return c
 
 
 def main():
@@ -505,12 +624,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=300,
-                    help="untimed steps first (about 30 ms: the clock settles from ~1.9 to ~2.3 GHz)")
-    ap.add_argument("--workload", type=int, default=1, help="decode workload: 0, 1 (default), 3 or 4")
-    ap.add_argument("--copies", type=int, default=4, help="rotated input copies (defeat the Infinity Cache)")
+                    help="untimed steps first (the clock settles from ~1.9 to ~2.3 GHz over ~0.2 s of work)")
+    ap.add_argument("--workloads", default="3,0,1,4",
+                    help="decode workloads, the first one the headline (0, 1, 3 and/or 4)")
+    ap.add_argument("--copies", type=int, default=64, help="most input copies rotated (defeat the Infinity Cache)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-peaks", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="oracle seconds for the headline workload")
+    ap.add_argument("--sub-cpu-budget", type=float, default=3.0, help="oracle seconds for each other workload")
     ap.add_argument("--no-next", action="store_true", help="skip the steps next to the path")
     ap.add_argument("--next-cpu-budget", type=float, default=2.0, help="oracle seconds per next-row baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -520,8 +642,9 @@ def main():
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
-    if args.workload not in (0, 1, 3, 4):
-        sys.exit("--workload must be a decode workload (0, 1, 3 or 4)")
+    workloads = [int(w) for w in args.workloads.split(",") if w.strip()]
+    if not workloads or any(w not in (0, 1, 3, 4) for w in workloads):
+        sys.exit("--workloads takes decode workloads 0, 1, 3 and 4")
 
     import torch
     from head_latent_attention_fp32_amd import binding
@@ -533,9 +656,31 @@ def main():
         return
     binding.lib()
 
-    res, d = decode_bench(args, torch, binding, S)
-    case = res["case"]
-    log(f"[bench] decode step {res['ms'] * 1e3:.1f} us; stages (ms) {json.dumps(res['stages_ms'])}")
+    peaks = None
+    if not args.no_peaks:
+        peaks = measure_peaks(torch)
+        log(f"[bench] peaks: stream read {peaks['stream_read_gbps']:.0f} GB/s, "
+            f"MFMA bf16 {peaks['mfma_bf16_tflops']:.0f} TFLOP/s")
+
+    records, head_res, head_d, dec1 = [], None, None, None
+    for k, w in enumerate(workloads):
+        res, d = decode_bench(args, torch, binding, S, w)
+        log(f"[bench] {res['case'].name}: step {res['ms'] * 1e3:.1f} us; attention "
+            f"{(res['attn_ms'] - res['event_pair_ms']) * 1e3:.1f} us; stages (ms) {json.dumps(res['stages_ms'])}")
+        cpu = None
+        if not args.no_cpu:
+            log(f"[bench] timing the CPU oracle on {res['case'].name}")
+            cpu = cpu_baseline(res["case"], d, args.cpu_budget if k == 0 else args.sub_cpu_budget)
+        records.append(decode_record(res, cpu, peaks))
+        if k == 0:
+            head_res, head_d = res, d
+        if w == 1:
+            dec1 = d
+        if k > 0 and w != 1:
+            del d
+        torch.cuda.empty_cache()
+    head = records[0]
+
     p_in = None
     if not (args.no_prefill and args.no_next):
         log(f"[bench] generating {S.workload(2).name}")
@@ -543,49 +688,41 @@ def main():
     pre = None if args.no_prefill else prefill_bench(args, torch, binding, S, p_in)
     if pre:
         log(f"[bench] prefill {pre['ms']:.3f} ms, {pre['tflops']:.1f} TFLOP/s")
+        if not args.no_cpu:
+            pre["cpu_baseline"] = prefill_cpu_baseline(p_in, args.sub_cpu_budget)
     nxt = None
     if not args.no_next:
-        dec_d = d if case.name == S.workload(1).name else S.decode_inputs(S.workload(1), seed=0)
+        dec_d = dec1 if dec1 is not None else S.decode_inputs(S.workload(1), seed=0)
         log("[bench] steps next to the path (kv append, top-k decode, prefix prefill, output projection)")
         nxt = next_rows_bench(args, torch, binding, S, dec_d, p_in)
         log(f"[bench] next rows: {json.dumps({k: v.get('us', v.get('ms')) for k, v in nxt.items()})}")
-    cpu = None
-    if not args.no_cpu:
-        log("[bench] timing the CPU oracle")
-        cpu = cpu_baseline(case, d, args.cpu_budget)
     line = {
         "metric": METRIC,
-        "value": res["value"],
+        "value": head["value"],
         "unit": "cache-token·heads/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": res["ms"],
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": case.name, "batch": res["B"], "heads": res["H"],
-                   "cached_tokens": res["tokens"], "step": "mla_query_path + mla_decode",
-                   "input_copies_rotated": args.copies},
-        "hbm_gbps": res["step_gbps"],
-        "decode_hbm_gbps": res["decode_gbps"],
-        "stages_ms": res["stages_ms"],
+        "config": {"workload": head["workload"], "batch": head["batch"], "heads": head["heads"],
+                   "cached_tokens": head["cached_tokens"], "step": "mla_query_path + mla_decode",
+                   "input_copies_rotated": head["input_copies_rotated"]},
+        "hbm_gbps": head["hbm_gbps"],
+        "decode_hbm_gbps": head["decode_hbm_gbps"],
+        "stages_ms": head["stages_ms"],
         "stages_note": "stages_ms from a separate pass with an event at every stage boundary (each event adds about "
                        "2 us); ms_per_step and the roofline come from the timed pass, whose only events bracket the "
                        "attention kernel",
-        "roofline": {"bound": "hbm", "kernel": "split-KV attention (mla_decode stage 2)",
-                     "achieved": res["attn_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": res["attn_gbps"] / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic() if case.name == "dsv32_decode_b32_l4096_h128" else None,
-                     "bytes_per_launch": res["alg_cache"],
-                     "attn_us": (res["attn_ms"] - res["event_pair_ms"]) * 1e3,
-                     "attn_us_between_events": res["attn_ms"] * 1e3,
-                     "event_pair_us": res["event_pair_ms"] * 1e3,
-                     "duration_note": "mean span between the events that bracket the kernel in the timed loop, "
-                                      "less the mean span of two events recorded back to back after a step "
-                                      "(what a pair of events adds by itself)"},
+        "roofline": head["roofline"],
+        "peaks": peaks,
+        "cpu_baseline": head["cpu_baseline"],
+        "decode_workloads": {r["workload"]: r for r in records},
         "prefill": None if pre is None else {
             "workload": pre["workload"], "ms": pre["ms"], "tflops": pre["tflops"],
-            "frac_of_bf16_peak": pre["tflops"] / BF16_PEAK_TFLOPS, "stages": pre["stages"]},
-        "cpu_baseline": cpu,
+            "frac_of_bf16_peak": pre["tflops"] / BF16_PEAK_TFLOPS,
+            "frac_of_measured_mfma_peak": (pre["tflops"] / peaks["mfma_bf16_tflops"]) if peaks else None,
+            "stages": pre["stages"], "cpu_baseline": pre.get("cpu_baseline")},
         "next_rows": nxt,
     }
     print(json.dumps(line), flush=True)

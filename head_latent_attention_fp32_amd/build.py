@@ -18,6 +18,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla.so")
 SOURCES = ["mla_api.cpp", "query_path.hip", "decode.hip", "prefill.hip", "kv_side.hip", "out_proj.hip"]
+# The benchmark's in-process rate probes (stream read, MFMA loop): a library of their own, outside
+# libmla's ABI.
+PEAKS_LIB = os.path.join(PKG, "libmla_peaks.so")
+PEAKS_SOURCES = ["peaks.hip"]
 ARCH = "gfx950"
 
 COMMON = [
@@ -56,18 +60,20 @@ def build(verbose: bool = False) -> str:
     cc = hipcc()
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
+    objs = {LIB: [], PEAKS_LIB: []}
     jobs = []
-    for s in SOURCES:
-        o = os.path.join(objdir, os.path.splitext(s)[0] + ".o")
-        objs.append(o)
-        lang = ["-x", "hip"] if s.endswith(".cpp") else []
-        jobs.append([cc] + COMMON + PER_FILE.get(s, []) + lang + ["-c", os.path.join(CSRC, s), "-o", o])
+    for lib, sources in ((LIB, SOURCES), (PEAKS_LIB, PEAKS_SOURCES)):
+        for s in sources:
+            o = os.path.join(objdir, os.path.splitext(s)[0] + ".o")
+            objs[lib].append(o)
+            lang = ["-x", "hip"] if s.endswith(".cpp") else []
+            jobs.append([cc] + COMMON + PER_FILE.get(s, []) + lang + ["-c", os.path.join(CSRC, s), "-o", o])
     with ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
-    tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
-    os.replace(tmp, LIB)
+    for lib, o in objs.items():
+        tmp = lib + ".tmp"
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + o, verbose)
+        os.replace(tmp, lib)
     return LIB
 
 
