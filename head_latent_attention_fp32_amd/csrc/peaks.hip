@@ -28,7 +28,10 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
-// Eight independent accumulator chains of v_mfma_f32_16x16x32_bf16 per wave, `iters` rounds.
+// Eight independent accumulator chains of v_mfma_f32_16x16x32_bf16 per wave, `iters` rounds. The
+// round is one asm block so that the accumulators stay in place (the compiler otherwise shuffles
+// them through other registers every round); a chain's next product comes eight products later,
+// past the result latency. The values only feed a comparison that keeps the loop alive.
 __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* sink) {
   const int lane = threadIdx.x & 63;
   bf16x8 a, b;
@@ -36,14 +39,24 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* sink) 
     a[e] = static_cast<__bf16>(1.0f + 0.001f * ((lane + e) & 7));
     b[e] = static_cast<__bf16>(0.5f - 0.001f * ((lane * 3 + e) & 7));
   }
-  f32x4 c[8];
-  for (int k = 0; k < 8; ++k) c[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  f32x4 c0 = z, c1 = z, c2 = z, c3 = z, c4 = z, c5 = z, c6 = z, c7 = z;
   for (int it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) c[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[k], 0, 0, 0);
+    asm volatile(
+        "v_mfma_f32_16x16x32_bf16 %0, %8, %9, %0\n\t"
+        "v_mfma_f32_16x16x32_bf16 %1, %8, %9, %1\n\t"
+        "v_mfma_f32_16x16x32_bf16 %2, %8, %9, %2\n\t"
+        "v_mfma_f32_16x16x32_bf16 %3, %8, %9, %3\n\t"
+        "v_mfma_f32_16x16x32_bf16 %4, %8, %9, %4\n\t"
+        "v_mfma_f32_16x16x32_bf16 %5, %8, %9, %5\n\t"
+        "v_mfma_f32_16x16x32_bf16 %6, %8, %9, %6\n\t"
+        "v_mfma_f32_16x16x32_bf16 %7, %8, %9, %7\n\t"
+        "s_nop 7"
+        : "+a"(c0), "+a"(c1), "+a"(c2), "+a"(c3), "+a"(c4), "+a"(c5), "+a"(c6), "+a"(c7)
+        : "v"(a), "v"(b));
   }
-  float s = 0.f;
-  for (int k = 0; k < 8; ++k) s += c[k][0] + c[k][1] + c[k][2] + c[k][3];
+  const f32x4 t = ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7));
+  const float s = (t[0] + t[1]) + (t[2] + t[3]);
   if (s == 1234.5f) sink[0] = s;
 }
 
