@@ -293,29 +293,33 @@ __global__ __launch_bounds__(256) void topk_compact_kernel(const int32_t* __rest
 //    a 4-deep ring of 32-row LDS tiles filled by 16-byte direct-to-LDS buffer loads. Each tile's
 //    buffer descriptor ends at the segment's last row, so rows past it read as zeros, and every
 //    row is read from HBM once per head group.
-//    The waves split by role, one of each role per SIMD:
-//      score waves 0-3   wave w holds the query of heads 16w .. 16w+15 (absorbed latent and
-//                        rotary part, 576 features) in VGPRs and computes S^T[t][h] =
-//                        sum_k tile[t][k] q[h][k] on MFMA (A operand: ds_read_b128 of tile rows),
-//                        then the softmax: per head a reference m (log2 units, scale folded in)
-//                        that moves only when a tile's maximum exceeds it by more than 8, so
-//                        p = 2^(s - m) <= 2^8, written to LDS as bf16 (a common part keeps the
-//                        reference; a full part on a branch of its own moves it);
-//      value waves 4-7   wave 4+w owns latent columns [128 w, 128 w + 128) of all 64 heads and
-//                        adds O^T[c][h] += sum_t tile[t][c] P^T[t][h] (A operand:
-//                        ds_read_b64_tr_b16, the transposing LDS read, of tile columns; B operand:
-//                        ds_read_b128 of P).
+//    Waves w and w + 4 share a SIMD. The waves split by role:
+//      score waves 0, 1   wave s holds the query of heads 32s .. 32s+31 (absorbed latent and rotary
+//                         part, 576 features, as two blocks of 16 heads) in VGPRs and computes
+//                         S^T[t][h] = sum_k tile[t][k] q[h][k] on MFMA (A operand: ds_read_b128 of
+//                         tile rows, each read feeding both head blocks), then the softmax: per
+//                         head a reference m (log2 units, scale folded in) that moves only when a
+//                         tile's maximum exceeds it by more than 8, so p = 2^(s - m) <= 2^8,
+//                         written to LDS as bf16 (a common part keeps the reference; a full part
+//                         on a branch of its own moves it);
+//      value waves 2, 3, 6, 7   value wave v (0..3 in that order) owns latent columns
+//                         [128 v, 128 v + 128) of all 64 heads and adds O^T[c][h] += sum_t
+//                         tile[t][c] P^T[t][h] (A operand: ds_read_b64_tr_b16, the transposing LDS
+//                         read, of tile columns; B operand: ds_read_b128 of P); the two value waves
+//                         of SIMDs 2 and 3 keep those matrix pipes busy while the score waves keep
+//                         those of SIMDs 0 and 1;
+//      loader waves 4, 5  issue every tile load (18 each per tile) and wait for them.
 //    One barrier per tile. Iteration j: the score waves run the MFMAs of S(j+1) with the softmax
 //    of tile j (its scores held in registers since the previous iteration) interleaved between
-//    them, so that the matrix pipe of each SIMD works on the scores while its vector ALU works on
-//    the exponentials; the value waves run the MFMAs of tile j-1 against P(j-1), read tile j's V^T
-//    into registers and issue the loads of tile j+3 into the stage tile j-1 held (so three tiles
-//    are in flight). P and the rescale factors are double-buffered by tile parity. A head block
-//    with a rescale factor other than 1 (its reference moved) has its accumulators rescaled before
-//    the value MFMAs of that tile, outside the MFMA chain.
+//    them, so that the matrix pipe works on the scores while the vector ALU works on the
+//    exponentials; the value waves run the MFMAs of tile j-1 against P(j-1) and read tile j's V^T
+//    into registers; the loaders issue the loads of tile j+3 into the stage tile j-1 held (so three
+//    tiles are in flight). P and the rescale factors are double-buffered by tile parity. A head
+//    block with a rescale factor other than 1 (its reference moved) has its accumulators rescaled
+//    before the value MFMAs of that tile, outside the MFMA chain.
 //    P^T comes out of the S^T accumulators with lane l holding tokens 4(l/16)+{0..3} and
-//    16+4(l/16)+{0..3} of head l%16 -- its k-group of the P.V product -- and V^T is read in the
-//    same token order.
+//    16+4(l/16)+{0..3} of head l%16 of a head block -- its k-group of the P.V product -- and V^T is
+//    read in the same token order.
 //    LDS layouts: latent part of a tile [32 rows][1024 B] with 16-byte chunk c of row r at
 //    c ^ fk(r), fk(r) = 2(r&7); rotary part [32 rows][128 B] with chunk c at c ^ ((r>>1)&7); P as
 //    [4 token chunks][64 heads][16 B]. A 128-bit LDS read serves each half-wave in two passes, one
@@ -331,6 +335,7 @@ constexpr int kTileBytes = kKvBytes + kPeBytes;            // 36864
 constexpr int kStages = 4;                                 // tiles in the LDS ring
 constexpr int kBlockHeads = 64;                            // heads of one workgroup
 constexpr int kPBytes = kTileTok / 8 * kBlockHeads * 16;   // one P buffer
+constexpr int kLoadsPerLoader = kTileBytes / 1024 / 2;     // 18: 16 latent rows and 16 rotary rows
 
 __device__ __forceinline__ int fk(int row) { return 2 * (row & 7); }
 __device__ __forceinline__ int fp(int row) { return (row >> 1) & 7; }
@@ -354,9 +359,15 @@ __device__ __forceinline__ bf16x8 lds_vt(const uint8_t* p) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// State shared by the two roles of an attention workgroup. Both walk the same segments (the
-// pieces of the run that lie in one sequence) and pass the same barriers: two before the first
-// tile, two per tile, three at the end of a segment.
+// State shared by the three roles of an attention workgroup. All walk the same segments (the
+// pieces of the run that lie in one sequence) and pass the same n_tiles + 3 barriers per segment.
+// Barrier k: tile k has landed (loaders wait for it before); for k >= 1 the stage of tile k-2 is
+// free (its scores were taken after barrier k-2, its V^T read after barrier k-1), and the score
+// waves have published P(k-2); after the last tile, barrier n_tiles + 1 publishes P(n_tiles - 1)
+// and barrier n_tiles + 2 the per-head sums. Score waves: barrier 0, then scores(0); barrier j + 1,
+// then scores(j+1) and softmax(j). Value waves: barriers 0 and 1, then V^T(0); barrier j + 1
+// (j >= 1), then P(j-1), the MFMAs of tile j-1 and V^T(j). Loaders: tiles 0, 1, barrier 0,
+// tiles 2, 3, barrier 1; barrier j + 1 (j >= 1), then tile j + 3.
 struct AttendCtx {
   const uint16_t* q_lat;
   const uint16_t* q;
@@ -421,82 +432,131 @@ struct SegmentWalk {
   }
 };
 
-// Loads of tile t of segment sg into ring stage t % 4, all issued by the value waves (the
-// score waves' critical path -- scores, then softmax -- must not stall behind the load queue):
-// value wave v fills latent rows v + 4k (k < 8) -- physical chunk `lane` holds logical chunk
-// lane ^ fk(row) -- and the rotary rows 8v .. 8v+7 (physical chunk lane%8 of row 8v + lane/8 holds
-// logical chunk (lane%8) ^ fp(row)). The descriptors start at the tile's first row and cover its
-// rows up to the segment's last (none for a tile past the segment: it loads zeros and reads no
-// memory); kv_voff[k] is the byte offset of lane's chunk of row v + 4k.
-__device__ __forceinline__ void issue_tile(const AttendCtx& c, const Segment& sg, int t, const uint32_t* kv_voff,
-                                           uint32_t pe_voff) {
-  const int v = c.wave & 3;
+// Loads of tile t of segment sg into ring stage t % 4 by loader ld (0, 1): latent rows ld + 2k
+// (k < 16) -- physical chunk `lane` holds logical chunk lane ^ fk(row) -- and rotary rows
+// 16 ld + 8e + lane/8 (e < 2; physical chunk lane%8 holds logical chunk (lane%8) ^ fp(row)). The
+// descriptors start at the tile's first row and cover its rows up to the segment's last (none for
+// a tile past the segment: it loads zeros and reads no memory); kv_voff[k] / pe_voff[e] are the
+// byte offsets of the lane's chunks from the tile's first row.
+__device__ __forceinline__ void issue_tile(const AttendCtx& c, const Segment& sg, int t, int ld,
+                                           const uint32_t* kv_voff, const uint32_t* pe_voff) {
   const int left = sg.n_rows - t * kTileTok;
   const uint32_t rows = static_cast<uint32_t>(left <= 0 ? 0 : (left < kTileTok ? left : kTileTok));
   const int64_t row0 = left <= 0 ? 0 : static_cast<int64_t>(t) * kTileTok;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(sg.kv_seg + row0 * kKvLora, rows * 1024u);
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(sg.pe_seg + row0 * kRope, rows * 128u);
-  const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)c.ring)) +
-                       (t % kStages) * kTileBytes;
+  const uint32_t dst = lds_addr(c.ring) + (t % kStages) * kTileBytes;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) dma16(rk, dst + (v + 4 * k) * 1024, kv_voff[k]);
-  dma16(rp, dst + kKvBytes + v * 1024, pe_voff);
+  for (int k = 0; k < 16; ++k) dma16(rk, dst + (ld + 2 * k) * 1024, kv_voff[k]);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) dma16(rp, dst + kKvBytes + (2 * ld + e) * 1024, pe_voff[e]);
 }
 
 // Top-k mode: the tile's rows are the cache rows of the positions list_seg[32 t .. 32 t + 31] of
 // the sequence (read with scalar loads: the list is uniform across the wave and never changes
 // during the kernel), fetched one issue ahead (TilePos) so that their latency is not paid at the
 // issue. Rows past the segment get a position one past the descriptors' range (max_seqlen rows
-// from the sequence's first), so they read as zeros. kv_chunk[k] and pe_chunk are the lane's byte
-// offsets within its row.
+// from the sequence's first), so they read as zeros. kv_chunk[k] and pe_chunk[e] are the lane's
+// byte offsets within its row.
 typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
 struct TilePos {
-  uint32_t kv[8];   // rows v + 4k of the tile (v = value wave)
-  uint32_t pe[8];   // rows 8v + j
+  uint32_t kv[16];   // rows ld + 2k of the tile
+  uint32_t pe[16];   // rows 16 ld + j
 };
-__device__ __forceinline__ void load_tile_pos(const AttendCtx& c, const Segment& sg, int t, TilePos& p) {
-  const int v = c.wave & 3;
+__device__ __forceinline__ void load_tile_pos(const AttendCtx& c, const Segment& sg, int t, int ld, TilePos& p) {
   const int left = sg.n_rows - t * kTileTok;
   const uint32_t past = static_cast<uint32_t>(c.max_seqlen);
   const const_i32_ptr ti = (const_i32_ptr)(sg.list_seg + t * kTileTok);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int row = v + 4 * k;
+  for (int k = 0; k < 16; ++k) {
+    const int row = ld + 2 * k;
     p.kv[k] = row < left ? static_cast<uint32_t>(ti[row]) : past;
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = 8 * v + j;
+  for (int j = 0; j < 16; ++j) {
+    const int row = 16 * ld + j;
     p.pe[j] = row < left ? static_cast<uint32_t>(ti[row]) : past;
   }
 }
-__device__ __forceinline__ void issue_tile_gather(const AttendCtx& c, const Segment& sg, int t, const uint32_t* kv_chunk,
-                                                  uint32_t pe_chunk, const TilePos& p) {
-  const int v = c.wave & 3;
+__device__ __forceinline__ void issue_tile_gather(const AttendCtx& c, const Segment& sg, int t, int ld,
+                                                  const uint32_t* kv_chunk, const uint32_t* pe_chunk,
+                                                  const TilePos& p) {
   const uint32_t past = static_cast<uint32_t>(c.max_seqlen);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(sg.kv_seg, past * 1024u);
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(sg.pe_seg, past * 128u);
-  const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)c.ring)) +
-                       (t % kStages) * kTileBytes;
+  const uint32_t dst = lds_addr(c.ring) + (t % kStages) * kTileBytes;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) dma16(rk, dst + (v + 4 * k) * 1024, p.kv[k] * 1024u + kv_chunk[k]);
-  uint32_t ppos = past;
+  for (int k = 0; k < 16; ++k) dma16(rk, dst + (ld + 2 * k) * 1024, p.kv[k] * 1024u + kv_chunk[k]);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) ppos = (c.lane >> 3) == j ? p.pe[j] : ppos;
-  dma16(rp, dst + kKvBytes + v * 1024, ppos * 128u + pe_chunk);
+  for (int e = 0; e < 2; ++e) {
+    uint32_t ppos = past;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ppos = (c.lane >> 3) == j ? p.pe[8 * e + j] : ppos;
+    dma16(rp, dst + kKvBytes + (2 * ld + e) * 1024, ppos * 128u + pe_chunk[e]);
+  }
 }
 
-// Score waves 0-3. Wave w holds the query of heads 16w .. 16w+15 (absorbed latent part, 16
-// k-steps, and rotary part, 2 k-steps; B operands, k-group grp of head 16 w + r per lane) and
-// computes S^T[t][h] for all 32 tokens of a tile over the full 576 features (A operand: ds_read_b128
-// of tile rows). Iteration j (one barrier each) runs the MFMAs of tile j+1 and, interleaved with
-// them, the softmax of tile j, whose scores the previous iteration left in registers: per head a
-// reference m (log2 units, scale folded in) that moves only when a tile's maximum exceeds it by
-// more than 8, so that p = 2^(s - m) <= 2^8; P goes to LDS as bf16 with the head's rescale factor.
-// They issue no loads: a tile is complete once the value waves, which wait for their own loads of
-// it, reach the next barrier.
+// Loader waves 4, 5: every tile load of the block, and the waits for them before the barrier that
+// publishes a tile. The first two tiles of a segment go out alone and the next two once the first
+// has landed, so that at a launch the first tile of every block is not queued behind 147 KB per CU;
+// then iteration j issues tile j+3 into the stage tile j-1 held.
+template <bool kGather>
+__device__ __forceinline__ void load_role(const AttendCtx& c) {
+  constexpr int L = kLoadsPerLoader;
+  const int ld = c.wave - 4, lane = c.lane;
+  uint32_t kv_voff[16], pe_voff[2];   // dense mode: from the tile's first row; top-k: within the row
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int row = ld + 2 * k;
+    kv_voff[k] = static_cast<uint32_t>((kGather ? 0 : row * 1024) + ((lane ^ fk(row)) << 4));
+  }
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int row = 16 * ld + 8 * e + (lane >> 3);
+    pe_voff[e] = static_cast<uint32_t>((kGather ? 0 : row * 128) + (((lane & 7) ^ fp(row)) << 4));
+  }
+  TilePos pos;   // top-k mode: positions of the next tile to issue
+  SegmentWalk walk(c);
+  Segment sg;
+  while (walk.next(c, sg)) {
+    const int n_tiles = sg.n_tiles;
+    int issued = 0;
+    auto issue = [&]() {
+      if (kGather) {
+        issue_tile_gather(c, sg, issued, ld, kv_voff, pe_voff, pos);
+        if (issued + 1 < n_tiles) load_tile_pos(c, sg, issued + 1, ld, pos);
+      } else {
+        issue_tile(c, sg, issued, ld, kv_voff, pe_voff);
+      }
+      ++issued;
+    };
+    if (kGather) load_tile_pos(c, sg, 0, ld, pos);
+    while (issued < 2 && issued < n_tiles) issue();
+    wait_tiles<L>(issued - 1);
+    lds_barrier();   // tile 0 landed
+    while (issued < kStages && issued < n_tiles) issue();
+    if (n_tiles > 1) wait_tiles<L>(issued - 2);
+    lds_barrier();   // tile 1 landed
+    for (int j = 1; j <= n_tiles; ++j) {
+      if (j + 1 < n_tiles) wait_tiles<L>(issued - 2 - j);
+      lds_barrier();   // tile j+1 landed; the stage of tile j-1 is free
+      if (issued < n_tiles) issue();
+    }
+    lds_barrier();   // l published
+  }
+}
+
+// Score waves 0, 1. Wave s holds the query of heads 32s + 16hb + r (hb = 0, 1: absorbed latent part,
+// 16 k-steps, and rotary part, 2 k-steps; B operands, k-group grp of the head per lane) and
+// computes S^T[t][h] for all 32 tokens of a tile over the full 576 features (A operand:
+// ds_read_b128 of tile rows, each read feeding the MFMAs of both head blocks). Iteration j (one
+// barrier each) runs the MFMAs of tile j+1 and, interleaved with them, the softmax of tile j, whose
+// scores the previous iteration left in registers: per head a reference m (log2 units, scale folded
+// in) that moves only when a tile's maximum exceeds it by more than 8, so that p = 2^(s - m) <= 2^8;
+// P goes to LDS as bf16 with the head's rescale factor. They issue no loads: a tile is complete
+// once the loader waves, which wait for their own loads of it, reach the next barrier.
 __device__ __forceinline__ void score_role(const AttendCtx& c) {
-  const int w = c.wave, lane = c.lane, r = lane & 15, grp = lane >> 4;
+  const int s = c.wave, lane = c.lane, r = lane & 15, grp = lane >> 4;
   // LDS byte offsets. Latent k-step ks = 4a + k: row 16 tb + r, logical chunk 4 ks + grp at
   // physical 16 a + 4 (k ^ (fk>>2)) + (grp ^ (fk&3)); a and tb go into immediates. Rotary k-step
   // 16 + e: row 16 tb + r, chunk 4 e + grp at (4 e + grp) ^ fp(r).
@@ -507,113 +567,126 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
   int e_off[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) e_off[e] = kKvBytes + r * 128 + 16 * ((4 * e + grp) ^ fp(r));
-  const int p_wr = (grp * kBlockHeads + w * 16 + r) * 16;
-  const int head = c.head0 + w * 16 + r;
-  const bool real = head < c.n_heads;
+  const int hl0 = 32 * s + r;                       // block-local head of head block 0 (+16 for block 1)
+  const int p_wr = (grp * kBlockHeads + hl0) * 16;  // + 256 for head block 1
+  const int head0 = c.head0 + hl0;
+  const bool real0 = head0 < c.n_heads, real1 = head0 + 16 < c.n_heads;
 
   SegmentWalk walk(c);
   Segment sg;
   while (walk.next(c, sg)) {
     const int n_tiles = sg.n_tiles;
-    bf16x8 qf[18];
+    bf16x8 qf[2][18];
     {
-      const int hq = real ? head : 0;
-      const uint16_t* ql = c.q_lat + (static_cast<int64_t>(sg.b) * c.n_heads + hq) * kKvLora + grp * 8;
-      const uint16_t* qp = c.q + (static_cast<int64_t>(sg.b) * c.n_heads + hq) * kQk + kNope + grp * 8;
       const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) qf[j] = as_bf16x8(real ? ldg16(ql + j * 32) : z);
+      for (int hb = 0; hb < 2; ++hb) {
+        const bool real = hb ? real1 : real0;
+        const int hq = real ? head0 + 16 * hb : 0;
+        const uint16_t* ql = c.q_lat + (static_cast<int64_t>(sg.b) * c.n_heads + hq) * kKvLora + grp * 8;
+        const uint16_t* qp = c.q + (static_cast<int64_t>(sg.b) * c.n_heads + hq) * kQk + kNope + grp * 8;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) qf[16 + e] = as_bf16x8(real ? ldg16(qp + e * 32) : z);
+        for (int j = 0; j < 16; ++j) qf[hb][j] = as_bf16x8(real ? ldg16(ql + j * 32) : z);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) qf[hb][16 + e] = as_bf16x8(real ? ldg16(qp + e * 32) : z);
+      }
     }
-    // S^T of tile t: acc[tb] holds tokens 16 tb + 4 grp + {0..3} of head 16 w + r.
-    auto scores = [&](int t, f32x4 (&acc)[2]) {
+    // S^T of tile t: acc[tb][hb] holds tokens 16 tb + 4 grp + {0..3} of head 32 s + 16 hb + r.
+    auto scores = [&](int t, f32x4 (&acc)[2][2]) {
       const uint8_t* tile = c.ring + (t % kStages) * kTileBytes;
       auto rd = [&](int tb, int ks) {
         return ks < 16 ? lds_b128(tile + tb * 16384 + (ks >> 2) * 256 + s_off[ks & 3])
                        : lds_b128(tile + tb * 2048 + e_off[ks - 16]);
       };
-      acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        acc[0] = mfma16x16x32(rd(0, ks), qf[ks], acc[0]);
-        acc[1] = mfma16x16x32(rd(1, ks), qf[ks], acc[1]);
-      }
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) acc[tb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          const bf16x8 a = rd(tb, ks);
+          acc[tb][0] = mfma16x16x32(a, qf[0][ks], acc[tb][0]);
+          acc[tb][1] = mfma16x16x32(a, qf[1][ks], acc[tb][1]);
+        }
     };
-    float m_ref = -INFINITY, lsum = 0.f;   // of head 16 w + r, log2 units; lsum over this lane's tokens
-    // Softmax of tile t from its scores, in two parts. The common part assumes the reference stays
+    // per head block: reference (log2 units) and this lane's running sum of its tokens' weights
+    float m_ref[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f}, lsum_prev[2] = {0.f, 0.f};
+    // Softmax of tile t from its scores, in two parts. The common part assumes the references stay
     // (rescale factor exactly 1): P = 2^(s - m) and the sums, with no cross-lane step, and reports
-    // whether any of the lane's scores exceeds the reference by more than 8. If one does anywhere
-    // in the wave (rare after the first tile of a segment, which always moves the reference from
+    // whether any of the lane's scores exceeds its reference by more than 8. If one does anywhere
+    // in the wave (rare after the first tile of a segment, which always moves the references from
     // -inf), the full part, on a branch of its own, takes each head's maximum, moves the references
     // that must move and redoes P, the sums and the factors. kMask: rows at or past the segment
     // end count as -inf (only the last tile of a segment can have such rows).
-    float lsum_prev = 0.f;
     bool above = false;
-    auto softmax_common = [&](int t, const f32x4 (&s)[2], bool mask) {
+    auto scaled = [&](int t, const f32x4 (&sc)[2][2], int hb, bool mask, float (&y)[8]) {
       const int valid = sg.n_rows - t * kTileTok - 4 * grp;
-      const float thr = m_ref + 8.f;
-      float p[8], y[8];
-      float ymax = -INFINITY;
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float v = s[tb][j] * c.scale_log2;
+          const float v = sc[tb][hb][j] * c.scale_log2;
           y[tb * 4 + j] = (!mask || tb * 16 + j < valid) ? v : -INFINITY;
         }
-      ymax = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])), fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(y[i] - m_ref);
-      lsum_prev = lsum;
-      lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      *reinterpret_cast<bf16x8*>(c.pbuf + (t & 1) * kPBytes + p_wr) = bf16x8_from_f32(p);
-      c.alpha_s[t & 1][w * 16 + r] = 1.f;
-      above = ymax > thr;
     };
-    auto softmax_full = [&](int t, const f32x4 (&s)[2], bool mask) {
-      const int valid = sg.n_rows - t * kTileTok - 4 * grp;
-      float y[8];
+    auto softmax_common = [&](int t, const f32x4 (&sc)[2][2], bool mask) {
+      bool up = false;
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+      for (int hb = 0; hb < 2; ++hb) {
+        float y[8], p[8];
+        scaled(t, sc, hb, mask, y);
+        const float ymax =
+            fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])), fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float v = s[tb][j] * c.scale_log2;
-          y[tb * 4 + j] = (!mask || tb * 16 + j < valid) ? v : -INFINITY;
-        }
-      const float m = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])), fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
-      const float mx = max_over_rows(m);
-      const bool up = mx > m_ref + 8.f;
-      const float m_new = up ? mx : m_ref;
-      const float alpha = fast_exp2(m_ref - m_new);
-      m_ref = m_new;
-      float p[8];
+        for (int i = 0; i < 8; ++i) p[i] = fast_exp2(y[i] - m_ref[hb]);
+        lsum_prev[hb] = lsum[hb];
+        lsum[hb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        *reinterpret_cast<bf16x8*>(c.pbuf + (t & 1) * kPBytes + p_wr + hb * 256) = bf16x8_from_f32(p);
+        c.alpha_s[t & 1][hl0 + 16 * hb] = 1.f;
+        up |= ymax > m_ref[hb] + 8.f;
+      }
+      above = up;
+    };
+    auto softmax_full = [&](int t, const f32x4 (&sc)[2][2], bool mask) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(y[i] - m_ref);
-      lsum = lsum_prev * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
-      *reinterpret_cast<bf16x8*>(c.pbuf + (t & 1) * kPBytes + p_wr) = bf16x8_from_f32(p);
-      c.alpha_s[t & 1][w * 16 + r] = alpha;
+      for (int hb = 0; hb < 2; ++hb) {
+        float y[8], p[8];
+        scaled(t, sc, hb, mask, y);
+        const float m =
+            fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])), fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+        const float mx = max_over_rows(m);
+        const bool up = mx > m_ref[hb] + 8.f;
+        const float m_new = up ? mx : m_ref[hb];
+        const float alpha = fast_exp2(m_ref[hb] - m_new);
+        m_ref[hb] = m_new;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = fast_exp2(y[i] - m_new);
+        lsum[hb] = lsum_prev[hb] * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+        *reinterpret_cast<bf16x8*>(c.pbuf + (t & 1) * kPBytes + p_wr + hb * 256) = bf16x8_from_f32(p);
+        c.alpha_s[t & 1][hl0 + 16 * hb] = alpha;
+      }
     };
     // Iteration j: the scores of tile j+1 (of a stale stage past the last tile: computed, never
     // used) and the common softmax part of tile j in one basic block, so that the softmax's vector
-    // instructions can fill the gaps between MFMAs: eight operand reads go out first, then each
-    // pair of MFMAs is followed by the next two reads.
-    auto step = [&](int j, const f32x4 (&cur)[2], f32x4 (&next)[2], bool mask) {
+    // instructions can fill the gaps between MFMAs: four operand reads go out first, then each
+    // pair of MFMAs (one per head block) is followed by the next read.
+    auto step = [&](int j, const f32x4 (&cur)[2][2], f32x4 (&next)[2][2], bool mask) {
       lds_barrier();   // tile j+1 landed; P(j-1) consumed by the value waves
       scores(j + 1, next);
       softmax_common(j, cur, mask);
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int i = 0; i < 14; ++i) {
+      for (int i = 0; i < 32; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       if (__any(above)) softmax_full(j, cur, mask);
     };
 
-    f32x4 sa[2], sb[2];
+    f32x4 sa[2][2], sb[2][2];
     lds_barrier();   // tile 0 landed
     scores(0, sa);
     // Unrolled by two so that the scores of consecutive tiles alternate between sa and sb; the
@@ -631,40 +704,23 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
     }
     lds_barrier();   // P of the last tile published
     // the log-sum-exp from the fp32 weights (the value waves normalise by their rounded sum)
-    const float ltot = sum_over_rows(lsum);
-    if (grp == 0 && real) c.part_l[(c.g + sg.b) * c.n_heads + head] = (m_ref + __log2f(ltot)) * kLn2;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const float ltot = sum_over_rows(lsum[hb]);
+      if (grp == 0 && (hb ? real1 : real0))
+        c.part_l[(c.g + sg.b) * c.n_heads + head0 + 16 * hb] = (m_ref[hb] + __log2f(ltot)) * kLn2;
+    }
     lds_barrier();   // l published
   }
 }
 
-// Value waves 4-7: O^T += V^T P^T for latent columns [128 w, 128 w + 128) of all 64 heads, one
-// tile behind the score waves. Iteration j: P^T and the rescale factors of tile j-1 from LDS (a
-// head block whose reference moved has its accumulators scaled first, outside the MFMA chain),
-// then, in one basic block, the MFMAs of tile j-1 (V^T from registers, read in the previous
-// iteration) with the loads of tile j+3 (into the stage tile j-1 held; in dense mode also past the
-// segment's end, as zero-length loads, so that the block has no branch) and the transposing reads
-// of tile j's V^T placed between them.
-template <bool kGather>
+// Value waves 2, 3, 6, 7 (v = 0..3): O^T += V^T P^T for latent columns [128 v, 128 v + 128) of
+// all 64 heads, one tile behind the score waves. Iteration j: P^T and the rescale factors of tile
+// j-1 from LDS (a head block whose reference moved has its accumulators scaled first, outside the
+// MFMA chain), then, in one basic block, the MFMAs of tile j-1 (V^T from registers, read in the
+// previous iteration) with the transposing reads of tile j's V^T placed between them.
 __device__ __forceinline__ void value_role(const AttendCtx& c) {
-  constexpr int L = 9;   // loads per tile
-  const int w = c.wave & 3, lane = c.lane, r = lane & 15, grp = lane >> 4;
-  uint32_t kv_voff[8];   // byte offset of the lane's chunk (dense mode: from the tile's first row)
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int row = w + 4 * k;
-    kv_voff[k] = static_cast<uint32_t>((kGather ? 0 : row * 1024) + ((lane ^ fk(row)) << 4));
-  }
-  const int pe_row = 8 * w + (lane >> 3);
-  const uint32_t pe_voff = static_cast<uint32_t>((kGather ? 0 : pe_row * 128) + (((lane & 7) ^ fp(pe_row)) << 4));
-  TilePos pos;   // top-k mode: positions of the next tile to issue
-  auto issue = [&](const Segment& sg, int t) {
-    if (kGather) {
-      issue_tile_gather(c, sg, t, kv_voff, pe_voff, pos);
-      if (t + 1 < sg.n_tiles) load_tile_pos(c, sg, t + 1, pos);
-    } else {
-      issue_tile(c, sg, t, kv_voff, pe_voff);
-    }
-  };
+  const int w = (c.wave & 1) + ((c.wave >> 2) << 1), lane = c.lane, r = lane & 15, grp = lane >> 4;
   // V^T: source row 4 grp + (r>>2) (+16), columns 16 (8 w + cb) + 4 (r&3) .. +3 at physical chunk
   // pair (8 w + cb) ^ (row & 7). P^T: head 16 hb + r, chunk grp.
   const int vrow = 4 * grp + (r >> 2);
@@ -677,15 +733,6 @@ __device__ __forceinline__ void value_role(const AttendCtx& c) {
   Segment sg;
   while (walk.next(c, sg)) {
     const int n_tiles = sg.n_tiles;
-    int issued = 0;
-    if (kGather) {
-      load_tile_pos(c, sg, 0, pos);
-      while (issued < 2 && issued < n_tiles) issue(sg, issued++);
-    } else {
-      issue(sg, issued++);
-      issue(sg, issued++);
-    }
-
     f32x4 o[8][4];   // O^T[16 (8 w + cb) + 4 grp + j][16 hb + r]
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb)
@@ -731,54 +778,29 @@ __device__ __forceinline__ void value_role(const AttendCtx& c) {
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) o[cb][hb] = mfma16x16x32(vf[cb], pf[hb], o[cb][hb]);
     };
-    // Iteration 1 <= j <= n_tiles: tile j+1 landed, barrier (for j = n_tiles: P of the last tile
-    // published), values of tile j-1, the V^T of tile j and the loads of tile j+3 (for j = n_tiles
-    // a stale stage is read and, in dense mode, zero-length loads go out: neither is used).
+    // Iteration 1 <= j <= n_tiles: barrier (tile j+1 landed; for j = n_tiles: P of the last tile
+    // published), values of tile j-1, then the V^T of tile j (for j = n_tiles a stale stage, never
+    // used), two MFMAs per transposing read.
     auto step = [&](int j, const bf16x8 (&prev)[8], bf16x8 (&cur)[8]) {
-      if (j + 1 < n_tiles) wait_tiles<L>(issued - 2 - j);
       lds_barrier();
       bf16x8 pf[4];
       float a[4];
       read_p(j - 1, pf, a);
-      if (kGather) {
-        rescale(j - 1, a);
-        mfmas(prev, pf);
-        sum_mine(j - 1);
-        read_v(j, cur);
-        // the operand reads are complete before the next tile's position loads go out, so that
-        // the waits for later LDS reads do not include those scalar loads
-        __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
-        if (issued < n_tiles && issued <= j + 3) issue(sg, issued++);
-      } else {
-        // the loads go out while P^T is read (the MFMAs may run beside them), then two MFMAs per
-        // transposing read
-        issue(sg, issued++);
-        rescale(j - 1, a);
-        mfmas(prev, pf);
-        sum_mine(j - 1);
-        read_v(j, cur);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      rescale(j - 1, a);
+      mfmas(prev, pf);
+      sum_mine(j - 1);
+      read_v(j, cur);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 #pragma unroll
-        for (int i = 0; i < 14; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      for (int i = 0; i < 14; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     };
 
     bf16x8 va[8], vb[8];
-    wait_tiles<L>(issued - 1);
     lds_barrier();   // tile 0 landed
-    // tiles 2 and 3 only now: at a launch every block asks for its first tiles at once, and the
-    // first tile lands sooner when fewer are queued behind it
-    if (kGather) {
-      while (issued < kStages && issued < n_tiles) issue(sg, issued++);
-    } else {
-      issue(sg, issued++);
-      issue(sg, issued++);
-    }
-    if (n_tiles > 1) wait_tiles<L>(issued - 2);
     lds_barrier();   // tile 1 landed
     read_v(0, va);
     // unrolled by two so that the V^T of consecutive tiles alternates between va and vb
@@ -854,8 +876,9 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(
   c.ring = ring; c.pbuf = pbuf; c.alpha_s = alpha_s; c.l_s = l_s;
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: wave-derived values live in SGPRs
   c.lane = threadIdx.x & 63;
-  if (c.wave < 4) score_role(c);
-  else value_role<kGather>(c);
+  if (c.wave < 2) score_role(c);
+  else if (c.wave == 4 || c.wave == 5) load_role<kGather>(c);
+  else value_role(c);
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -169,9 +169,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_
 }
 
 // Workgroup barrier that orders LDS accesses only. __syncthreads() also orders global memory,
-// which waits for every vector-memory load in flight -- the next stages' loads among them.
+// which waits for every vector-memory load in flight -- the next stages' loads among them. The
+// explicit lgkmcnt(0) (an asm block, which the compiler's wait insertion cannot relax) makes every
+// LDS access this wave issued complete before it reaches the barrier: the release fence alone, and
+// the same wait as a builtin, were seen compiled to a wait after the barrier on a path whose last
+// LDS stores came from a branch, so that another wave could read before they landed.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
