@@ -29,7 +29,10 @@ DecodeLayout decode_layout(int n_heads, int batch, int64_t max_seqlen, int topk 
 
 struct PrefillLayout {
   int64_t t_pad;        // sequence length padded to the key tile
-  size_t knope_off, vt_off, total;
+  size_t knope_off, vt_off;
+  size_t bound_off;     // fp32: per-head max row L1 norm of W_UV [H], then max |latent| per slot [256]
+  size_t vexp_off;      // int32 [H]: the power of two the stored values are divided by
+  size_t total;
 };
 PrefillLayout prefill_layout(int n_heads, int batch, int seqlen);
 

@@ -9,10 +9,15 @@
 // 0 .. kv_len - q_len + i.
 //
 // Two kernels:
+//   0. vbound   an upper bound of every value a head can produce: max_t max_c |latent[t,c]| times
+//               the largest row L1 norm of the head's W_UV, and from it the power of two 2^e_h that
+//               brings the bound into [2^14, 2^15): the head's values are divided by it before they
+//               are stored as f16, so that they neither overflow nor fall into f16's subnormals.
 //   1. expand   [k_nope | v] = latent . wkv_b^T per head for all kv_len positions (MFMA GEMM, bf16
-//               outputs as the bf16 Linear of the excerpt; the values, bf16-rounded, are stored as f16,
-//               which holds every bf16 value below 65504 exactly and lets P be rounded to f16 rather
-//               than bf16 for the P.V product). k_nope is written [b][h][t][128] and v
+//               outputs as the bf16 Linear of the excerpt; the values, bf16-rounded and divided by
+//               2^e_h -- exact, a power of two -- are stored as f16, which holds every such value
+//               exactly and lets P be rounded to f16 rather than bf16 for the P.V product; the
+//               attention multiplies its output back by 2^e_h). k_nope is written [b][h][t][128] and v
 //               transposed in key tiles of 64, [b][h][t/64][128][64], so that the attention kernel's
 //               P.V operand reads runs of keys and each tile's V^T is one contiguous 16 KB run;
 //               within every 32 keys the order is permuted (key 16a + 4g + j at 8g + 4a + j) to
@@ -57,6 +62,7 @@ struct ExpandEpi {
   uint16_t* vt;
   int n_heads, seqlen;
   int64_t t_pad, n_rows, m0, b0;   // b0 = m0 / seqlen
+  float vdiv;                      // 2^-e_h of this tile's head
   __device__ bool transposed(int wn) const { return wn >= 2; }
   // (b, t) of token row m of this tile
   __device__ void locate(int64_t m, int64_t& b, int64_t& t) const {
@@ -78,12 +84,13 @@ struct ExpandEpi {
       *reinterpret_cast<uint2*>(knope + ((b * n_heads + h) * t_pad + t) * kNope + j) = u;
       return;
     }
-    // values: the bf16 Linear output, stored as f16 (exact for |v| < 65504) for the f16 P.V product
+    // values: the bf16 Linear output divided by 2^e_h (exact), stored as f16 -- exact below 65504,
+    // which the head's bound keeps them under -- for the f16 P.V product
     const int d = j - kNope;
     if ((t & 3) == 0 && t + 3 < seqlen) {   // four consecutive keys of one sequence, aligned
       uint2 u;
-      u.x = pack_f16x2(round_bf16(v[0]), round_bf16(v[1]));
-      u.y = pack_f16x2(round_bf16(v[2]), round_bf16(v[3]));
+      u.x = pack_f16x2(round_bf16(v[0]) * vdiv, round_bf16(v[1]) * vdiv);
+      u.y = pack_f16x2(round_bf16(v[2]) * vdiv, round_bf16(v[3]) * vdiv);
       *reinterpret_cast<uint2*>(vt + (b * n_heads + h) * kVDim * t_pad + vt_index(d, t)) = u;
       return;
     }
@@ -93,19 +100,98 @@ struct ExpandEpi {
       int64_t bb, tt;
       locate(m + e, bb, tt);
       vt[(bb * n_heads + h) * kVDim * t_pad + vt_index(d, tt)] =
-          static_cast<uint16_t>(pack_f16x2(round_bf16(v[e]), 0.f) & 0xFFFFu);
+          static_cast<uint16_t>(pack_f16x2(round_bf16(v[e]) * vdiv, 0.f) & 0xFFFFu);
     }
   }
 };
 
+// 2^-e as a float, e in [-100, 100].
+__device__ __forceinline__ float pow2_neg(int e) { return __uint_as_float(static_cast<uint32_t>(127 - e) << 23); }
+
+// Block h < n_heads: the largest row L1 norm of W_UV[h] (rows h*256 + 128 .. h*256 + 255 of
+// wkv_b). Block n_heads + s: max |latent| over its slot of the latent, the 8-element groups
+// s*256 + i + k*(256*kBoundSlots). Every slot and norm is written exactly once (no accumulation
+// across blocks).
+constexpr int kBoundSlots = 256;
+__global__ __launch_bounds__(256) void vbound_kernel(const uint16_t* __restrict__ lat, int64_t n_elems,
+                                                     const uint16_t* __restrict__ wkv_b, int n_heads,
+                                                     float* __restrict__ bound) {
+  __shared__ float red[256];
+  const int tid = threadIdx.x;
+  float m = 0.f;
+  if (static_cast<int>(blockIdx.x) < n_heads) {
+    // thread = (row 2 * (tid / 4) + {0, 1}, quarter tid % 4 of its 512 columns)
+    const int h = blockIdx.x;
+    for (int rr = 0; rr < 2; ++rr) {
+      const int row = 2 * (tid >> 2) + rr;
+      const uint16_t* w = wkv_b + (static_cast<int64_t>(h) * kKvRows + kNope + row) * kKvLora + (tid & 3) * 128;
+      float s = 0.f;
+#pragma unroll 4
+      for (int c = 0; c < 128; c += 8) {
+        const uint4 u = ldg16(w + c);
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) s += fabsf(bf16_bits_to_f32(wd[k] & 0xFFFFu)) + fabsf(bf16_bits_to_f32(wd[k] >> 16));
+      }
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);   // the row's sum over its four quarters
+      m = fmaxf(m, s);
+    }
+  } else {
+    const int64_t slot = blockIdx.x - n_heads, n_vec = n_elems / 8;   // rows of 512: whole groups
+#pragma unroll 4
+    for (int64_t i = slot * 256 + tid; i < n_vec; i += 256 * kBoundSlots) {
+      const uint4 u = ldg16(lat + i * 8);
+      const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        m = fmaxf(m, fmaxf(fabsf(bf16_bits_to_f32(wd[k] & 0xFFFFu)), fabsf(bf16_bits_to_f32(wd[k] >> 16))));
+    }
+  }
+  red[tid] = m;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
+    __syncthreads();
+  }
+  if (tid == 0) bound[blockIdx.x] = red[0];
+}
+
+// e_h = the e with b = (max |latent|) * (row L1 norm of W_UV[h]) * (1 + 2^-7) in [2^(14+e), 2^(15+e)):
+// the bf16-rounded values of head h, divided by 2^e_h, stay below 2^15 and thus inside fp16's range,
+// and values up to 2^29 times smaller than the bound stay above fp16's subnormals (where a bf16 value
+// would lose bits). A zero bound, or NaN or infinite inputs, give e_h = 0 (such values propagate as
+// they would without the division).
+__global__ __launch_bounds__(256) void vscale_kernel(const float* __restrict__ bound, int n_heads,
+                                                     int32_t* __restrict__ vexp) {
+  __shared__ float lmax_s;
+  const int tid = threadIdx.x;
+  float m = bound[n_heads + tid];   // kBoundSlots = 256 = blockDim.x
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float wred[4];
+  if ((tid & 63) == 0) wred[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) lmax_s = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
+  __syncthreads();
+  for (int h = tid; h < n_heads; h += 256) {
+    const float b = lmax_s * bound[h] * (1.f + 0.0078125f);
+    int e = 0;
+    if (b > 0.f && b <= 3.0e38f) {
+      e = static_cast<int>((__float_as_uint(b) >> 23) & 0xff) - 127 - 14;   // 2^(e+14) <= b < 2^(e+15)
+      e = e < -100 ? -100 : (e > 100 ? 100 : e);
+    }
+    vexp[h] = e;
+  }
+}
+
 __global__ __launch_bounds__(512, 1) void expand_kernel(const uint16_t* __restrict__ lat,
                                                         const uint16_t* __restrict__ wkv_b, int n_heads, int seqlen,
-                                                        int64_t t_pad, int64_t n_rows, uint16_t* __restrict__ knope,
-                                                        uint16_t* __restrict__ vt) {
+                                                        int64_t t_pad, int64_t n_rows, const int32_t* __restrict__ vexp,
+                                                        uint16_t* __restrict__ knope, uint16_t* __restrict__ vt) {
   __shared__ __attribute__((aligned(1024))) uint8_t stage[2 * gemm::kStageBytes];
   const int h = blockIdx.x % n_heads;
   const int64_t m0 = static_cast<int64_t>(blockIdx.x / n_heads) * gemm::kBM;
-  const ExpandEpi epi{knope, vt, n_heads, seqlen, t_pad, n_rows, m0, m0 / seqlen};
+  const ExpandEpi epi{knope, vt, n_heads, seqlen, t_pad, n_rows, m0, m0 / seqlen, pow2_neg(vexp[h])};
   gemm::nt_tile(wkv_b, static_cast<int64_t>(n_heads) * kKvRows, lat, n_rows, kKvLora, h * kKvRows, m0, 0, kKvLora,
                 stage, epi);
 }
@@ -150,7 +236,7 @@ __device__ __forceinline__ int swz_128(int row) { return (row >> 1) & 7; }
 __global__ __launch_bounds__(256, 2) void attend_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ knope, const uint16_t* __restrict__ vt,
     const uint16_t* __restrict__ k_pe, int batch, int n_heads, int q_len, int kv_len, int64_t t_pad,
-    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    const int32_t* __restrict__ vexp, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) uint8_t stage[2][kStage];
 
   const int n_qb = (q_len + kPQ - 1) / kPQ;
@@ -324,7 +410,8 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
     const float ltot = sum_over_rows(lsum[qh]);
     const int tq = q0 + 16 * qh + r;
     if (tq < q_len) {
-      const float inv = 1.f / ltot;
+      // normalised, and multiplied back by the power of two the stored values were divided by
+      const float inv = __uint_as_float(static_cast<uint32_t>(127 + vexp[h]) << 23) / ltot;
       uint16_t* dst = out + ((b * q_len + tq) * n_heads + h) * kVDim + grp * 4;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
@@ -346,7 +433,9 @@ PrefillLayout prefill_layout(int n_heads, int batch, int seqlen) {
   const size_t per = static_cast<size_t>(batch) * n_heads * static_cast<size_t>(L.t_pad) * 128 * sizeof(uint16_t);
   L.knope_off = 0;
   L.vt_off = align_up(per);
-  L.total = align_up(L.vt_off + per);
+  L.bound_off = align_up(L.vt_off + per);
+  L.vexp_off = align_up(L.bound_off + (static_cast<size_t>(n_heads) + kBoundSlots) * sizeof(float));
+  L.total = align_up(L.vexp_off + static_cast<size_t>(n_heads) * sizeof(int32_t));
   return L;
 }
 
@@ -365,16 +454,20 @@ hipError_t launch_prefill(int n_heads, int batch, int q_len, int kv_len, const u
     const int64_t n = rows * (lay.t_pad - seqlen);
     zero_vt_tail_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(vt, rows, seqlen, lay.t_pad);
   }
+  float* bound = reinterpret_cast<float*>(ws + lay.bound_off);
+  int32_t* vexp = reinterpret_cast<int32_t*>(ws + lay.vexp_off);
+  vbound_kernel<<<n_heads + kBoundSlots, 256, 0, stream>>>(kv_latent, n_rows * kKvLora, wkv_b, n_heads, bound);
+  vscale_kernel<<<1, 256, 0, stream>>>(bound, n_heads, vexp);
   const int64_t m_tiles = (n_rows + gemm::kBM - 1) / gemm::kBM;
   expand_kernel<<<static_cast<unsigned>(m_tiles * n_heads), 512, 0, stream>>>(kv_latent, wkv_b, n_heads, seqlen,
-                                                                              lay.t_pad, n_rows, knope, vt);
+                                                                              lay.t_pad, n_rows, vexp, knope, vt);
   mark(ev, 1, stream);
   {
     // blocks of one (b, h) on one XCD: grid = 8 x ceil(B H / 8) x query blocks
     const int64_t n_qb = (q_len + kPQ - 1) / kPQ;
     const int64_t n_bh8 = (static_cast<int64_t>(batch) * n_heads + 7) / 8;
     attend_kernel<<<static_cast<unsigned>(8 * n_bh8 * n_qb), 256, 0, stream>>>(
-        q, knope, vt, k_pe, batch, n_heads, q_len, kv_len, lay.t_pad, scale * kLog2e, out, lse);
+        q, knope, vt, k_pe, batch, n_heads, q_len, kv_len, lay.t_pad, vexp, scale * kLog2e, out, lse);
   }
   mark(ev, 2, stream);
   return hipGetLastError();

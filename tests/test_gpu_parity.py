@@ -276,6 +276,29 @@ def test_prefill_parity_small(H, B, T):
         assert_f32_parity(lse[b], lo, f"lse[b={b}]", magnitude=mag)
 
 
+@pytest.mark.parametrize("shift", [16, -20])
+def test_prefill_values_outside_fp16_range(shift):
+    """The expanded values are stored as f16 divided by a power of two per head, chosen from a
+    bound of what the head can produce: with the value half of wkv_b scaled by 2^shift the scores
+    are unchanged and the outputs 2^shift times larger -- for shift 16 past f16's largest finite
+    value, for -20 inside its subnormal range -- and must still meet the bar ("Kimi-K2 ·
+    value_states", mla-prefill: the values are kv_b_proj's bf16 output, of any size)."""
+    H, B, T = 32, 1, 200
+    say(f"prefill with the value half of wkv_b scaled by 2^{shift}")
+    case = S.PrefillCase("t", 470 + (shift > 0), H, B, T)
+    d = S.prefill_inputs(case, seed=6, with_q_latent=False)
+    q = S.prefill_query(case, seed=6)
+    w = O.bf16_decode(d["wkv_b"]).reshape(H, 256, 512)
+    w[:, 128:, :] *= 2.0 ** shift
+    wb = bits_of(w.reshape(H * 256, 512))
+    out, lse = _run_prefill(q, d["kv_latent"], d["k_pe"], wb, H)
+    qv = O.bf16_decode(q[0])
+    oo, lo = O.prefill_causal(qv, d["kv_latent"][0], d["k_pe"][0], wb, SCALE, round_output=False)
+    assert_bf16_parity(out[0], oo, "out")
+    mag = O.prefill_score_magnitude(qv, d["kv_latent"][0], d["k_pe"][0], wb, SCALE)
+    assert_f32_parity(lse[0], lo, "lse", magnitude=mag)
+
+
 @pytest.mark.slow
 def test_prefill_expansion_past_4gib_of_latent():
     """1025 sequences of 4096 positions at 16 heads: 4,198,400 latent rows (4.3 GB). The expansion
