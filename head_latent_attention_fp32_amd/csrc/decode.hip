@@ -631,21 +631,29 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
           y[tb * 4 + j] = (!mask || tb * 16 + j < valid) ? v : -INFINITY;
         }
     };
+    // The common part works on the raw scores: p = 2^(s c - m) as one fma and one exp per score
+    // (c = scale log2 e > 0), and the test against the reference on the raw maximum.
     auto softmax_common = [&](int t, const f32x4 (&sc)[2][2], bool mask) {
+      const int valid = sg.n_rows - t * kTileTok - 4 * grp;
       bool up = false;
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
-        float y[8], p[8];
-        scaled(t, sc, hb, mask, y);
-        const float ymax =
-            fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])), fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+        float x[8], p[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] = fast_exp2(y[i] - m_ref[hb]);
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            x[tb * 4 + j] = (!mask || tb * 16 + j < valid) ? sc[tb][hb][j] : -INFINITY;
+        const float xmax =
+            fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        const float nm = -m_ref[hb];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(x[i], c.scale_log2, nm));
         lsum_prev[hb] = lsum[hb];
         lsum[hb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         *reinterpret_cast<bf16x8*>(c.pbuf + (t & 1) * kPBytes + p_wr + hb * 256) = bf16x8_from_f32(p);
         c.alpha_s[t & 1][hl0 + 16 * hb] = 1.f;
-        up |= ymax > m_ref[hb] + 8.f;
+        up |= xmax * c.scale_log2 > m_ref[hb] + 8.f;
       }
       above = up;
     };
