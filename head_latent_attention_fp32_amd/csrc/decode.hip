@@ -193,21 +193,23 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
     return;
   }
 
-  // Block (h, 1 + slice): columns 64 slice .. +63 for every query. The queries go in groups of
-  // 16, loaded two groups ahead of their products; the first two before the weight slice.
+  // Block (h, 1 + slice): columns 64 slice .. +63 for every query. Wave w takes the query groups
+  // (16 queries each) w, w + 4, ...; a wave's first kAhead groups are loaded before the weight
+  // slice, so that their latency overlaps its load, and every later group kAhead products ahead.
   const int h = blockIdx.x;
   const int c0 = (blockIdx.y - 1) * 64;
   const int r = lane & 15, grp = lane >> 4;
-  constexpr int kAhead = 2;
+  const int n_grp = (batch + 15) / 16;
+  constexpr int kAhead = 4;
   uint4 qa[kAhead][4];
-  auto load_q = [&](int b0, uint4 (&dst)[4]) {
-    const uint16_t* qrow = q + (static_cast<int64_t>(min(b0 + r, batch - 1)) * n_heads + h) * kQk;
+  auto load_q = [&](int gi, uint4 (&dst)[4]) {
+    const uint16_t* qrow = q + (static_cast<int64_t>(min(16 * gi + r, batch - 1)) * n_heads + h) * kQk;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) dst[ks] = ldg16(qrow + ks * 32 + grp * 8);
   };
 #pragma unroll
   for (int i = 0; i < kAhead; ++i)
-    if (16 * i < batch) load_q(16 * i, qa[i]);
+    if (wave + 4 * i < n_grp) load_q(wave + 4 * i, qa[i]);
 
   // W_UK[h][0:128][c0:c0+64], row-major in LDS (rows kWrPitch bytes apart)
   const uint16_t* wk = wkv_b + static_cast<int64_t>(h) * kKvRows * kKvLora + c0;
@@ -218,35 +220,44 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
     *reinterpret_cast<uint4*>(wr + d * kWrPitch + ch * 16) = ldg16(wk + static_cast<int64_t>(d) * kKvLora + ch * 8);
   }
   __syncthreads();
+  if (wave >= n_grp) return;
 
-  // B operand of k-step ks: column c = 16 wave + r, rows d = 32 ks + 8 grp .. +7, by two
-  // transposing reads (rows +0..3 and +4..7 of the 16-column block)
-  bf16x8 bw[4];
+  // B operand of column block cb, k-step ks: column c = 16 cb + r, rows d = 32 ks + 8 grp .. +7,
+  // by two transposing reads (rows +0..3 and +4..7 of the 16-column block)
+  bf16x8 bw[4][4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const uint8_t* p = wr + (32 * ks + 8 * grp + (r >> 2)) * kWrPitch + (16 * wave + 4 * (r & 3)) * 2;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p + 4 * kWrPitch));
-    bw[ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  }
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint8_t* p = wr + (32 * ks + 8 * grp + (r >> 2)) * kWrPitch + (16 * cb + 4 * (r & 3)) * 2;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+      const i16x4 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p + 4 * kWrPitch));
+      bw[cb][ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
 
-  // q_lat^T = W_UK^T q^T for 16 columns x 16 queries: lane (r, grp) ends with columns
-  // 16 wave + 4 grp .. +3 of query b0 + r, stored as one 8-byte write
-  auto product = [&](int b0, const uint4 (&a)[4]) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // q_lat^T = W_UK^T q^T for the slice's 64 columns x 16 queries: lane (r, grp) ends with columns
+  // 16 cb + 4 grp .. +3 of query 16 gi + r (one 8-byte store per column block: 128 contiguous
+  // bytes of the query's row per wave)
+  auto product = [&](int gi, const uint4 (&a)[4]) {
+    const int b = 16 * gi + r;
+    uint16_t* dst = q_lat + (static_cast<int64_t>(b) * n_heads + h) * kKvLora + c0 + grp * 4;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(bw[ks], as_bf16x8(a[ks]), acc);
-    if (b0 + r < batch)
-      *reinterpret_cast<uint2*>(q_lat + (static_cast<int64_t>(b0 + r) * n_heads + h) * kKvLora + c0 + wave * 16 + grp * 4) =
-          make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+    for (int cb = 0; cb < 4; ++cb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(bw[cb][ks], as_bf16x8(a[ks]), acc);
+      if (b < batch)
+        *reinterpret_cast<uint2*>(dst + 16 * cb) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+    }
   };
-  for (int b0 = 0; b0 < batch; b0 += 16 * kAhead) {
+  for (int g0 = wave; g0 < n_grp; g0 += 4 * kAhead) {
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) {
-      const int b = b0 + 16 * i;
-      if (b < batch) {
-        product(b, qa[i]);
-        if (b + 16 * kAhead < batch) load_q(b + 16 * kAhead, qa[i]);
+      const int gi = g0 + 4 * i;
+      if (gi < n_grp) {
+        product(gi, qa[i]);
+        if (gi + 4 * kAhead < n_grp) load_q(gi + 4 * kAhead, qa[i]);
       }
     }
   }
@@ -899,6 +910,8 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(
 //    product per tile into the same accumulator (A: o_lat rows from LDS; B: W_UV rows 16 w ..
 //    16 w + 15 for wave w, from VGPRs). A sequence with no rows gets out = 0, lse = -inf.
 // ---------------------------------------------------------------------------------------------
+constexpr int kMergeAhead = 2;   // runs whose partial loads go out together
+
 __global__ __launch_bounds__(512, 4) void combine_proj_kernel(
     const Plan* __restrict__ plan, const int64_t* __restrict__ cum, int batch, int n_heads,
     const uint16_t* __restrict__ part_o, const float* __restrict__ part_s, const float* __restrict__ part_l,
@@ -944,25 +957,48 @@ __global__ __launch_bounds__(512, 4) void combine_proj_kernel(
     if (js < nseq) {
       const int64_t x0 = cum[b], x1 = cum[b + 1];
       if (x1 > x0) {
+        // One pass over the runs, kMergeAhead at a time: their loads go out together, then the running
+        // maximum M moves to cover them (the sums so far scaled by e^(M_old - M_new)).
         const int64_t g0 = run_of(x0, N, G) + part, g1 = run_of(x1 - 1, N, G);
-        for (int64_t g = g0; g <= g1; g += parts) M = fmaxf(M, part_l[(g + b) * n_heads + h]);
-        for (int64_t g = g0; g <= g1; g += parts) {
-          const int64_t slot = g + b;
-          const float w = __expf(part_l[slot * n_heads + h] - M);
-          wsum += w;
-          // fp16 partial times the inverse of its power-of-two factor (columns c0.. lie in the
-          // 128-column slice c0 / 128 of one attention wave)
-          const float ws = w * part_s[(slot * n_heads + h) * 4 + (c0 >> 7)];
-          const uint4* src = reinterpret_cast<const uint4*>(part_o + (slot * n_heads + h) * kKvLora + c0);
+        for (int64_t g = g0; g <= g1; g += kMergeAhead * parts) {
+          float l[kMergeAhead], s[kMergeAhead];
+          uint4 v[kMergeAhead][2];
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const uint4 v = src[i];
-            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+          for (int u = 0; u < kMergeAhead; ++u) {
+            const int64_t gg = g + u * parts;
+            const int64_t slot = (gg <= g1 ? gg : g) + b;
+            l[u] = part_l[slot * n_heads + h];
+            // factor of the 128-column slice c0 / 128 (one attention wave's columns)
+            s[u] = part_s[(slot * n_heads + h) * 4 + (c0 >> 7)];
+            const uint4* src = reinterpret_cast<const uint4*>(part_o + (slot * n_heads + h) * kKvLora + c0);
+            v[u][0] = src[0];
+            v[u][1] = src[1];
+          }
+          float mt = M;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const f32x2 f = unpack_f16x2(u[k]);
-              acc[8 * i + 2 * k] += ws * f[0];
-              acc[8 * i + 2 * k + 1] += ws * f[1];
+          for (int u = 0; u < kMergeAhead; ++u)
+            if (g + u * parts <= g1) mt = fmaxf(mt, l[u]);
+          const float a = M == -INFINITY ? 0.f : __expf(M - mt);
+          wsum *= a;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[i] *= a;
+          M = mt;
+#pragma unroll
+          for (int u = 0; u < kMergeAhead; ++u) {
+            if (g + u * parts > g1) continue;
+            const float w = __expf(l[u] - M);
+            wsum += w;
+            // fp16 partial times the inverse of its power-of-two factor
+            const float ws = w * s[u];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const uint32_t uu[4] = {v[u][i].x, v[u][i].y, v[u][i].z, v[u][i].w};
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                const f32x2 f = unpack_f16x2(uu[k]);
+                acc[8 * i + 2 * k] += ws * f[0];
+                acc[8 * i + 2 * k + 1] += ws * f[1];
+              }
             }
           }
         }
