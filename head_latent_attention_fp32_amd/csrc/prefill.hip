@@ -216,6 +216,8 @@ __global__ __launch_bounds__(256) void zero_vt_tail_kernel(uint16_t* __restrict_
 //    once for both 16-query halves; the online softmax in fp32 (log2 units, scale folded in; the
 //    accumulators are rescaled only when a query's maximum grows by more than 8); O^T (128 dims x
 //    32 queries) += V^T . P^T, 32 MFMAs, with P^T taken from the score accumulators in registers.
+//    Operand reads go out six ahead of their MFMAs, and the first value operands while the softmax
+//    runs, so that the LDS latency under eight waves' traffic stays behind the matrix pipe.
 //    LDS layouts (16-byte chunks): k_nope chunk c of key row r at c ^ 2(r&7); rotary key and V^T
 //    rows (128 B) chunk c of row r at c ^ ((r>>1)&7) -- every 128-bit operand read is free of bank
 //    conflicts under the two-pass service of a half-wave (lanes 0-7 with 24-31, lanes 8-23).
@@ -339,13 +341,24 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
     for (int kb = 0; kb < 4; ++kb) {
       s[0][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
       s[1][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // operand reads issued six ahead of their MFMAs (the scheduler otherwise places each read two
+    // MFMAs before its use, which leaves the LDS latency exposed)
 #pragma unroll
-      for (int ks = 0; ks < 6; ++ks) {
+    for (int ks = 0; ks < 6; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
         const bf16x8 a = ks < 4 ? lds_b128(st + kb * 16 * 256 + kn_rd[ks]) : lds_b128(st + kb * 16 * 128 + kp_rd[ks - 4]);
         s[0][kb] = mfma16x16x32(a, qf[0][ks], s[0][kb]);
         s[1][kb] = mfma16x16x32(a, qf[1][ks], s[1][kb]);
       }
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 18; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
     // causal and length mask on the tiles that reach past this wave's first query position
     if (k0 + kPK - 1 > p0 || k0 + kPK > kv_len) {
 #pragma unroll
@@ -360,6 +373,12 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
           }
       }
     }
+    // the first value operands, read while the softmax runs
+    constexpr int kVPre = 6;
+    f16x8 va[16];
+#pragma unroll
+    for (int i = 0; i < kVPre; ++i) va[i] = *reinterpret_cast<const f16x8*>(st + (i >> 1) * 16 * 128 + v_rd[i & 1]);
+    __builtin_amdgcn_sched_group_barrier(0x100, kVPre, 0);
     f16x8 pb[2][2];   // [query half][key group of 32]
     bool any_up = false;
     float alpha[2];
@@ -396,13 +415,21 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
         for (int db = 0; db < 8; ++db) o[qh][db] *= alpha[qh];
     }
 #pragma unroll
+    for (int i = kVPre; i < 16; ++i) va[i] = *reinterpret_cast<const f16x8*>(st + (i >> 1) * 16 * 128 + v_rd[i & 1]);
+#pragma unroll
     for (int db = 0; db < 8; ++db)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const f16x8 a = *reinterpret_cast<const f16x8*>(st + db * 16 * 128 + v_rd[ks]);
+        const f16x8 a = va[2 * db + ks];
         o[0][db] = mfma16x16x32_f16(a, pb[0][ks], o[0][db]);
         o[1][db] = mfma16x16x32_f16(a, pb[1][ks], o[1][db]);
       }
+#pragma unroll
+    for (int i = 0; i < 16 - kVPre; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kVPre, 0);
   }
 
 #pragma unroll

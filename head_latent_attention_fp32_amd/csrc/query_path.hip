@@ -103,7 +103,11 @@ __global__ __launch_bounds__(256) void normalize_kernel(const uint16_t* __restri
 // Ring step layout [32 k rows][16 NB columns], so that the 8 rows of a half-wave's transposing read
 // (two groups of 4 consecutive rows) fall into distinct 32-byte bank groups:
 //   NB = 4: 16-byte chunk c of row k at c ^ 2 gx(k), gx(k) = ((k >> 1) & 1) | (((k >> 3) & 1) << 1);
+//   NB = 6: 32-byte group g of row k at g ^ ((k >> 3) & 1) (192-byte rows: four consecutive rows
+//           start at four different quarters of the 256-byte bank line, and the flip moves rows
+//           8..11 to the other half of each quarter);
 //   NB = 8: 32-byte group g of row k at g ^ f(k), f(k) = (k & 3) | ((k >> 1) & 4).
+// With 128 heads, 96-column slices make exactly 256 of them: one per CU.
 // ---------------------------------------------------------------------------------------------
 constexpr int kSmallM = 32;          // largest token count of the small kernel
 constexpr int kWaveK = kQLora / 4;   // 384
@@ -111,19 +115,26 @@ constexpr int kSteps = kWaveK / 32;  // 12 k-steps per slice
 
 template <int NB>
 struct SmallCfg {
+  static_assert(NB == 4 || NB == 6 || NB == 8, "slices of 64, 96 or 128 columns");
   static constexpr int kCols = 16 * NB;                        // columns per slice
-  static constexpr int kRowBytes = kCols * 2;                  // 128 or 256
-  static constexpr int kStepBytes = 32 * kRowBytes;            // 4 or 8 KB
+  static constexpr int kRowBytes = kCols * 2;                  // 128, 192 or 256
+  static constexpr int kStepBytes = 32 * kRowBytes;            // 4, 6 or 8 KB
   static constexpr int kLoads = kStepBytes / 1024;             // loads per wave and step
-  static constexpr int kRing = NB == 4 ? 6 : 4;                // steps in a wave's ring
-  static constexpr int kRingBytes = 4 * kRing * kStepBytes;    // 96 or 128 KB
-  static constexpr int kRedBytes = 4 * 2 * NB * 64 * 16;       // 32 or 64 KB
-  static constexpr bool kOneSlice = NB == 8;                   // one slice per block, reduction in the ring
+  static constexpr int kRing = NB == 8 ? 4 : 6;                // steps in a wave's ring
+  static constexpr int kRingBytes = 4 * kRing * kStepBytes;    // 96, 144 or 128 KB
+  static constexpr int kRedBytes = 4 * 2 * NB * 64 * 16;       // 32, 48 or 64 KB
+  static constexpr bool kOneSlice = NB != 4;                   // one slice per block, reduction in the ring
   static constexpr int kLdsBytes = kOneSlice ? kRingBytes : kRingBytes + kRedBytes;
+  static_assert(!kOneSlice || kRedBytes <= kRingBytes, "the reduction reuses the ring");
 };
 
-// Slice t of XCD x's list: x, x + 8, x + 16, ...
-__device__ __forceinline__ int slice_of(int x, int t) { return x + 8 * t; }
+// Slice t of XCD x's list: x, x + 8, x + 16, ... For 96-column slices, whose 192-byte row pieces
+// share 128-byte lines with their neighbours, pairs of neighbours instead: 2 (x + 8 (t/2)) + t%2,
+// so that a line is fetched into one XCD's L2 only.
+template <int NB>
+__device__ __forceinline__ int slice_of(int x, int t) {
+  return NB == 6 ? 2 * (x + 8 * (t >> 1)) + (t & 1) : x + 8 * t;
+}
 __device__ __forceinline__ int gx(int k) { return ((k >> 1) & 1) | (((k >> 3) & 1) << 1); }
 __device__ __forceinline__ int wswz(int k) { return (k & 3) | ((k >> 1) & 4); }
 
@@ -160,6 +171,12 @@ __global__ __launch_bounds__(256, 1) void query_gemm_small_kernel(
       const int row = 8 * d + (lane >> 3);
       const int chunk = (lane & 7) ^ (2 * gx(row));
       w_voff[d] = static_cast<uint32_t>(row * n_cols * 2 + chunk * 16);
+    } else if constexpr (NB == 6) {
+      // LDS bytes 1024 d + 16 lane of the step: row P / 192, physical 16-byte chunk (P % 192) / 16
+      const int pos = 1024 * d + 16 * lane;
+      const int row = pos / 192, pc = (pos % 192) >> 4;
+      const int lc = (((pc >> 1) ^ ((row >> 3) & 1)) << 1) | (pc & 1);
+      w_voff[d] = static_cast<uint32_t>(row * n_cols * 2 + lc * 16);
     } else {
       const int row = 4 * d + (lane >> 4);
       const int pc = lane & 15;
@@ -168,7 +185,7 @@ __global__ __launch_bounds__(256, 1) void query_gemm_small_kernel(
     }
   }
   auto issue = [&](int g) {
-    const int sl = slice_of(xcd, i0 + per * (g / kSteps));
+    const int sl = slice_of<NB>(xcd, i0 + per * (g / kSteps));
     const uint32_t off = static_cast<uint32_t>(g % kSteps) * 32u * n_cols * 2u + sl * C::kRowBytes;
     const uint32_t dst = ring_lds + (g % C::kRing) * C::kStepBytes;
 #pragma unroll
@@ -238,6 +255,8 @@ __global__ __launch_bounds__(256, 1) void query_gemm_small_kernel(
       if constexpr (NB == 4) {
         const int c = 2 * nb + ((r & 3) >> 1);
         a_off[nb][h] = row * 128 + ((c ^ (2 * gx(row))) << 4) + 8 * (r & 1);
+      } else if constexpr (NB == 6) {
+        a_off[nb][h] = row * 192 + ((nb ^ ((row >> 3) & 1)) << 5) + 8 * (r & 3);
       } else {
         a_off[nb][h] = row * 256 + ((nb ^ wswz(row)) << 5) + 8 * (r & 3);
       }
@@ -280,7 +299,8 @@ __global__ __launch_bounds__(256, 1) void query_gemm_small_kernel(
         for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma16x16x32(af[nb], xf[mb][st], acc[nb][mb]);
     }
 
-    // Sum of the four waves' partials: wave w finalises n-blocks w NB/4 .. w NB/4 + NB/4 - 1.
+    // Sum of the four waves' partials: wave w finalises the (n-block, m-block) pairs p = nb 2 + mb
+    // in [w NB/2, w NB/2 + NB/2).
     if (C::kOneSlice) __syncthreads();   // every wave's ring reads are done before it is overwritten
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -290,33 +310,30 @@ __global__ __launch_bounds__(256, 1) void query_gemm_small_kernel(
         red[(wave * 2 * NB + nb * 2 + mb) * 64 + lane] = make_float4(v[0], v[1], v[2], v[3]);
       }
     __syncthreads();
-    constexpr int kOwn = NB / 4;   // n-blocks finalised per wave
-    float vv[kOwn][2][4];
+    constexpr int kOwn = NB / 2;   // pairs finalised per wave
+    float vv[kOwn][4];
 #pragma unroll
-    for (int o = 0; o < kOwn; ++o)
+    for (int o = 0; o < kOwn; ++o) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int e = 0; e < 4; ++e) vv[o][e] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vv[o][mb][e] = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float4 u = red[(w * 2 * NB + (wave * kOwn + o) * 2 + mb) * 64 + lane];
-          vv[o][mb][0] += u.x;
-          vv[o][mb][1] += u.y;
-          vv[o][mb][2] += u.z;
-          vv[o][mb][3] += u.w;
-        }
+      for (int w = 0; w < 4; ++w) {
+        const float4 u = red[(w * 2 * NB + wave * kOwn + o) * 64 + lane];
+        vv[o][0] += u.x;
+        vv[o][1] += u.y;
+        vv[o][2] += u.z;
+        vv[o][3] += u.w;
       }
+    }
     if (!C::kOneSlice) __syncthreads();   // red is rewritten for the next slice
 #pragma unroll
-    for (int o = 0; o < kOwn; ++o)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        // lane holds q[m][n .. n+3], m = 16 mb + r, n = slice start + 16 nb + 4 grp
-        float* v = vv[o][mb];
+    for (int o = 0; o < kOwn; ++o) {
+      {   // lane holds q[m][n .. n+3], m = 16 mb + r, n = slice start + 16 nb + 4 grp
+        const int pr = wave * kOwn + o, nb = pr >> 1, mb = pr & 1;
+        float* v = vv[o];
         const int m = 16 * mb + r;
         if (m < n_tokens) {
-          const int n = slice_of(xcd, i0 + per * j) * C::kCols + 16 * (wave * kOwn + o) + 4 * grp;
+          const int n = slice_of<NB>(xcd, i0 + per * j) * C::kCols + 16 * nb + 4 * grp;
           const int hd = n % kQk;
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = round_bf16(v[e]);   // bf16 Linear output
@@ -336,6 +353,7 @@ __global__ __launch_bounds__(256, 1) void query_gemm_small_kernel(
           *reinterpret_cast<uint2*>(q_out + static_cast<int64_t>(m) * n_cols + n) = u;
         }
       }
+    }
   }
 }
 
@@ -590,9 +608,13 @@ hipError_t launch_query_path(int n_heads, int64_t n_tokens, const uint16_t* q_la
   mark(ev, 0, stream);
   if (n_tokens <= kSmallM) {
     // one block per CU (at most one per slice); slice counts are multiples of 8, so every XCD has
-    // blocks. Slices of 128 columns when they do not outnumber the CUs (one per block), else 64.
+    // blocks. Slices of 96 columns when they make exactly one per CU (128 heads), else 128 columns
+    // when they do not outnumber the CUs and fill at least half of them (one per block), else 64.
     mark(ev, 1, stream);
-    if (n_cols / SmallCfg<8>::kCols <= 256 && n_cols / SmallCfg<8>::kCols >= 128) {
+    if (n_cols == 256 * SmallCfg<6>::kCols) {
+      query_gemm_small_kernel<6><<<256, 256, 0, stream>>>(q_latent, gamma, wq_b, rope_cs, static_cast<int>(n_tokens),
+                                                          n_cols, eps, inv_rms, q_out);
+    } else if (n_cols / SmallCfg<8>::kCols <= 256 && n_cols / SmallCfg<8>::kCols >= 128) {
       query_gemm_small_kernel<8><<<n_cols / SmallCfg<8>::kCols, 256, 0, stream>>>(
           q_latent, gamma, wq_b, rope_cs, static_cast<int>(n_tokens), n_cols, eps, inv_rms, q_out);
     } else {
