@@ -266,24 +266,76 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
 // ---------------------------------------------------------------------------------------------
 // 0. Top-k mode ("DeepSeek-V3.2-Exp · Attention update", mla-decode excerpt: the indexer's top-k
 //    positions of each sequence become a mask of 0 at those positions and -inf elsewhere, added to
-//    the scores). Block b keeps, in order, the entries of its list that name a position of the
-//    sequence (0 <= index < L_b) and counts them; the attention then runs over that many rows of
-//    sequence b, read through the compacted list. Entries outside [0, L_b) name nothing.
+//    the scores). The mask is a scatter, so a position the list names twice is still attended
+//    once. Block b keeps, in list order, the first entry for each position of the sequence
+//    (0 <= index < L_b) and counts them; the attention then runs over that many rows of sequence b,
+//    read through the compacted list. Entries outside [0, L_b) name nothing.
+//    First entries: an open-addressing table of `slots` (a power of two >= 2 k) per sequence, in
+//    LDS or the workspace, key = position, value = the lowest list index naming it (atomicMin), so
+//    that the survivor of a repeated position does not depend on the order of the atomics.
 // ---------------------------------------------------------------------------------------------
+constexpr int32_t kEmptySlot = -1;
+
+__device__ __forceinline__ uint32_t topk_hash(int32_t idx, int slots) {
+  return (static_cast<uint32_t>(idx) * 0x9E3779B1u) & static_cast<uint32_t>(slots - 1);
+}
+
+// Lists of up to kTopkLdsEntries entries keep their table in LDS (slots * 8 bytes, dynamic);
+// longer ones in the workspace, where the atomics go to L2.
+constexpr int kTopkLdsEntries = 2048;
+
+template <bool kLds>
 __global__ __launch_bounds__(256) void topk_compact_kernel(const int32_t* __restrict__ topk, int k,
                                                            const int32_t* __restrict__ seqlens, int64_t max_seqlen,
+                                                           int slots, int2* __restrict__ table,
                                                            int32_t* __restrict__ list, int32_t* __restrict__ counts) {
+  extern __shared__ int2 tab_lds[];
   __shared__ int wave_count[4];
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t L = min<int64_t>(max<int64_t>(seqlens[b], 0), max_seqlen);
   const int32_t* src = topk + static_cast<int64_t>(b) * k;
   int32_t* dst = list + static_cast<int64_t>(b) * k;
+  int2* tab = kLds ? tab_lds : table + static_cast<int64_t>(b) * slots;
+  const uint32_t mask = static_cast<uint32_t>(slots - 1);
+  // the table starts empty
+  for (int i = threadIdx.x; i < slots; i += 256) tab[i] = make_int2(kEmptySlot, 0x7fffffff);
+  if (!kLds) __threadfence();
+  __syncthreads();
+  // every valid entry claims its position's slot (or finds it claimed) and lowers its value
+  for (int j = threadIdx.x; j < k; j += 256) {
+    const int32_t idx = src[j];
+    if (idx < 0 || idx >= L) continue;
+    uint32_t h = topk_hash(idx, slots);
+    while (true) {
+      const int32_t prev = atomicCAS(&tab[h].x, kEmptySlot, idx);
+      if (prev == kEmptySlot || prev == idx) {
+        atomicMin(&tab[h].y, j);
+        break;
+      }
+      h = (h + 1) & mask;
+    }
+  }
+  if (!kLds) __threadfence();
+  __syncthreads();
+  // the entry survives iff it is the first naming its position (workspace table: read at device
+  // scope, since atomics wrote it in L2)
+  auto slot_key = [&](uint32_t h) {
+    return kLds ? tab[h].x : __hip_atomic_load(&tab[h].x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto slot_val = [&](uint32_t h) {
+    return kLds ? tab[h].y : __hip_atomic_load(&tab[h].y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
   int base = 0;
   for (int j0 = 0; j0 < k; j0 += 256) {
     const int j = j0 + static_cast<int>(threadIdx.x);
     const int32_t idx = j < k ? src[j] : -1;
-    const bool keep = idx >= 0 && idx < L;
+    bool keep = idx >= 0 && idx < L;
+    if (keep) {
+      uint32_t h = topk_hash(idx, slots);
+      while (slot_key(h) != idx) h = (h + 1) & mask;
+      keep = slot_val(h) == j;
+    }
     const uint64_t m = __ballot(keep);
     if (lane == 0) wave_count[wave] = __popcll(m);
     __syncthreads();
@@ -1107,12 +1159,20 @@ DecodeLayout decode_layout(int n_heads, int batch, int64_t max_seqlen, int topk)
   L.part_o_off = off; off = align_up(off + slots * H * kKvLora * sizeof(uint16_t));
   L.part_s_off = off; off = align_up(off + slots * H * 4 * sizeof(float));
   L.part_l_off = off; off = align_up(off + slots * H * sizeof(float));
-  L.list_off = L.count_off = 0;
+  L.list_off = L.count_off = L.table_off = 0;
+  L.topk_slots = 0;
   if (topk >= 0) {
     // 64 entries of slack: the attention's scalar loads of a last partial tile may read past a
     // sequence's count (those values are never used)
     L.list_off = off;  off = align_up(off + (B * static_cast<size_t>(topk) + 64) * sizeof(int32_t));
     L.count_off = off; off = align_up(off + B * sizeof(int32_t));
+    // first-entry table: a power of two >= 2 topk slots (at least 256) of 8 bytes per sequence
+    int64_t slots = 256;
+    while (slots < 2 * static_cast<int64_t>(topk)) slots *= 2;
+    L.topk_slots = static_cast<int>(slots);
+    // (in LDS instead for lists of up to kTopkLdsEntries entries)
+    L.table_off = off;
+    if (topk > kTopkLdsEntries) off = align_up(off + B * static_cast<size_t>(slots) * 8);
   }
   L.total = off;
   return L;
@@ -1138,7 +1198,15 @@ hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16
   int32_t* counts = sparse ? reinterpret_cast<int32_t*>(ws + lay.count_off) : nullptr;
 
   mark(ev, 0, stream);
-  if (sparse) topk_compact_kernel<<<batch, 256, 0, stream>>>(topk_indices, topk, seqlens, max_seqlen, list, counts);
+  if (sparse) {
+    int2* table = reinterpret_cast<int2*>(ws + lay.table_off);
+    if (topk <= kTopkLdsEntries)
+      topk_compact_kernel<true><<<batch, 256, static_cast<size_t>(lay.topk_slots) * sizeof(int2), stream>>>(
+          topk_indices, topk, seqlens, max_seqlen, lay.topk_slots, table, list, counts);
+    else
+      topk_compact_kernel<false><<<batch, 256, 0, stream>>>(topk_indices, topk, seqlens, max_seqlen, lay.topk_slots,
+                                                            table, list, counts);
+  }
   // the run plan covers the attended rows: L_b per sequence, or the count of its top-k positions
   absorb_plan_kernel<<<dim3(n_heads, 1 + kKvLora / 64), 256, 0, stream>>>(
       q, wkv_b, batch, n_heads, q_lat, sparse ? counts : seqlens, sparse ? topk : max_seqlen, lay.units,

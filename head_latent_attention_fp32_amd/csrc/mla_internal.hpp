@@ -23,7 +23,9 @@ inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a
 struct DecodeLayout {
   int units;            // workgroups launched for the split attention
   int min_unit_tokens;  // fewer tokens than this per run are not worth a partial
-  size_t plan_off, cum_off, runs_off, qlat_off, part_o_off, part_s_off, part_l_off, list_off, count_off, total;
+  int topk_slots;       // top-k mode: slots of each sequence's first-entry table
+  size_t plan_off, cum_off, runs_off, qlat_off, part_o_off, part_s_off, part_l_off, list_off, count_off, table_off,
+      total;
 };
 DecodeLayout decode_layout(int n_heads, int batch, int64_t max_seqlen, int topk = -1);
 

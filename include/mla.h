@@ -180,9 +180,10 @@ mla_status_t mla_decode_sparse_workspace_size(const mla_dims_t* dims, int32_t ba
  * mla_decode, over the rows of sequence b at the positions topk_indices[b, :] names:
  *   topk_indices  int32 [batch, topk], device: positions within sequence b (0-based, as cache rows
  *                 cache_row_offset[b] + position). Entries outside [0, L_b) name no position (e.g.
- *                 -1 padding of a list longer than the sequence). The positions of one list must be
- *                 distinct, as a top-k selection's are: a position listed twice is attended twice
- *                 (the mask of the excerpt would count it once).
+ *                 -1 padding of a list longer than the sequence). A position listed more than once
+ *                 is attended once, as the excerpt's scattered mask counts it (the first entry
+ *                 naming it is kept; for lists longer than 2048 entries the workspace holds a
+ *                 table of about 16 bytes per entry for finding first entries).
  *   topk          entries per list, 0 .. 2^21
  *   workspace     >= mla_decode_sparse_workspace_size(dims, batch, max_seqlen, topk) bytes
  * The order of a list does not matter beyond floating-point summation order. A sequence with no

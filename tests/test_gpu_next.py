@@ -263,6 +263,46 @@ def test_decode_sparse_empty_lists_and_full_lists():
     np.testing.assert_allclose(O.bf16_decode(out_s), O.bf16_decode(host_bits(out_d)), rtol=0, atol=0.05)
 
 
+@pytest.mark.parametrize("H,k", [(16, 64), (128, 300), (64, 3000)])
+def test_decode_sparse_repeated_positions(H, k):
+    """A position listed more than once is attended once ([AU] mla-decode: the index mask is a
+    scatter of 0 into -inf). Lists mix distinct positions, repeats of them, -1 and positions past
+    the sequence; the result matches the oracle's mask, and is bit-identical to the run on the same
+    lists with every repeat after the first replaced by -1 (the compacted lists are the same).
+    k = 3000 takes the first-entry table in the workspace, the others the one in LDS."""
+    lens = [97, 300, 1, 64, 0, 250]
+    say(f"decode_sparse repeated positions H={H} k={k}")
+    case = S.DecodeCase("t", 970 + H + k, H, np.array(lens, np.int32), layout="padded", max_seqlen=300)
+    d = S.decode_inputs(case, seed=13, with_q_latent=False)
+    q = S.decode_query(case, seed=13)
+    rng = np.random.default_rng(97 + k)
+    topk = np.full((len(lens), k), -1, np.int32)
+    for b, L in enumerate(lens):
+        if L == 0:
+            topk[b, : k // 2] = rng.integers(0, 5, k // 2)   # names nothing: the sequence is empty
+            continue
+        n = min(L, k // 3)
+        base = rng.choice(L, n, replace=False)
+        rep = rng.choice(base, k - n - 4)                      # repeats of listed positions
+        row = np.concatenate([base, rep, [-1, L, L + 7, -3]])
+        rng.shuffle(row)
+        topk[b] = row.astype(np.int32)
+    topk[2, :] = 0                                             # one position, listed k times
+    out, lse = _run_sparse(case, q, d, topk)
+    _check_sparse(case, q, d, topk, out, lse, list(range(case.batch)))
+    first = topk.copy()
+    for b in range(len(lens)):
+        seen = set()
+        for j, x in enumerate(first[b]):
+            if x in seen:
+                first[b, j] = -1
+            elif 0 <= x < lens[b]:
+                seen.add(int(x))
+    out1, lse1 = _run_sparse(case, q, d, first)
+    assert np.array_equal(out, out1), "repeats changed the result beyond dropping them"
+    assert np.array_equal(lse.view(np.uint32), lse1.view(np.uint32))
+
+
 @pytest.mark.slow
 def test_decode_sparse_config1_top2048_sampled():
     """32 sequences of 4096 cached positions, 2048 of them selected per sequence."""
