@@ -14,6 +14,12 @@
 // Orientation: normally the weight row is the MFMA A operand, so a lane ends with four consecutive
 // features of one token; an epilogue may ask a wave for the transposed product instead (token as A:
 // four consecutive tokens of one feature), chosen per wave.
+// Weights stored input x output instead (kWkn: W[k][n], n contiguous, row pitch w_pitch elements):
+// the weight part of a stage is [64 k][256 n], 512-byte rows whose 32-byte column group g sits at
+// g ^ wswz(k), wswz(k) = (k & 3) | ((k >> 1) & 4) (the 8 rows of a half-wave's transposing read, two
+// groups of 4 consecutive rows, then hit 8 distinct 32-byte bank groups), and the A operand (16
+// features x 8 consecutive k) comes from two ds_read_b64_tr_b16. Normal orientation only; the
+// tile's 256 features must all exist.
 #pragma once
 
 #include <type_traits>
@@ -28,6 +34,7 @@ constexpr int kStageBytes = (kBM + kBN) * kBK * 2;              // 64 KB
 constexpr int kIssuers = 4;                                     // waves 0-3 issue the loads
 constexpr int kLoadsPerWave = kStageBytes / 1024 / kIssuers;    // 16 loads of 1 KB per issuing wave and step
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int wswz(int k) { return (k & 3) | ((k >> 1) & 4); }
 
 // One block tile: features [n0, n0 + 256) of W (w_rows rows in all), tokens [m0, m0 + 256) of X
 // (x_rows rows), k in [k_begin, k_begin + k_len) (k_len a multiple of 64; rows are K elements).
@@ -35,10 +42,10 @@ __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 //   epi.store(m, n, v, false)  v = C[m][n .. n+3]      (normal orientation), or
 //   epi.store(m, n, v, true)   v = C[m .. m+3][n]      (when epi.transposed(wn) for the wave)
 // for tokens m < x_rows and features n < w_rows only.
-template <class Epi>
+template <bool kWkn = false, class Epi>
 __device__ __forceinline__ void nt_tile(const uint16_t* __restrict__ w, int64_t w_rows, const uint16_t* __restrict__ x,
                                         int64_t x_rows, int K, int n0, int64_t m0, int k_begin, int k_len,
-                                        uint8_t* stage, const Epi& epi) {
+                                        uint8_t* stage, const Epi& epi, int w_pitch = 0) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, grp = lane >> 4;
@@ -50,31 +57,42 @@ __device__ __forceinline__ void nt_tile(const uint16_t* __restrict__ w, int64_t 
   // clock) the other's MFMAs keep the matrix pipe busy. Lane l: row 8d' + l/8, physical chunk l%8
   // holding logical chunk (l%8) ^ swz(row).
   const bool issuer = wave < kIssuers;
+  // (kWkn: weight instruction d < 32 covers k rows 2d, 2d + 1 of 512 B; lane l: row 2d + l/32,
+  // physical 16-byte chunk l%32, i.e. 32-byte group (l%32)/2 holding logical group that ^ wswz(row))
   uint32_t voff[kLoadsPerWave];
 #pragma unroll
   for (int e = 0; e < kLoadsPerWave; ++e) {
     const int d = (wave & (kIssuers - 1)) + kIssuers * e;
-    const int row = 8 * (d & 31) + (lane >> 3);
-    voff[e] = static_cast<uint32_t>(row * K * 2 + (((lane & 7) ^ swz(row)) << 4));
+    if (kWkn && d < 32) {
+      const int row = 2 * d + (lane >> 5), pc = lane & 31;
+      const int lc = (((pc >> 1) ^ wswz(row)) << 1) | (pc & 1);
+      voff[e] = static_cast<uint32_t>(row * w_pitch * 2 + lc * 16);
+    } else {
+      const int row = 8 * (d & 31) + (lane >> 3);
+      voff[e] = static_cast<uint32_t>(row * K * 2 + (((lane & 7) ^ swz(row)) << 4));
+    }
   }
   const uint32_t st_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)stage));
   // Descriptor ranges: the rows this tile reads (at most 256 of each operand; rows past an operand's
   // end read as zeros), so that the 32-bit byte ranges stay below 4 GiB for any operand size
   // (256 rows x K x 2 B; K <= 16384 here).
+  // (kWkn: the K rows of the tile's 256 columns, K x w_pitch x 2 bytes from column n0)
   const int64_t w_left = w_rows - n0, x_left = x_rows - m0;
-  const uint32_t w_bytes = static_cast<uint32_t>((w_left < kBN ? w_left : kBN) * K * 2);
+  const uint32_t w_bytes = kWkn ? static_cast<uint32_t>(static_cast<int64_t>(K) * w_pitch * 2 - static_cast<int64_t>(n0) * 2)
+                                : static_cast<uint32_t>((w_left < kBN ? w_left : kBN) * K * 2);
   const uint32_t x_bytes = static_cast<uint32_t>((x_left < kBM ? x_left : kBM) * K * 2);
   auto issue = [&](int kt) {
     if (!issuer) return;
     // descriptors rebuilt per step (scalar work): short-lived, they stay in SGPRs
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + static_cast<int64_t>(n0) * K, w_bytes);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(kWkn ? w + n0 : w + static_cast<int64_t>(n0) * K, w_bytes);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + m0 * K, x_bytes);
     const uint32_t koff = static_cast<uint32_t>(k_begin + kt * kBK) * 2u;
+    const uint32_t wkoff = kWkn ? static_cast<uint32_t>(k_begin + kt * kBK) * static_cast<uint32_t>(w_pitch) * 2u : koff;
     const uint32_t dst = st_lds + (kt & 1) * kStageBytes;
 #pragma unroll
     for (int e = 0; e < kLoadsPerWave; ++e) {
       const int d = wave + kIssuers * e;
-      if (d < 32) dma16(rw, dst + d * 1024, voff[e] + koff);
+      if (d < 32) dma16(rw, dst + d * 1024, voff[e] + wkoff);
       else dma16(rx, dst + d * 1024, voff[e] + koff);
     }
   };
@@ -110,8 +128,23 @@ __device__ __forceinline__ void nt_tile(const uint16_t* __restrict__ w, int64_t 
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         bf16x8 af[4], bf[8];
+        if constexpr (kWkn) {
+          // k rows 32 ks + 8 grp + 4 h + r/4, features 16 (4 wn + nb) + 4 (r%4) .. +3
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) af[nb] = *reinterpret_cast<const bf16x8*>(st + a_off[ks] + nb * 16 * 128);
+          for (int nb = 0; nb < 4; ++nb) {
+            i16x4 half[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int row = 32 * ks + 8 * grp + 4 * h + (r >> 2);
+              const int byte = row * 512 + (((4 * wn + nb) ^ wswz(row)) << 5) + 8 * (r & 3);
+              half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(st + byte));
+            }
+            af[nb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) af[nb] = *reinterpret_cast<const bf16x8*>(st + a_off[ks] + nb * 16 * 128);
+        }
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb) bf[mb] = *reinterpret_cast<const bf16x8*>(st + b_off[ks] + mb * 16 * 128);
 #pragma unroll

@@ -38,12 +38,12 @@ struct PrefillLayout {
 };
 PrefillLayout prefill_layout(int n_heads, int batch, int seqlen);
 
-// Query path for more than 32 tokens: the normalised activation y [n][1536] bf16 and, when the
-// caller passes no inv_rms, the per-token statistics; for many tokens (large) also wq_b transposed
-// ([H*192][1536]). Empty for 32 tokens or fewer.
+// Query path for more than 32 tokens: the normalised activation y [n][1536] bf16 (row-major for
+// many tokens, `large`, else in the mid-size product's LDS-image order) and, when the caller passes
+// no inv_rms, the per-token statistics. Empty for 32 tokens or fewer.
 struct QueryLayout {
   bool large;
-  size_t y_off, wt_off, inv_off, total;
+  size_t y_off, inv_off, total;
 };
 QueryLayout query_layout(int n_heads, int64_t n_tokens);
 

@@ -513,36 +513,12 @@ __global__ __launch_bounds__(256, 1) void query_gemm_big_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// Large token counts (prefill, >= kNtTokens): wq_b is first transposed into the workspace
-// (wt[n][k], k contiguous), so that both operands of the product have k contiguous, and the tiled
-// product of gemm_nt.hpp (256 x 256 tiles, plain 128-bit operand reads) runs on wt and the
-// row-major y. The epilogue is the one above: bf16 rounding of the Linear output, RoPE of the
-// rotary pairs in registers, one 8-byte store per lane.
+// Large token counts (prefill, >= kNtTokens): the tiled product of gemm_nt.hpp (256 x 256 tiles)
+// on the row-major y and on wq_b as it is stored, its weight stages [64 k][256 n] read with the
+// transposing LDS read. The epilogue is the one above: bf16 rounding of the Linear output, RoPE of
+// the rotary pairs in registers, one 8-byte store per lane.
 // ---------------------------------------------------------------------------------------------
 constexpr int64_t kNtTokens = 1024;
-
-// wt[n][k] = wq_b[k][n], tiles of 64 k x 64 n through LDS.
-__global__ __launch_bounds__(256) void transpose_w_kernel(const uint16_t* __restrict__ w, int n_cols,
-                                                          uint16_t* __restrict__ wt) {
-  __shared__ __attribute__((aligned(16))) uint16_t t[64][64 + 8];
-  const int n0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = tid + 256 * i, k = idx >> 3, ch = idx & 7;
-    *reinterpret_cast<uint4*>(&t[k][ch * 8]) = ldg16(w + static_cast<int64_t>(k0 + k) * n_cols + n0 + ch * 8);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = tid + 256 * i, n = idx >> 3, kc = idx & 7;
-    uint32_t p[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      p[e] = static_cast<uint32_t>(t[kc * 8 + 2 * e][n]) | (static_cast<uint32_t>(t[kc * 8 + 2 * e + 1][n]) << 16);
-    *reinterpret_cast<uint4*>(wt + static_cast<int64_t>(n0 + n) * kQLora + k0 + kc * 8) = make_uint4(p[0], p[1], p[2], p[3]);
-  }
-}
 
 struct QueryEpi {
   const float* rope_cs;
@@ -570,7 +546,9 @@ struct QueryEpi {
   }
 };
 
-__global__ __launch_bounds__(512, 1) void query_gemm_nt_kernel(const uint16_t* __restrict__ wt,
+// wq_b read as it is stored (input x output): the product's weight operand through the transposing
+// LDS read (n_cols is a multiple of 256 for every supported head count).
+__global__ __launch_bounds__(512, 1) void query_gemm_nt_kernel(const uint16_t* __restrict__ wq_b,
                                                                const uint16_t* __restrict__ y,
                                                                const float* __restrict__ rope_cs, int64_t n_tokens,
                                                                int n_cols, uint16_t* __restrict__ q_out) {
@@ -579,7 +557,7 @@ __global__ __launch_bounds__(512, 1) void query_gemm_nt_kernel(const uint16_t* _
   const int nt = blockIdx.x % n_tiles;
   const int64_t mt = blockIdx.x / n_tiles;
   const QueryEpi epi{rope_cs, q_out, n_cols};
-  gemm::nt_tile(wt, n_cols, y, n_tokens, kQLora, nt * gemm::kBN, mt * gemm::kBM, 0, kQLora, stage, epi);
+  gemm::nt_tile<true>(wq_b, n_cols, y, n_tokens, kQLora, nt * gemm::kBN, mt * gemm::kBM, 0, kQLora, stage, epi, n_cols);
 }
 
 }  // namespace
@@ -590,8 +568,7 @@ QueryLayout query_layout(int n_heads, int64_t n_tokens) {
   if (n_tokens >= kNtTokens) {
     L.large = true;
     L.y_off = 0;
-    L.wt_off = align_up(static_cast<size_t>(n_tokens) * kQLora * sizeof(uint16_t));
-    L.inv_off = align_up(L.wt_off + static_cast<size_t>(n_heads) * kQk * kQLora * sizeof(uint16_t));
+    L.inv_off = align_up(static_cast<size_t>(n_tokens) * kQLora * sizeof(uint16_t));
   } else {
     const int64_t n_pad = y_tiles(n_tokens) * kYTile;
     L.y_off = 0;
@@ -628,13 +605,11 @@ hipError_t launch_query_path(int n_heads, int64_t n_tokens, const uint16_t* q_la
     uint16_t* y = reinterpret_cast<uint16_t*>(ws + lay.y_off);
     float* inv = inv_rms ? inv_rms : reinterpret_cast<float*>(ws + lay.inv_off);
     if (lay.large) {
-      uint16_t* wt = reinterpret_cast<uint16_t*>(ws + lay.wt_off);
-      transpose_w_kernel<<<dim3(n_cols / 64, kQLora / 64), 256, 0, stream>>>(wq_b, n_cols, wt);
       normalize_kernel<false><<<static_cast<unsigned>((n_tokens + 3) / 4), 256, 0, stream>>>(q_latent, gamma, n_tokens,
                                                                                             0, eps, inv, y);
       mark(ev, 1, stream);
       const int64_t blocks = static_cast<int64_t>(n_cols / gemm::kBN) * ((n_tokens + gemm::kBM - 1) / gemm::kBM);
-      query_gemm_nt_kernel<<<static_cast<unsigned>(blocks), 512, 0, stream>>>(wt, y, rope_cs, n_tokens, n_cols, q_out);
+      query_gemm_nt_kernel<<<static_cast<unsigned>(blocks), 512, 0, stream>>>(wq_b, y, rope_cs, n_tokens, n_cols, q_out);
     } else {
       const int64_t n_tiles = y_tiles(n_tokens);
       normalize_kernel<true><<<static_cast<unsigned>(n_tiles * kYTile / 4), 256, 0, stream>>>(q_latent, gamma, n_tokens,
