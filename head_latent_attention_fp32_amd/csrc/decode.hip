@@ -270,14 +270,66 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
 //    once. Block b keeps, in list order, the first entry for each position of the sequence
 //    (0 <= index < L_b) and counts them; the attention then runs over that many rows of sequence b,
 //    read through the compacted list. Entries outside [0, L_b) name nothing.
-//    First entries: an open-addressing table of `slots` (a power of two >= 2 k) per sequence, in
-//    LDS or the workspace, key = position, value = the lowest list index naming it (atomicMin), so
-//    that the survivor of a repeated position does not depend on the order of the atomics.
+//    Caches of up to kBitmapPositions positions (max_seqlen): a bitmap of the sequence's positions
+//    in LDS, one bit set per named position (a repeat sets it again), then a scan over its words
+//    writes the named positions in ascending order -- the attention then reads the cache rows
+//    front to back. Longer caches: an open-addressing table of `slots` (a power of two >= 2 k) per
+//    sequence, in LDS or the workspace, key = position, value = the lowest list index naming it
+//    (atomicMin), and the first entries in list order, so that neither the survivors nor their
+//    order depend on the order of the atomics.
 // ---------------------------------------------------------------------------------------------
 constexpr int32_t kEmptySlot = -1;
 
 __device__ __forceinline__ uint32_t topk_hash(int32_t idx, int slots) {
   return (static_cast<uint32_t>(idx) * 0x9E3779B1u) & static_cast<uint32_t>(slots - 1);
+}
+
+constexpr int kBitmapWords = 15360;                       // 60 KB of LDS
+constexpr int64_t kBitmapPositions = 32LL * kBitmapWords;   // 491,520 positions
+
+__global__ __launch_bounds__(256) void topk_bitmap_kernel(const int32_t* __restrict__ topk, int k,
+                                                          const int32_t* __restrict__ seqlens, int64_t max_seqlen,
+                                                          int32_t* __restrict__ list, int32_t* __restrict__ counts) {
+  extern __shared__ uint32_t bits[];
+  __shared__ int wave_total[4];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int L = static_cast<int>(min<int64_t>(max<int64_t>(seqlens[b], 0), max_seqlen));
+  const int32_t* src = topk + static_cast<int64_t>(b) * k;
+  int32_t* dst = list + static_cast<int64_t>(b) * k;
+  const int nw = (L + 31) >> 5;
+  for (int i = tid; i < nw; i += 256) bits[i] = 0u;
+  __syncthreads();
+  for (int j = tid; j < k; j += 256) {
+    const int32_t idx = src[j];
+    if (idx >= 0 && idx < L) atomicOr(&bits[idx >> 5], 1u << (idx & 31));
+  }
+  __syncthreads();
+  // thread t owns words [t per, t per + per): its count, the block's exclusive prefix of the counts
+  // (shuffles within a wave, then across the four waves through LDS), then its positions in order
+  const int per = (nw + 255) >> 8;
+  const int w0 = min(nw, tid * per), w1 = min(nw, w0 + per);
+  int cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __popc(bits[w]);
+  int incl = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += t;
+  }
+  if (lane == 63) wave_total[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wave_total[w];
+  int pos = base + incl - cnt;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t m = bits[w];
+    while (m) {
+      dst[pos++] = 32 * w + __ffs(m) - 1;
+      m &= m - 1;
+    }
+  }
+  if (tid == 255) counts[b] = base + incl;
 }
 
 // Lists of up to kTopkLdsEntries entries keep their table in LDS (slots * 8 bytes, dynamic);
@@ -1170,9 +1222,9 @@ DecodeLayout decode_layout(int n_heads, int batch, int64_t max_seqlen, int topk)
     int64_t slots = 256;
     while (slots < 2 * static_cast<int64_t>(topk)) slots *= 2;
     L.topk_slots = static_cast<int>(slots);
-    // (in LDS instead for lists of up to kTopkLdsEntries entries)
+    // (needed only beyond the bitmap's positions, and in LDS for lists of up to kTopkLdsEntries)
     L.table_off = off;
-    if (topk > kTopkLdsEntries) off = align_up(off + B * static_cast<size_t>(slots) * 8);
+    if (max_seqlen > kBitmapPositions && topk > kTopkLdsEntries) off = align_up(off + B * static_cast<size_t>(slots) * 8);
   }
   L.total = off;
   return L;
@@ -1200,7 +1252,10 @@ hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16
   mark(ev, 0, stream);
   if (sparse) {
     int2* table = reinterpret_cast<int2*>(ws + lay.table_off);
-    if (topk <= kTopkLdsEntries)
+    if (max_seqlen <= kBitmapPositions)
+      topk_bitmap_kernel<<<batch, 256, static_cast<size_t>((max_seqlen + 31) / 32) * sizeof(uint32_t), stream>>>(
+          topk_indices, topk, seqlens, max_seqlen, list, counts);
+    else if (topk <= kTopkLdsEntries)
       topk_compact_kernel<true><<<batch, 256, static_cast<size_t>(lay.topk_slots) * sizeof(int2), stream>>>(
           topk_indices, topk, seqlens, max_seqlen, lay.topk_slots, table, list, counts);
     else

@@ -181,9 +181,10 @@ mla_status_t mla_decode_sparse_workspace_size(const mla_dims_t* dims, int32_t ba
  *   topk_indices  int32 [batch, topk], device: positions within sequence b (0-based, as cache rows
  *                 cache_row_offset[b] + position). Entries outside [0, L_b) name no position (e.g.
  *                 -1 padding of a list longer than the sequence). A position listed more than once
- *                 is attended once, as the excerpt's scattered mask counts it (the first entry
- *                 naming it is kept; for lists longer than 2048 entries the workspace holds a
- *                 table of about 16 bytes per entry for finding first entries).
+ *                 is attended once, as the excerpt's scattered mask counts it. For max_seqlen up
+ *                 to 491,520 the named positions are attended in ascending order; beyond, in the
+ *                 order of their first entries (and for lists longer than 2048 entries the
+ *                 workspace then holds a table of about 16 bytes per entry).
  *   topk          entries per list, 0 .. 2^21
  *   workspace     >= mla_decode_sparse_workspace_size(dims, batch, max_seqlen, topk) bytes
  * The order of a list does not matter beyond floating-point summation order. A sequence with no

@@ -263,16 +263,19 @@ def test_decode_sparse_empty_lists_and_full_lists():
     np.testing.assert_allclose(O.bf16_decode(out_s), O.bf16_decode(host_bits(out_d)), rtol=0, atol=0.05)
 
 
-@pytest.mark.parametrize("H,k", [(16, 64), (128, 300), (64, 3000)])
-def test_decode_sparse_repeated_positions(H, k):
+@pytest.mark.parametrize("H,k,max_seqlen", [(16, 64, 300), (128, 300, 300), (64, 3000, 300), (16, 64, 600000),
+                                          (64, 3000, 600000)])
+def test_decode_sparse_repeated_positions(H, k, max_seqlen):
     """A position listed more than once is attended once ([AU] mla-decode: the index mask is a
     scatter of 0 into -inf). Lists mix distinct positions, repeats of them, -1 and positions past
     the sequence; the result matches the oracle's mask, and is bit-identical to the run on the same
     lists with every repeat after the first replaced by -1 (the compacted lists are the same).
-    k = 3000 takes the first-entry table in the workspace, the others the one in LDS."""
+    max_seqlen 300: the positions' bitmap; 600000 (packed caches, the same short sequences): the
+    first-entry table, in LDS for k = 64 and in the workspace for k = 3000."""
     lens = [97, 300, 1, 64, 0, 250]
-    say(f"decode_sparse repeated positions H={H} k={k}")
-    case = S.DecodeCase("t", 970 + H + k, H, np.array(lens, np.int32), layout="padded", max_seqlen=300)
+    say(f"decode_sparse repeated positions H={H} k={k} max_seqlen={max_seqlen}")
+    case = S.DecodeCase("t", 970 + H + k, H, np.array(lens, np.int32),
+                        layout="padded" if max_seqlen == 300 else "packed", max_seqlen=max_seqlen)
     d = S.decode_inputs(case, seed=13, with_q_latent=False)
     q = S.decode_query(case, seed=13)
     rng = np.random.default_rng(97 + k)
