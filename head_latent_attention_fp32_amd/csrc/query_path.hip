@@ -358,18 +358,25 @@ __global__ __launch_bounds__(256, 1) void query_gemm_small_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// Many tokens (prefill): large-tile MFMA GEMM on the normalised activation y (normalize_kernel),
-// q^T = W^T . y^T per block tile of BN output columns x BM tokens, 4 waves as 2 x 2, each wave
+// Mid-size token counts (33 .. 1023): large-tile MFMA GEMM on the normalised activation y
+// (normalize_kernel), q^T = W^T . y^T per block tile of BN output columns x BM tokens (BN = 96 at
+// 128 heads: 256 column tiles, one per CU; else 128), 4 waves as 2 x 2, each wave
 // (BN/2) x (BM/2). The W operand (the transposing read, half the LDS rate of a plain read) is reused
 // across the wave's BM/32 token blocks. K advances 64 at a time through three LDS stages (two in flight), filled
 // by direct-to-LDS loads, so the main loop holds no conversion work:
 //   W stage [64 k][BN] bf16: 32-byte column group g of row k at g ^ f(k), f(k) = (k & 3) |
-//     ((k >> 1) & 4), so the 8 rows of a half-wave's transposing read (ds_read_b64_tr_b16: 16
-//     columns x 8 consecutive k, the A operand) hit 8 distinct 32-byte bank groups;
+//     ((k >> 1) & 4) (BN = 96: (k >> 3) & 1), so the 8 rows of a half-wave's transposing read
+//     (ds_read_b64_tr_b16: 16 columns x 8 consecutive k, the A operand) hit 8 distinct 32-byte bank
+//     groups;
 //   Y stage [BM tokens][64 k] bf16: 16-byte chunk c of row m at c ^ ((m >> 1) & 7).
 // The epilogue rounds the Linear output to bf16 and rotates the rotary pairs in registers.
 // ---------------------------------------------------------------------------------------------
 constexpr int kBigStages = 3;   // LDS stages of 64 k; two in flight ahead of the one in use
+
+// W stage swizzle: 32-byte group g of row k at g ^ big_swz(k); 96-column (192-byte) rows flip
+// rows 8..15 of every 16 (the same reasoning as the small kernel's 96-column slices)
+template <int BN>
+__device__ __forceinline__ int big_swz(int k) { return BN == 96 ? (k >> 3) & 1 : wswz(k); }
 
 template <int BN, int BM>
 struct BigTile {
@@ -393,20 +400,22 @@ __global__ __launch_bounds__(256, 1) void query_gemm_big_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, grp = lane >> 4;
   const int wn = wave >> 1, wm = wave & 1;
-  const int n0 = blockIdx.x * BN;
+  // 96-column tiles (exactly 256 at 128 heads): neighbours, whose 192-byte row pieces share
+  // 128-byte lines, paired on one XCD as in the small kernel
+  const int nt = BN == 96 ? 2 * ((blockIdx.x & 7) + 8 * (blockIdx.x >> 4)) + ((blockIdx.x >> 3) & 1) : blockIdx.x;
+  const int n0 = nt * BN;
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
 
   // W loads: stage rows k0 .. k0+63, columns n0 .. n0+BN-1 of wq_b (row pitch n_cols); load li
   // covers 1 KB = 1024 / (2 BN) rows; lane l -> row, physical 16-byte chunk.
-  constexpr int kRowChunks = BN * 2 / 16;
-  constexpr int kRowsPerLoad = 1024 / (BN * 2);
   uint32_t w_voff[T::kWLoads];
 #pragma unroll
   for (int e = 0; e < T::kWLoads; ++e) {
     const int li = wave + 4 * e;
-    const int row = li * kRowsPerLoad + lane / kRowChunks;
-    const int pc = lane % kRowChunks;
-    const int lc = (((pc >> 1) ^ wswz(row)) << 1) | (pc & 1);
+    // byte 1024 li + 16 lane of the stage: row and physical 16-byte chunk
+    const int pos = 1024 * li + 16 * lane;
+    const int row = pos / (BN * 2), pc = (pos % (BN * 2)) >> 4;
+    const int lc = (((pc >> 1) ^ big_swz<BN>(row)) << 1) | (pc & 1);
     w_voff[e] = static_cast<uint32_t>(row * n_cols * 2 + lc * 16);
   }
   // Y loads: the block's BM tokens of a stage are BM / 128 consecutive tiles of the workspace
@@ -469,7 +478,7 @@ __global__ __launch_bounds__(256, 1) void query_gemm_big_kernel(
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int row = 32 * ks + 8 * grp + 4 * h + (r >> 2);
-          const int byte = row * (BN * 2) + ((g ^ wswz(row)) << 5) + 8 * (r & 3);
+          const int byte = row * (BN * 2) + ((g ^ big_swz<BN>(row)) << 5) + 8 * (r & 3);
           half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(wb + byte));
         }
         af[nb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
@@ -615,8 +624,14 @@ hipError_t launch_query_path(int n_heads, int64_t n_tokens, const uint16_t* q_la
       normalize_kernel<true><<<static_cast<unsigned>(n_tiles * kYTile / 4), 256, 0, stream>>>(q_latent, gamma, n_tokens,
                                                                                              n_tiles, eps, inv, y);
       mark(ev, 1, stream);
-      const dim3 grid(n_cols / 128, static_cast<unsigned>((n_tokens + 127) / 128));
-      query_gemm_big_kernel<128, 128><<<grid, 256, 0, stream>>>(y, wq_b, rope_cs, n_tokens, n_cols, q_out);
+      // 96-column tiles when they make exactly 256 (128 heads), else 128
+      if (n_cols == 256 * 96) {
+        const dim3 grid(256, static_cast<unsigned>((n_tokens + 127) / 128));
+        query_gemm_big_kernel<96, 128><<<grid, 256, 0, stream>>>(y, wq_b, rope_cs, n_tokens, n_cols, q_out);
+      } else {
+        const dim3 grid(n_cols / 128, static_cast<unsigned>((n_tokens + 127) / 128));
+        query_gemm_big_kernel<128, 128><<<grid, 256, 0, stream>>>(y, wq_b, rope_cs, n_tokens, n_cols, q_out);
+      }
     }
   }
   mark(ev, 2, stream);
