@@ -36,12 +36,20 @@ constexpr int kLoadsPerWave = kStageBytes / 1024 / kIssuers;    // 16 loads of 1
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int wswz(int k) { return (k & 3) | ((k >> 1) & 4); }
 
+template <class E, class = void>
+struct staged_epi : std::false_type {};
+template <class E>
+struct staged_epi<E, std::void_t<decltype(E::kStaged)>> : std::bool_constant<E::kStaged> {};
+
 // One block tile: features [n0, n0 + 256) of W (w_rows rows in all), tokens [m0, m0 + 256) of X
 // (x_rows rows), k in [k_begin, k_begin + k_len) (k_len a multiple of 64; rows are K elements).
 // At the end calls, per wave and 16 x 16 sub-tile,
 //   epi.store(m, n, v, false)  v = C[m][n .. n+3]      (normal orientation), or
 //   epi.store(m, n, v, true)   v = C[m .. m+3][n]      (when epi.transposed(wn) for the wave)
-// for tokens m < x_rows and features n < w_rows only.
+// for tokens m < x_rows and features n < w_rows only. An epilogue with kStaged = true may instead
+// take the whole tile through LDS when epi.can_stage() holds (the same for the whole block): after
+// the last step's reads, epi.stage_store(lds, ml, nl, v, tr) with tile-local ml, nl, a barrier, then
+// epi.copy_out(lds) by all threads; `stage` must then hold what the epilogue stages.
 template <bool kWkn = false, class Epi>
 __device__ __forceinline__ void nt_tile(const uint16_t* __restrict__ w, int64_t w_rows, const uint16_t* __restrict__ x,
                                         int64_t x_rows, int K, int n0, int64_t m0, int k_begin, int k_len,
@@ -157,6 +165,22 @@ __device__ __forceinline__ void nt_tile(const uint16_t* __restrict__ w, int64_t 
   };
   if (tr) run(std::true_type{});
   else run(std::false_type{});
+
+  if constexpr (staged_epi<Epi>::value) {
+    if (epi.can_stage()) {
+      __syncthreads();   // every wave's operand reads of the last stage are done
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          if (!tr) epi.stage_store(stage, 128 * wm + 16 * mb + r, 64 * wn + 16 * nb + 4 * grp, acc[nb][mb], false);
+          else epi.stage_store(stage, 128 * wm + 16 * mb + 4 * grp, 64 * wn + 16 * nb + r, acc[nb][mb], true);
+        }
+      __syncthreads();
+      epi.copy_out(stage);
+      return;
+    }
+  }
 
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb)

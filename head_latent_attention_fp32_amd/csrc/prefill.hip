@@ -60,10 +60,60 @@ __device__ __forceinline__ int64_t vt_index(int d, int64_t t) {
 struct ExpandEpi {
   uint16_t* knope;
   uint16_t* vt;
-  int n_heads, seqlen;
+  int n_heads, seqlen, h;          // h: this tile's head
   int64_t t_pad, n_rows, m0, b0;   // b0 = m0 / seqlen
   float vdiv;                      // 2^-e_h of this tile's head
   __device__ bool transposed(int wn) const { return wn >= 2; }
+
+  // Through LDS, when the tile's 256 tokens are positions t0 .. t0 + 255 of one sequence with t0 a
+  // multiple of 64 (every tile when seqlen is a multiple of 256): k_nope staged as [256 tokens]
+  // [128 features] bf16 (16-byte chunk c of token row m at c ^ (m & 15), so that the 16 tokens of a
+  // lane group write 16 distinct bank groups), the values as [128 features][4 key tiles][64 keys]
+  // f16 in the key order of the attention's V^T tiles, rows of 512 bytes at a pitch of 528 (16
+  // features then start at 16 distinct bank groups); then both copied out in 16-byte pieces along
+  // their destination rows (256 bytes per token of k_nope, one 16 KB V^T tile after another).
+  static constexpr bool kStaged = true;
+  static constexpr int kKnStage = 256 * kNope * 2;             // 65536
+  static constexpr int kVPitch = 64 * 4 * 2 + 16;              // 528
+  static constexpr int kLdsBytes = kKnStage + kVDim * kVPitch; // 133120
+  __device__ bool can_stage() const {
+    const int64_t t0 = m0 - b0 * seqlen;
+    return seqlen % 64 == 0 && m0 + 256 <= n_rows && t0 + 256 <= seqlen;
+  }
+  __device__ void stage_store(uint8_t* lds, int ml, int nl, f32x4 v, bool tr) const {
+    if (!tr) {
+      const int c = nl >> 3;
+      uint2 u;
+      u.x = pack_bf16x2(v[0], v[1]);
+      u.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(lds + ml * 256 + ((c ^ (ml & 15)) << 4) + 8 * ((nl >> 2) & 1)) = u;
+      return;
+    }
+    const int d = nl - kNope;
+    uint2 u;
+    u.x = pack_f16x2(round_bf16(v[0]) * vdiv, round_bf16(v[1]) * vdiv);
+    u.y = pack_f16x2(round_bf16(v[2]) * vdiv, round_bf16(v[3]) * vdiv);
+    *reinterpret_cast<uint2*>(lds + kKnStage + d * kVPitch + (ml >> 6) * 128 + (vt_pos(ml) & 63) * 2) = u;
+  }
+  __device__ void copy_out(const uint8_t* lds) const {
+    const int tid = threadIdx.x;
+    const int64_t t0 = m0 - b0 * seqlen;
+    uint16_t* kn = knope + ((b0 * n_heads + h) * t_pad + t0) * kNope;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = tid + 512 * i, m = q >> 4, c = q & 15;
+      *reinterpret_cast<uint4*>(kn + m * kNope + 8 * c) =
+          *reinterpret_cast<const uint4*>(lds + m * 256 + ((c ^ (m & 15)) << 4));
+    }
+    // V^T tiles t0/64 .. t0/64 + 3 of (b0, h): [128 features][64 keys] each, one after another
+    uint16_t* v0 = vt + (b0 * n_heads + h) * kVDim * t_pad + (t0 >> 6) * kVDim * 64;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = tid + 512 * i, kt = q >> 10, d = (q >> 3) & 127, c = q & 7;
+      *reinterpret_cast<uint4*>(v0 + (kt * kVDim + d) * 64 + 8 * c) =
+          *reinterpret_cast<const uint4*>(lds + kKnStage + d * kVPitch + kt * 128 + 16 * c);
+    }
+  }
   // (b, t) of token row m of this tile
   __device__ void locate(int64_t m, int64_t& b, int64_t& t) const {
     b = b0;
@@ -188,10 +238,11 @@ __global__ __launch_bounds__(512, 1) void expand_kernel(const uint16_t* __restri
                                                         const uint16_t* __restrict__ wkv_b, int n_heads, int seqlen,
                                                         int64_t t_pad, int64_t n_rows, const int32_t* __restrict__ vexp,
                                                         uint16_t* __restrict__ knope, uint16_t* __restrict__ vt) {
-  __shared__ __attribute__((aligned(1024))) uint8_t stage[2 * gemm::kStageBytes];
+  static_assert(ExpandEpi::kLdsBytes >= 2 * gemm::kStageBytes, "the staged epilogue's LDS holds the stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t stage[ExpandEpi::kLdsBytes];
   const int h = blockIdx.x % n_heads;
   const int64_t m0 = static_cast<int64_t>(blockIdx.x / n_heads) * gemm::kBM;
-  const ExpandEpi epi{knope, vt, n_heads, seqlen, t_pad, n_rows, m0, m0 / seqlen, pow2_neg(vexp[h])};
+  const ExpandEpi epi{knope, vt, n_heads, seqlen, h, t_pad, n_rows, m0, m0 / seqlen, pow2_neg(vexp[h])};
   gemm::nt_tile(wkv_b, static_cast<int64_t>(n_heads) * kKvRows, lat, n_rows, kKvLora, h * kKvRows, m0, 0, kKvLora,
                 stage, epi);
 }
