@@ -533,8 +533,11 @@ struct QueryEpi {
   const float* rope_cs;
   uint16_t* q_out;
   int n_cols;
+  int64_t n_tokens, m0;
+  int n0;
   __device__ bool transposed(int) const { return false; }
-  __device__ void store(int64_t m, int n, f32x4 acc, bool) const {
+  // Final values of q[m][n .. n+3]: the bf16 Linear output, rotary pairs rotated, packed.
+  __device__ uint2 finish(int64_t m, int n, f32x4 acc) const {
     const int hd = n % kQk;
     float v[4];
 #pragma unroll
@@ -551,7 +554,29 @@ struct QueryEpi {
     uint2 u;
     u.x = pack_bf16x2(v[0], v[1]);
     u.y = pack_bf16x2(v[2], v[3]);
-    *reinterpret_cast<uint2*>(q_out + m * n_cols + n) = u;
+    return u;
+  }
+  // A whole 256 x 256 tile goes out through LDS: [256 tokens][256 features] bf16 (the two 64 KB
+  // stages), 16-byte chunk c of token row m at c ^ (m & 15), so that the 16 tokens of a lane group
+  // write 16 distinct bank groups; then each token's 512 bytes are copied out in 16-byte pieces.
+  static constexpr bool kStaged = true;
+  __device__ bool can_stage() const { return m0 + 256 <= n_tokens; }
+  __device__ void stage_store(uint8_t* lds, int ml, int nl, f32x4 acc, bool) const {
+    const int c = nl >> 3;
+    *reinterpret_cast<uint2*>(lds + ml * 512 + ((c ^ (ml & 15)) << 4) + 8 * ((nl >> 2) & 1)) =
+        finish(m0 + ml, n0 + nl, acc);
+  }
+  __device__ void copy_out(const uint8_t* lds) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int q = tid + 512 * i, m = q >> 5, c = q & 31;
+      *reinterpret_cast<uint4*>(q_out + (m0 + m) * n_cols + n0 + 8 * c) =
+          *reinterpret_cast<const uint4*>(lds + m * 512 + ((c ^ (m & 15)) << 4));
+    }
+  }
+  __device__ void store(int64_t m, int n, f32x4 acc, bool) const {
+    *reinterpret_cast<uint2*>(q_out + m * n_cols + n) = finish(m, n, acc);
   }
 };
 
@@ -565,7 +590,7 @@ __global__ __launch_bounds__(512, 1) void query_gemm_nt_kernel(const uint16_t* _
   const int n_tiles = n_cols / gemm::kBN;
   const int nt = blockIdx.x % n_tiles;
   const int64_t mt = blockIdx.x / n_tiles;
-  const QueryEpi epi{rope_cs, q_out, n_cols};
+  const QueryEpi epi{rope_cs, q_out, n_cols, n_tokens, mt * gemm::kBM, nt * gemm::kBN};
   gemm::nt_tile<true>(wq_b, n_cols, y, n_tokens, kQLora, nt * gemm::kBN, mt * gemm::kBM, 0, kQLora, stage, epi, n_cols);
 }
 
