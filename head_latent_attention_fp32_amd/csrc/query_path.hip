@@ -8,9 +8,10 @@
 // The GEMM is computed transposed, q^T[n][m] = sum_k wq_b[k][n] y[m][k]: weight columns n are the
 // MFMA rows, so every lane ends with four consecutive output columns of one token -- both halves
 // of two rotary pairs -- and RoPE runs in registers in the epilogue. wq_b is stored input x
-// output (n contiguous), so its tiles are transposed into LDS ([n][k]) on the way in; the
-// activation tile is normalised, multiplied by the gain and rounded to bf16 on the way in,
-// which keeps the rounding point of the RMSNorm excerpt ahead of the product.
+// output (n contiguous): its tiles go to LDS as stored ([k][n]) and the transposing LDS read
+// (ds_read_b64_tr_b16) gives the MFMA operand, eight consecutive k per lane. The activation is
+// normalised, multiplied by the gain and rounded to bf16 before the product, which keeps the
+// rounding point of the RMSNorm excerpt ahead of it.
 #include "gemm_nt.hpp"
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
