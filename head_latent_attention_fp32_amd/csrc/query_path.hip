@@ -111,19 +111,22 @@ __global__ __launch_bounds__(256) void normalize_kernel(const uint16_t* __restri
 // With 128 heads, 96-column slices make exactly 256 of them: one per CU.
 // ---------------------------------------------------------------------------------------------
 constexpr int kSmallM = 32;          // largest token count of the small kernel
-constexpr int kWaveK = kQLora / 4;   // 384
-constexpr int kSteps = kWaveK / 32;  // 12 k-steps per slice
 
-template <int NB>
+// NW waves per block, each owning kQLora / NW rows of K (4 waves: 384 rows in 12 steps of 32;
+// 8 waves: 192 rows in 6 steps), each with a ring of kRing steps.
+template <int NB, int NW>
 struct SmallCfg {
   static_assert(NB == 4 || NB == 6 || NB == 8, "slices of 64, 96 or 128 columns");
+  static_assert(NW == 4 || (NW == 8 && NB != 4), "8 waves only with one slice per block");
+  static constexpr int kWaveK = kQLora / NW;                   // 384 or 192
+  static constexpr int kSteps = kWaveK / 32;                   // 12 or 6 k-steps per slice
   static constexpr int kCols = 16 * NB;                        // columns per slice
   static constexpr int kRowBytes = kCols * 2;                  // 128, 192 or 256
   static constexpr int kStepBytes = 32 * kRowBytes;            // 4, 6 or 8 KB
   static constexpr int kLoads = kStepBytes / 1024;             // loads per wave and step
-  static constexpr int kRing = NB == 8 ? 4 : 6;                // steps in a wave's ring
-  static constexpr int kRingBytes = 4 * kRing * kStepBytes;    // 96, 144 or 128 KB
-  static constexpr int kRedBytes = 4 * 2 * NB * 64 * 16;       // 32, 48 or 64 KB
+  static constexpr int kRing = NW == 8 ? (NB == 8 ? 2 : 3) : (NB == 8 ? 4 : 6);   // steps in a wave's ring
+  static constexpr int kRingBytes = NW * kRing * kStepBytes;   // 96, 144 or 128 KB
+  static constexpr int kRedBytes = NW * 2 * NB * 64 * 16;      // NW x 2 NB KB
   static constexpr bool kOneSlice = NB != 4;                   // one slice per block, reduction in the ring
   static constexpr int kLdsBytes = kOneSlice ? kRingBytes : kRingBytes + kRedBytes;
   static_assert(!kOneSlice || kRedBytes <= kRingBytes, "the reduction reuses the ring");
@@ -139,15 +142,16 @@ __device__ __forceinline__ int slice_of(int x, int t) {
 __device__ __forceinline__ int gx(int k) { return ((k >> 1) & 1) | (((k >> 3) & 1) << 1); }
 __device__ __forceinline__ int wswz(int k) { return (k & 3) | ((k >> 1) & 4); }
 
-template <int NB>
-__global__ __launch_bounds__(256, 1) void query_gemm_small_kernel(
+template <int NB, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void query_gemm_small_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ gamma, const uint16_t* __restrict__ wq_b,
     const float* __restrict__ rope_cs, int n_tokens, int n_cols, float eps, float* __restrict__ inv_rms,
     uint16_t* __restrict__ q_out) {
-  using C = SmallCfg<NB>;
+  using C = SmallCfg<NB, NW>;
+  constexpr int kWaveK = C::kWaveK, kSteps = C::kSteps;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLdsBytes];
-  __shared__ float ss_s[4][kSmallM];
-  float4* red = reinterpret_cast<float4*>(lds + (C::kOneSlice ? 0 : C::kRingBytes));   // [4][2 NB][64]
+  __shared__ float ss_s[NW][kSmallM];
+  float4* red = reinterpret_cast<float4*>(lds + (C::kOneSlice ? 0 : C::kRingBytes));   // [NW][2 NB][64]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -159,8 +163,8 @@ __global__ __launch_bounds__(256, 1) void query_gemm_small_kernel(
   const int n_mine = i0 < list_len ? (list_len - i0 + per - 1) / per : 0;
   const int total_steps = n_mine * kSteps;
 
-  // Weight rows k0 .. k0 + 383 of the whole matrix through one descriptor; global step g is slice
-  // g / 12 of this block, k-step g % 12: kLoads loads of 1 KB (8 rows of 128 B or 4 rows of 256 B).
+  // Weight rows k0 .. k0 + kWaveK - 1 of the whole matrix through one descriptor; global step g is
+  // slice g / kSteps of this block, k-step g % kSteps: kLoads loads of 1 KB.
   const uint16_t* wbase = wq_b + static_cast<int64_t>(k0) * n_cols;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(wbase, static_cast<uint32_t>(kWaveK) * n_cols * 2u);
   uint8_t* ring = lds + wave * C::kRing * C::kStepBytes;
@@ -226,7 +230,8 @@ __global__ __launch_bounds__(256, 1) void query_gemm_small_kernel(
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     const int mm = 16 * mb + r;
-    const float t = (ss_s[0][mm] + ss_s[1][mm]) + (ss_s[2][mm] + ss_s[3][mm]);
+    float t = (ss_s[0][mm] + ss_s[1][mm]) + (ss_s[2][mm] + ss_s[3][mm]);
+    if constexpr (NW == 8) t += (ss_s[4][mm] + ss_s[5][mm]) + (ss_s[6][mm] + ss_s[7][mm]);
     inv[mb] = 1.f / sqrtf(t * (1.f / kQLora) + eps);
     if (inv_rms && blockIdx.x == 0 && wave == 0 && grp == 0 && mm < n_tokens) inv_rms[mm] = inv[mb];
   }
@@ -300,8 +305,8 @@ __global__ __launch_bounds__(256, 1) void query_gemm_small_kernel(
         for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma16x16x32(af[nb], xf[mb][st], acc[nb][mb]);
     }
 
-    // Sum of the four waves' partials: wave w finalises the (n-block, m-block) pairs p = nb 2 + mb
-    // in [w NB/2, w NB/2 + NB/2).
+    // Sum of the NW waves' partials (in wave order): wave w finalises the (n-block, m-block) pairs
+    // p = nb 2 + mb with p = w (mod NW).
     if (C::kOneSlice) __syncthreads();   // every wave's ring reads are done before it is overwritten
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -311,29 +316,32 @@ __global__ __launch_bounds__(256, 1) void query_gemm_small_kernel(
         red[(wave * 2 * NB + nb * 2 + mb) * 64 + lane] = make_float4(v[0], v[1], v[2], v[3]);
       }
     __syncthreads();
-    constexpr int kOwn = NB / 2;   // pairs finalised per wave
+    constexpr int kOwn = (2 * NB + NW - 1) / NW;   // pairs finalised per wave, at most
     float vv[kOwn][4];
 #pragma unroll
     for (int o = 0; o < kOwn; ++o) {
+      const int pr = wave + NW * o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) vv[o][e] = 0.f;
+      if (pr < 2 * NB) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float4 u = red[(w * 2 * NB + wave * kOwn + o) * 64 + lane];
-        vv[o][0] += u.x;
-        vv[o][1] += u.y;
-        vv[o][2] += u.z;
-        vv[o][3] += u.w;
+        for (int w = 0; w < NW; ++w) {
+          const float4 u = red[(w * 2 * NB + pr) * 64 + lane];
+          vv[o][0] += u.x;
+          vv[o][1] += u.y;
+          vv[o][2] += u.z;
+          vv[o][3] += u.w;
+        }
       }
     }
     if (!C::kOneSlice) __syncthreads();   // red is rewritten for the next slice
 #pragma unroll
     for (int o = 0; o < kOwn; ++o) {
       {   // lane holds q[m][n .. n+3], m = 16 mb + r, n = slice start + 16 nb + 4 grp
-        const int pr = wave * kOwn + o, nb = pr >> 1, mb = pr & 1;
+        const int pr = wave + NW * o, nb = pr >> 1, mb = pr & 1;
         float* v = vv[o];
         const int m = 16 * mb + r;
-        if (m < n_tokens) {
+        if (pr < 2 * NB && m < n_tokens) {
           const int n = slice_of<NB>(xcd, i0 + per * j) * C::kCols + 16 * nb + 4 * grp;
           const int hd = n % kQk;
 #pragma unroll
@@ -623,16 +631,16 @@ hipError_t launch_query_path(int n_heads, int64_t n_tokens, const uint16_t* q_la
     // blocks. Slices of 96 columns when they make exactly one per CU (128 heads), else 128 columns
     // when they do not outnumber the CUs and fill at least half of them (one per block), else 64.
     mark(ev, 1, stream);
-    if (n_cols == 256 * SmallCfg<6>::kCols) {
-      query_gemm_small_kernel<6><<<256, 256, 0, stream>>>(q_latent, gamma, wq_b, rope_cs, static_cast<int>(n_tokens),
-                                                          n_cols, eps, inv_rms, q_out);
-    } else if (n_cols / SmallCfg<8>::kCols <= 256 && n_cols / SmallCfg<8>::kCols >= 128) {
-      query_gemm_small_kernel<8><<<n_cols / SmallCfg<8>::kCols, 256, 0, stream>>>(
+    if (n_cols == 256 * SmallCfg<6, 8>::kCols) {
+      query_gemm_small_kernel<6, 8><<<256, 512, 0, stream>>>(q_latent, gamma, wq_b, rope_cs,
+                                                             static_cast<int>(n_tokens), n_cols, eps, inv_rms, q_out);
+    } else if (n_cols / SmallCfg<8, 4>::kCols <= 256 && n_cols / SmallCfg<8, 4>::kCols >= 128) {
+      query_gemm_small_kernel<8, 4><<<n_cols / SmallCfg<8, 4>::kCols, 256, 0, stream>>>(
           q_latent, gamma, wq_b, rope_cs, static_cast<int>(n_tokens), n_cols, eps, inv_rms, q_out);
     } else {
-      const int n_slices = n_cols / SmallCfg<4>::kCols;
+      const int n_slices = n_cols / SmallCfg<4, 4>::kCols;
       const int grid = n_slices < 256 ? n_slices : 256;
-      query_gemm_small_kernel<4><<<grid, 256, 0, stream>>>(q_latent, gamma, wq_b, rope_cs,
+      query_gemm_small_kernel<4, 4><<<grid, 256, 0, stream>>>(q_latent, gamma, wq_b, rope_cs,
                                                            static_cast<int>(n_tokens), n_cols, eps, inv_rms, q_out);
     }
   } else {
