@@ -261,10 +261,11 @@ def _run_prefill(q_bits, lat, kpe, w, H):
 
 
 @pytest.mark.parametrize("H,B,T", [(16, 1, 1), (16, 2, 5), (64, 1, 64), (32, 1, 65), (128, 1, 130),
-                                   (64, 3, 200), (16, 1, 257), (16, 2, 384), (64, 1, 512)])
+                                   (64, 3, 200), (16, 1, 257), (16, 2, 384), (64, 1, 512), (32, 2, 512)])
 def test_prefill_parity_small(H, B, T):
     """(16, 2, 384): expansion tiles of 256 tokens inside one sequence (through LDS) and one across
-    the boundary (direct stores); (64, 1, 512): every tile through LDS."""
+    the boundary (direct stores); (64, 1, 512) and (32, 2, 512): every tile through LDS, in one and
+    in two sequences."""
     say(f"prefill H={H} B={B} T={T}")
     case = S.PrefillCase("t", 400 + H + T + B, H, B, T)
     d = S.prefill_inputs(case, seed=4, with_q_latent=False)
