@@ -45,8 +45,12 @@ def _run_query(x, g, w, cs, H, with_inv=True):
 
 @pytest.mark.parametrize("H,n,with_inv", [(16, 1, True), (64, 1, True), (128, 1, True), (128, 5, False),
                                           (128, 32, True), (64, 32, False), (16, 32, True), (128, 33, True),
-                                          (128, 64, True), (64, 67, True), (32, 130, False), (128, 200, True)])
+                                          (128, 64, True), (64, 67, True), (32, 130, False), (128, 200, True),
+                                          (16, 1100, True), (32, 1024, False)])
 def test_query_path_parity(H, n, with_inv):
+    """Every path of the product: n <= 32 (activation in registers), 33..1023 (mid-size tiles),
+    >= 1024 (256 x 256 tiles on wq_b as stored; full tiles through LDS, a partial last tile at
+    1100 tokens through direct stores)."""
     say(f"query_path H={H} n={n} inv={with_inv}")
     x, g, w, cs = _query_case(H, n, 0, 200 + H + n)
     qg, inv = _run_query(x, g, w, cs, H, with_inv)
