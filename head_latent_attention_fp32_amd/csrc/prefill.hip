@@ -385,6 +385,10 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
     lds_barrier();                                               // everyone's; stage kt-1 free
     if (kt + 1 < n_kt) issue(kt + 1);
     const uint8_t* st = &stage[kt & 1][0];
+    // Matrix phases run at a raised wave priority and the softmax at the base one, so that of the
+    // two blocks on a CU the one in its matrix phase keeps the matrix pipe while the other's
+    // softmax fills the vector ALU (about 1% on the 4096-token shape).
+    __builtin_amdgcn_s_setprio(1);
     const int k0 = kt * kPK;
 
     f32x4 s[2][4];   // [query half][key block]
@@ -410,6 +414,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+    __builtin_amdgcn_s_setprio(0);
     // causal and length mask on the tiles that reach past this wave's first query position
     if (k0 + kPK - 1 > p0 || k0 + kPK > kv_len) {
 #pragma unroll
@@ -465,6 +470,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[qh][db] *= alpha[qh];
     }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = kVPre; i < 16; ++i) va[i] = *reinterpret_cast<const f16x8*>(st + (i >> 1) * 16 * 128 + v_rd[i & 1]);
 #pragma unroll
