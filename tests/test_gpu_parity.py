@@ -148,7 +148,7 @@ def _many_lengths(B, mod, zero_every):
 
 
 @pytest.mark.parametrize("H,B,layout", [(16, 300, "packed"), (64, 300, "padded"), (16, 1000, "padded"),
-                                        (64, 1000, "packed")])
+                                        (64, 1000, "packed"), (128, 300, "packed")])
 def test_decode_parity_many_sequences(H, B, layout):
     """More than 256 sequences: the run plan takes its chunked branch (each plan thread owns a
     contiguous chunk of sequences, prefix sums across the chunks, run start records stepped within
