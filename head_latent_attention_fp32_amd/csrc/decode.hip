@@ -1179,7 +1179,7 @@ __global__ __launch_bounds__(512, 4) void combine_proj_kernel(
 }  // namespace
 
 constexpr int kMergeBlocks = 512;
-constexpr int64_t kMinRunTokens = 64;
+constexpr int64_t kMinRunTokens = 32;
 
 DecodeLayout decode_layout(int n_heads, int batch, int64_t max_seqlen, int topk) {
   DecodeLayout L{};
