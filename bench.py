@@ -1,11 +1,13 @@
 """Benchmark of the MLA hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads 3,0,1,4] [--no-prefill]
-                    [--no-next] [--no-cpu] [--no-peaks]
+                    [--no-next] [--no-cpu] [--no-peaks] [--query-weights packed|stored]
 
-A step is one pass of the decode hot path over one batch of a decode workload: mla_query_path on
+A step is one pass of the decode hot path over one batch of a decode workload: the query path on
 the batch's new tokens, then mla_decode (absorb, split-KV attention, log-sum-exp combine, value
-projection). Inputs are synthetic (seeded) and resident in HBM before the timed region; workloads
+projection). The query path reads wq_b rearranged once by mla_wq_b_pack, as a model would do when
+it loads its weights (mla_query_path_packed; --query-weights stored times mla_query_path on wq_b as
+stored instead); the rearrangement is not part of a step. Inputs are synthetic (seeded) and resident in HBM before the timed region; workloads
 whose inputs fit the 256 MB Infinity Cache rotate copies of every input so that a step never finds
 the previous step's data there.
 
@@ -118,6 +120,13 @@ def decode_bench(args, torch, binding, S, workload):
     }
     for i in range(n_copies):
         sets.append({k: (v if i == 0 else v.clone()) for k, v in base.items()})
+    qpath = L.mla_query_path_ex
+    if args.query_weights == "packed":
+        # the query weights rearranged once, as at model load (mla_wq_b_pack), outside every timed step
+        for s_ in sets:
+            s_["wq_b"] = binding.wq_b_pack(s_["wq_b"], H)
+        qpath = L.mla_query_path_packed_ex
+        torch.cuda.synchronize()
     ws_bytes = binding.decode_workspace_size(H, B, int(case.max_seqlen))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     q = torch.empty((B, H, 192), dtype=torch.bfloat16, device="cuda")
@@ -142,9 +151,9 @@ def decode_bench(args, torch, binding, S, workload):
         s = sets[i % n_copies]
         eq = evq.ptr(3 * (i - W)) if (timed and all_stages) else None
         ed = (evd.ptr(4 * (i - W)) if all_stages else attn_ev[i - W]) if timed else None
-        st = L.mla_query_path_ex(ctypes.byref(dims), B, s["q_latent"].data_ptr(), s["gamma"].data_ptr(),
-                                 s["wq_b"].data_ptr(), s["rope_cs"].data_ptr(), q.data_ptr(), inv.data_ptr(),
-                                 qws_ptr, qws_bytes, stream, eq)
+        st = qpath(ctypes.byref(dims), B, s["q_latent"].data_ptr(), s["gamma"].data_ptr(),
+                   s["wq_b"].data_ptr(), s["rope_cs"].data_ptr(), q.data_ptr(), inv.data_ptr(),
+                   qws_ptr, qws_bytes, stream, eq)
         assert st == 0, st
         st = L.mla_decode_ex(ctypes.byref(dims), B, q.data_ptr(), s["wkv_b"].data_ptr(), s["kv"].data_ptr(),
                              s["pe"].data_ptr(), s["off"].data_ptr() if packed else None, s["lens"].data_ptr(),
@@ -153,6 +162,7 @@ def decode_bench(args, torch, binding, S, workload):
         assert st == 0, st
 
     L.mla_query_path_ex.argtypes = list(L.mla_query_path.argtypes) + [ctypes.POINTER(ctypes.c_void_p)]
+    L.mla_query_path_packed_ex.argtypes = list(L.mla_query_path.argtypes) + [ctypes.POINTER(ctypes.c_void_p)]
     L.mla_decode_ex.argtypes = list(L.mla_decode.argtypes) + [ctypes.POINTER(ctypes.c_void_p)]
     for i in range(W):
         step(i, False)
@@ -222,15 +232,21 @@ def prefill_bench(args, torch, binding, S, p):
     stream = torch.cuda.current_stream().cuda_stream
     L.mla_prefill_ex.argtypes = list(L.mla_prefill.argtypes) + [ctypes.POINTER(ctypes.c_void_p)]
     L.mla_query_path_ex.argtypes = list(L.mla_query_path.argtypes) + [ctypes.POINTER(ctypes.c_void_p)]
+    L.mla_query_path_packed_ex.argtypes = list(L.mla_query_path.argtypes) + [ctypes.POINTER(ctypes.c_void_p)]
+    qpath = L.mla_query_path_ex
+    if args.query_weights == "packed":
+        wq = binding.wq_b_pack(wq, H)
+        qpath = L.mla_query_path_packed_ex
+        torch.cuda.synchronize()
     K, W = max(3, args.steps // 4), 2
     evq, evp = HipEvents(3 * K), HipEvents(3 * K)
 
     def step(i, timed):
         eq = evq.ptr(3 * (i - W)) if timed else None
         ep = evp.ptr(3 * (i - W)) if timed else None
-        assert L.mla_query_path_ex(ctypes.byref(dims), B * T, xs.data_ptr(), g.data_ptr(), wq.data_ptr(),
-                                   cs.data_ptr(), q.data_ptr(), inv.data_ptr(), qws.data_ptr(), qws_bytes,
-                                   stream, eq) == 0
+        assert qpath(ctypes.byref(dims), B * T, xs.data_ptr(), g.data_ptr(), wq.data_ptr(),
+                     cs.data_ptr(), q.data_ptr(), inv.data_ptr(), qws.data_ptr(), qws_bytes,
+                     stream, eq) == 0
         assert L.mla_prefill_ex(ctypes.byref(dims), B, T, q.data_ptr(), lat.data_ptr(), kpe.data_ptr(),
                                 wkv.data_ptr(), ws.data_ptr(), ws_bytes, out.data_ptr(), None, stream, ep) == 0
 
@@ -635,6 +651,8 @@ def main():
     ap.add_argument("--sub-cpu-budget", type=float, default=3.0, help="oracle seconds for each other workload")
     ap.add_argument("--no-next", action="store_true", help="skip the steps next to the path")
     ap.add_argument("--next-cpu-budget", type=float, default=2.0, help="oracle seconds per next-row baseline")
+    ap.add_argument("--query-weights", choices=("packed", "stored"), default="packed",
+                    help="wq_b layout the query path reads: rearranged once by mla_wq_b_pack (default), or as stored")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -706,7 +724,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": head["workload"], "batch": head["batch"], "heads": head["heads"],
-                   "cached_tokens": head["cached_tokens"], "step": "mla_query_path + mla_decode",
+                   "cached_tokens": head["cached_tokens"],
+                   "step": ("mla_query_path_packed" if args.query_weights == "packed" else "mla_query_path")
+                           + " + mla_decode",
+                   "query_weights": args.query_weights,
                    "input_copies_rotated": head["input_copies_rotated"]},
         "hbm_gbps": head["hbm_gbps"],
         "decode_hbm_gbps": head["decode_hbm_gbps"],

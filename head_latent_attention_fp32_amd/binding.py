@@ -53,6 +53,8 @@ def _lib():
         lib.mla_dims_default.argtypes = [_I32, dp]
         lib.mla_query_path_workspace_size.argtypes = [dp, _I64, ctypes.POINTER(_SZ)]
         lib.mla_query_path.argtypes = [dp, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+        lib.mla_query_path_packed.argtypes = [dp, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+        lib.mla_wq_b_pack.argtypes = [dp, _P, _P, _P]
         lib.mla_decode_workspace_size.argtypes = [dp, _I32, _I64, ctypes.POINTER(_SZ)]
         lib.mla_decode.argtypes = [dp, _I32, _P, _P, _P, _P, _P, _P, _I64, _P, _SZ, _P, _P, _P]
         lib.mla_prefill_workspace_size.argtypes = [dp, _I32, _I32, ctypes.POINTER(_SZ)]
@@ -67,7 +69,8 @@ def _lib():
         for f in ("mla_dims_default", "mla_query_path_workspace_size", "mla_query_path", "mla_decode_workspace_size",
                   "mla_decode", "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_with_prefix",
                   "mla_kv_append", "mla_decode_sparse_workspace_size", "mla_decode_sparse",
-                  "mla_output_proj_workspace_size", "mla_output_proj", "mla_decode_noalloc"):
+                  "mla_output_proj_workspace_size", "mla_output_proj", "mla_decode_noalloc", "mla_wq_b_pack",
+                  "mla_query_path_packed"):
             getattr(lib, f).restype = ctypes.c_int
         lib.mla_status_string.argtypes = [ctypes.c_int]
         lib.mla_status_string.restype = ctypes.c_char_p
@@ -127,11 +130,26 @@ def query_path_workspace_size(n_heads: int, n_tokens: int, d: Optional[MlaDims] 
     return n.value
 
 
+def wq_b_pack(wq_b: torch.Tensor, n_heads: int, out: Optional[torch.Tensor] = None,
+              d: Optional[MlaDims] = None) -> torch.Tensor:
+    """wq_b bf16 [1536, H*192] -> the packed copy bf16 [H*192/32, 1536, 32] that query_path(...,
+    packed=True) reads (out[g, k, j] = wq_b[k, 32 g + j])."""
+    d = d or dims(n_heads)
+    _need(wq_b, "wq_b", torch.bfloat16, (Q_LORA, n_heads * QK))
+    shape = (n_heads * QK // 32, Q_LORA, 32)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=wq_b.device)
+    _need(out, "out", torch.bfloat16, shape)
+    _check(_lib().mla_wq_b_pack(ctypes.byref(d), _ptr(wq_b), _ptr(out), _stream()), "mla_wq_b_pack")
+    return out
+
+
 def query_path(q_latent: torch.Tensor, q_norm_w: torch.Tensor, wq_b: torch.Tensor, rope_cs: torch.Tensor,
                n_heads: int, q_out: Optional[torch.Tensor] = None, inv_rms: Optional[torch.Tensor] = None,
-               workspace: Optional[torch.Tensor] = None, d: Optional[MlaDims] = None
+               workspace: Optional[torch.Tensor] = None, d: Optional[MlaDims] = None, packed: bool = False
                ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """q_latent bf16 [n, 1536] (or [..., 1536]), q_norm_w fp32 [1536], wq_b bf16 [1536, H*192],
+    """q_latent bf16 [n, 1536] (or [..., 1536]), q_norm_w fp32 [1536], wq_b bf16 [1536, H*192]
+    (packed=True: the [H*192/32, 1536, 32] copy from wq_b_pack, through mla_query_path_packed),
     rope_cs fp32 [n, 32, 2] -> q_out bf16 [n, H, 192] (and inv_rms fp32 [n] if given). The workspace
     (uint8, needed above 32 tokens) is allocated when not given."""
     d = d or dims(n_heads)
@@ -143,7 +161,7 @@ def query_path(q_latent: torch.Tensor, q_norm_w: torch.Tensor, wq_b: torch.Tenso
     if q_latent.shape[-1] != Q_LORA:
         raise ValueError("q_latent last dim must be 1536")
     _need(q_norm_w, "q_norm_w", torch.float32, (Q_LORA,))
-    _need(wq_b, "wq_b", torch.bfloat16, (Q_LORA, n_heads * QK))
+    _need(wq_b, "wq_b", torch.bfloat16, (n_heads * QK // 32, Q_LORA, 32) if packed else (Q_LORA, n_heads * QK))
     _need(rope_cs, "rope_cs", torch.float32)
     if rope_cs.numel() != n * (ROPE // 2) * 2:
         raise ValueError("rope_cs must hold one (cos, sin) row of 32 pairs per token")
@@ -159,9 +177,10 @@ def query_path(q_latent: torch.Tensor, q_norm_w: torch.Tensor, wq_b: torch.Tenso
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q_latent.device)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8)
-    _check(_lib().mla_query_path(ctypes.byref(d), n, _ptr(q_latent), _ptr(q_norm_w), _ptr(wq_b), _ptr(rope_cs),
-                                 _ptr(q_out), _ptr(inv_rms), _ptr(workspace),
-                                 0 if workspace is None else workspace.numel(), _stream()), "mla_query_path")
+    fn = _lib().mla_query_path_packed if packed else _lib().mla_query_path
+    _check(fn(ctypes.byref(d), n, _ptr(q_latent), _ptr(q_norm_w), _ptr(wq_b), _ptr(rope_cs), _ptr(q_out),
+              _ptr(inv_rms), _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream()),
+           "mla_query_path_packed" if packed else "mla_query_path")
     return q_out, inv_rms
 
 

@@ -20,6 +20,9 @@
 // groups of 4 consecutive rows, then hit 8 distinct 32-byte bank groups), and the A operand (16
 // features x 8 consecutive k) comes from two ds_read_b64_tr_b16. Normal orientation only; the
 // tile's 256 features must all exist.
+// Weights stored input x output in 32-column groups instead (kWkn and kPacked: group g = columns
+// 32 g .. 32 g + 31, its K rows of 64 bytes back to back, groups one after another; see
+// packed_lane_off): the same LDS image, filled from the group runs.
 #pragma once
 
 #include <type_traits>
@@ -36,6 +39,13 @@ constexpr int kLoadsPerWave = kStageBytes / 1024 / kIssuers;    // 16 loads of 1
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int wswz(int k) { return (k & 3) | ((k >> 1) & 4); }
 
+// Packed input x output weights: [n / 32][K][32]. Byte offset, from the start of the group that
+// holds column n0 (n0 a multiple of 32), of the 16 bytes at row k, columns n0 + 8 c .. n0 + 8 c + 7.
+constexpr int kPackCols = 32;
+__device__ __forceinline__ uint32_t packed_lane_off(int K, int k, int c) {
+  return static_cast<uint32_t>((c >> 2) * K * (kPackCols * 2) + k * (kPackCols * 2) + (c & 3) * 16);
+}
+
 template <class E, class = void>
 struct staged_epi : std::false_type {};
 template <class E>
@@ -50,7 +60,7 @@ struct staged_epi<E, std::void_t<decltype(E::kStaged)>> : std::bool_constant<E::
 // take the whole tile through LDS when epi.can_stage() holds (the same for the whole block): after
 // the last step's reads, epi.stage_store(lds, ml, nl, v, tr) with tile-local ml, nl, a barrier, then
 // epi.copy_out(lds) by all threads; `stage` must then hold what the epilogue stages.
-template <bool kWkn = false, class Epi>
+template <bool kWkn = false, bool kPacked = false, class Epi>
 __device__ __forceinline__ void nt_tile(const uint16_t* __restrict__ w, int64_t w_rows, const uint16_t* __restrict__ x,
                                         int64_t x_rows, int K, int n0, int64_t m0, int k_begin, int k_len,
                                         uint8_t* stage, const Epi& epi, int w_pitch = 0) {
@@ -74,7 +84,7 @@ __device__ __forceinline__ void nt_tile(const uint16_t* __restrict__ w, int64_t 
     if (kWkn && d < 32) {
       const int row = 2 * d + (lane >> 5), pc = lane & 31;
       const int lc = (((pc >> 1) ^ wswz(row)) << 1) | (pc & 1);
-      voff[e] = static_cast<uint32_t>(row * w_pitch * 2 + lc * 16);
+      voff[e] = kPacked ? packed_lane_off(K, row, lc) : static_cast<uint32_t>(row * w_pitch * 2 + lc * 16);
     } else {
       const int row = 8 * (d & 31) + (lane >> 3);
       voff[e] = static_cast<uint32_t>(row * K * 2 + (((lane & 7) ^ swz(row)) << 4));
@@ -84,18 +94,24 @@ __device__ __forceinline__ void nt_tile(const uint16_t* __restrict__ w, int64_t 
   // Descriptor ranges: the rows this tile reads (at most 256 of each operand; rows past an operand's
   // end read as zeros), so that the 32-bit byte ranges stay below 4 GiB for any operand size
   // (256 rows x K x 2 B; K <= 16384 here).
-  // (kWkn: the K rows of the tile's 256 columns, K x w_pitch x 2 bytes from column n0)
+  // (kWkn: the K rows of the tile's 256 columns, K x w_pitch x 2 bytes from column n0; packed:
+  // the tile's eight column groups)
   const int64_t w_left = w_rows - n0, x_left = x_rows - m0;
-  const uint32_t w_bytes = kWkn ? static_cast<uint32_t>(static_cast<int64_t>(K) * w_pitch * 2 - static_cast<int64_t>(n0) * 2)
-                                : static_cast<uint32_t>((w_left < kBN ? w_left : kBN) * K * 2);
+  const uint32_t w_bytes =
+      kWkn ? (kPacked ? static_cast<uint32_t>(K) * (kBN * 2)
+                      : static_cast<uint32_t>(static_cast<int64_t>(K) * w_pitch * 2 - static_cast<int64_t>(n0) * 2))
+           : static_cast<uint32_t>((w_left < kBN ? w_left : kBN) * K * 2);
+  const uint16_t* w_tile = kWkn ? (kPacked ? w + static_cast<int64_t>(n0) * K : w + n0) : w + static_cast<int64_t>(n0) * K;
   const uint32_t x_bytes = static_cast<uint32_t>((x_left < kBM ? x_left : kBM) * K * 2);
   auto issue = [&](int kt) {
     if (!issuer) return;
     // descriptors rebuilt per step (scalar work): short-lived, they stay in SGPRs
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(kWkn ? w + n0 : w + static_cast<int64_t>(n0) * K, w_bytes);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_tile, w_bytes);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + m0 * K, x_bytes);
     const uint32_t koff = static_cast<uint32_t>(k_begin + kt * kBK) * 2u;
-    const uint32_t wkoff = kWkn ? static_cast<uint32_t>(k_begin + kt * kBK) * static_cast<uint32_t>(w_pitch) * 2u : koff;
+    const uint32_t wkoff = !kWkn ? koff
+                           : kPacked ? static_cast<uint32_t>(k_begin + kt * kBK) * (kPackCols * 2u)
+                                     : static_cast<uint32_t>(k_begin + kt * kBK) * static_cast<uint32_t>(w_pitch) * 2u;
     const uint32_t dst = st_lds + (kt & 1) * kStageBytes;
 #pragma unroll
     for (int e = 0; e < kLoadsPerWave; ++e) {

@@ -71,10 +71,14 @@ mla_status_t mla_query_path_workspace_size(const mla_dims_t* dims, int64_t n_tok
   return MLA_OK;
 }
 
-mla_status_t mla_query_path_ex(const mla_dims_t* dims, int64_t n_tokens, const uint16_t* q_latent,
-                               const float* q_norm_w, const uint16_t* wq_b, const float* rope_cs, uint16_t* q_out,
-                               float* inv_rms, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                               hipEvent_t* stage_events) {
+}  // extern "C"
+
+namespace {
+
+mla_status_t query_path_impl(const mla_dims_t* dims, int64_t n_tokens, const uint16_t* q_latent,
+                             const float* q_norm_w, const uint16_t* wq_b, bool packed, const float* rope_cs,
+                             uint16_t* q_out, float* inv_rms, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream, hipEvent_t* stage_events) {
   mla_status_t st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (n_tokens < 0 || n_tokens > kMaxTokens) return MLA_ERR_SHAPE;
@@ -86,16 +90,53 @@ mla_status_t mla_query_path_ex(const mla_dims_t* dims, int64_t n_tokens, const u
       !aligned16(q_out) || (inv_rms && !aligned16(inv_rms)) || (workspace && !aligned16(workspace)))
     return MLA_ERR_ALIGNMENT;
   if (workspace_bytes < lay.total) return MLA_ERR_WORKSPACE;
-  hipError_t e = mla::launch_query_path(dims->n_heads, n_tokens, q_latent, q_norm_w, wq_b, rope_cs, q_out, inv_rms,
-                                        workspace, lay, dims->rms_eps, stream, stage_events);
+  hipError_t e = mla::launch_query_path(dims->n_heads, n_tokens, q_latent, q_norm_w, wq_b, packed, rope_cs, q_out,
+                                        inv_rms, workspace, lay, dims->rms_eps, stream, stage_events);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_query_path_ex(const mla_dims_t* dims, int64_t n_tokens, const uint16_t* q_latent,
+                               const float* q_norm_w, const uint16_t* wq_b, const float* rope_cs, uint16_t* q_out,
+                               float* inv_rms, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                               hipEvent_t* stage_events) {
+  return query_path_impl(dims, n_tokens, q_latent, q_norm_w, wq_b, false, rope_cs, q_out, inv_rms, workspace,
+                         workspace_bytes, stream, stage_events);
 }
 
 mla_status_t mla_query_path(const mla_dims_t* dims, int64_t n_tokens, const uint16_t* q_latent,
                             const float* q_norm_w, const uint16_t* wq_b, const float* rope_cs, uint16_t* q_out,
                             float* inv_rms, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return mla_query_path_ex(dims, n_tokens, q_latent, q_norm_w, wq_b, rope_cs, q_out, inv_rms, workspace,
-                           workspace_bytes, stream, nullptr);
+  return query_path_impl(dims, n_tokens, q_latent, q_norm_w, wq_b, false, rope_cs, q_out, inv_rms, workspace,
+                         workspace_bytes, stream, nullptr);
+}
+
+mla_status_t mla_wq_b_pack(const mla_dims_t* dims, const uint16_t* wq_b, uint16_t* wq_b_packed, hipStream_t stream) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!wq_b || !wq_b_packed) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(wq_b) || !aligned16(wq_b_packed)) return MLA_ERR_ALIGNMENT;
+  hipError_t e = mla::launch_pack_wq_b(dims->n_heads, wq_b, wq_b_packed, stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_query_path_packed_ex(const mla_dims_t* dims, int64_t n_tokens, const uint16_t* q_latent,
+                                      const float* q_norm_w, const uint16_t* wq_b_packed, const float* rope_cs,
+                                      uint16_t* q_out, float* inv_rms, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream, hipEvent_t* stage_events) {
+  return query_path_impl(dims, n_tokens, q_latent, q_norm_w, wq_b_packed, true, rope_cs, q_out, inv_rms, workspace,
+                         workspace_bytes, stream, stage_events);
+}
+
+mla_status_t mla_query_path_packed(const mla_dims_t* dims, int64_t n_tokens, const uint16_t* q_latent,
+                                   const float* q_norm_w, const uint16_t* wq_b_packed, const float* rope_cs,
+                                   uint16_t* q_out, float* inv_rms, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  return query_path_impl(dims, n_tokens, q_latent, q_norm_w, wq_b_packed, true, rope_cs, q_out, inv_rms, workspace,
+                         workspace_bytes, stream, nullptr);
 }
 
 mla_status_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch, int64_t max_seqlen, size_t* bytes) {

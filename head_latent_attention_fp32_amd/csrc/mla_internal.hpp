@@ -47,10 +47,12 @@ struct QueryLayout {
 };
 QueryLayout query_layout(int n_heads, int64_t n_tokens);
 
+// wq_b as stored ([1536][H*192]) or, packed, in 32-column groups ([H*192/32][1536][32]).
 hipError_t launch_query_path(int n_heads, int64_t n_tokens, const uint16_t* q_latent, const float* gamma,
-                             const uint16_t* wq_b, const float* rope_cs, uint16_t* q_out, float* inv_rms,
-                             void* workspace, const QueryLayout& lay, float eps, hipStream_t stream,
+                             const uint16_t* wq_b, bool packed, const float* rope_cs, uint16_t* q_out,
+                             float* inv_rms, void* workspace, const QueryLayout& lay, float eps, hipStream_t stream,
                              hipEvent_t* ev);
+hipError_t launch_pack_wq_b(int n_heads, const uint16_t* wq_b, uint16_t* packed, hipStream_t stream);
 
 // Decode on a fixed device array instead of a caller workspace (for callers that cannot allocate):
 // its size, and the array's device address on the current device (looked up once per device).

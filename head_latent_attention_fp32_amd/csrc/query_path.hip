@@ -142,7 +142,7 @@ __device__ __forceinline__ int slice_of(int x, int t) {
 __device__ __forceinline__ int gx(int k) { return ((k >> 1) & 1) | (((k >> 3) & 1) << 1); }
 __device__ __forceinline__ int wswz(int k) { return (k & 3) | ((k >> 1) & 4); }
 
-template <int NB, int NW>
+template <int NB, int NW, bool kPacked>
 __global__ __launch_bounds__(64 * NW, 1) void query_gemm_small_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ gamma, const uint16_t* __restrict__ wq_b,
     const float* __restrict__ rope_cs, int n_tokens, int n_cols, float eps, float* __restrict__ inv_rms,
@@ -163,35 +163,41 @@ __global__ __launch_bounds__(64 * NW, 1) void query_gemm_small_kernel(
   const int n_mine = i0 < list_len ? (list_len - i0 + per - 1) / per : 0;
   const int total_steps = n_mine * kSteps;
 
-  // Weight rows k0 .. k0 + kWaveK - 1 of the whole matrix through one descriptor; global step g is
-  // slice g / kSteps of this block, k-step g % kSteps: kLoads loads of 1 KB.
-  const uint16_t* wbase = wq_b + static_cast<int64_t>(k0) * n_cols;
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wbase, static_cast<uint32_t>(kWaveK) * n_cols * 2u);
+  // Weight rows k0 .. k0 + kWaveK - 1 of the whole matrix through one descriptor (packed: the whole
+  // packed matrix); global step g is slice g / kSteps of this block, k-step g % kSteps: kLoads
+  // loads of 1 KB.
+  const uint16_t* wbase = kPacked ? wq_b : wq_b + static_cast<int64_t>(k0) * n_cols;
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(wbase, static_cast<uint32_t>(kPacked ? kQLora : kWaveK) * static_cast<uint32_t>(n_cols) * 2u);
   uint8_t* ring = lds + wave * C::kRing * C::kStepBytes;
   const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)ring));
   uint32_t w_voff[C::kLoads];
 #pragma unroll
   for (int d = 0; d < C::kLoads; ++d) {
+    // step row and logical 16-byte chunk (of the slice's row) that this lane's 16 bytes fill
+    int row, lc;
     if constexpr (NB == 4) {
-      const int row = 8 * d + (lane >> 3);
-      const int chunk = (lane & 7) ^ (2 * gx(row));
-      w_voff[d] = static_cast<uint32_t>(row * n_cols * 2 + chunk * 16);
+      row = 8 * d + (lane >> 3);
+      lc = (lane & 7) ^ (2 * gx(row));
     } else if constexpr (NB == 6) {
       // LDS bytes 1024 d + 16 lane of the step: row P / 192, physical 16-byte chunk (P % 192) / 16
       const int pos = 1024 * d + 16 * lane;
-      const int row = pos / 192, pc = (pos % 192) >> 4;
-      const int lc = (((pc >> 1) ^ ((row >> 3) & 1)) << 1) | (pc & 1);
-      w_voff[d] = static_cast<uint32_t>(row * n_cols * 2 + lc * 16);
+      row = pos / 192;
+      const int pc = (pos % 192) >> 4;
+      lc = (((pc >> 1) ^ ((row >> 3) & 1)) << 1) | (pc & 1);
     } else {
-      const int row = 4 * d + (lane >> 4);
+      row = 4 * d + (lane >> 4);
       const int pc = lane & 15;
-      const int lc = (((pc >> 1) ^ wswz(row)) << 1) | (pc & 1);
-      w_voff[d] = static_cast<uint32_t>(row * n_cols * 2 + lc * 16);
+      lc = (((pc >> 1) ^ wswz(row)) << 1) | (pc & 1);
     }
+    w_voff[d] = kPacked ? gemm::packed_lane_off(kQLora, row, lc) : static_cast<uint32_t>(row * n_cols * 2 + lc * 16);
   }
   auto issue = [&](int g) {
     const int sl = slice_of<NB>(xcd, i0 + per * (g / kSteps));
-    const uint32_t off = static_cast<uint32_t>(g % kSteps) * 32u * n_cols * 2u + sl * C::kRowBytes;
+    const uint32_t off =
+        kPacked ? static_cast<uint32_t>(sl * (C::kCols / gemm::kPackCols)) * (kQLora * gemm::kPackCols * 2u) +
+                      static_cast<uint32_t>(k0 + (g % kSteps) * 32) * (gemm::kPackCols * 2u)
+                : static_cast<uint32_t>(g % kSteps) * 32u * n_cols * 2u + sl * C::kRowBytes;
     const uint32_t dst = ring_lds + (g % C::kRing) * C::kStepBytes;
 #pragma unroll
     for (int d = 0; d < C::kLoads; ++d) dma16(rw, dst + d * 1024, w_voff[d] + off);
@@ -397,7 +403,7 @@ struct BigTile {
   static constexpr int kYLoads = kYBytes / 1024 / 4;
 };
 
-template <int BN, int BM>
+template <int BN, int BM, bool kPacked>
 __global__ __launch_bounds__(256, 1) void query_gemm_big_kernel(
     const uint16_t* __restrict__ y, const uint16_t* __restrict__ wq_b, const float* __restrict__ rope_cs,
     int64_t n_tokens, int n_cols, uint16_t* __restrict__ q_out) {
@@ -425,7 +431,7 @@ __global__ __launch_bounds__(256, 1) void query_gemm_big_kernel(
     const int pos = 1024 * li + 16 * lane;
     const int row = pos / (BN * 2), pc = (pos % (BN * 2)) >> 4;
     const int lc = (((pc >> 1) ^ big_swz<BN>(row)) << 1) | (pc & 1);
-    w_voff[e] = static_cast<uint32_t>(row * n_cols * 2 + lc * 16);
+    w_voff[e] = kPacked ? gemm::packed_lane_off(kQLora, row, lc) : static_cast<uint32_t>(row * n_cols * 2 + lc * 16);
   }
   // Y loads: the block's BM tokens of a stage are BM / 128 consecutive tiles of the workspace
   // (already in LDS order): contiguous 1 KB loads.
@@ -437,9 +443,12 @@ __global__ __launch_bounds__(256, 1) void query_gemm_big_kernel(
   const uint32_t y_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)&yst[0][0]));
   auto issue = [&](int kt) {
     // descriptors rebuilt per stage (scalar work): kept short-lived, they stay in SGPRs
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(wq_b + n0, static_cast<uint32_t>(kQLora) * n_cols * 2u);
+    // (packed: the tile's BN / 32 column groups)
+    const __amdgpu_buffer_rsrc_t rw =
+        kPacked ? make_rsrc(wq_b + static_cast<int64_t>(n0) * kQLora, static_cast<uint32_t>(kQLora) * BN * 2u)
+                : make_rsrc(wq_b + n0, static_cast<uint32_t>(kQLora) * n_cols * 2u);
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(y_blk, y_bytes);
-    const uint32_t wk = static_cast<uint32_t>(kt) * 64u * n_cols * 2u;
+    const uint32_t wk = static_cast<uint32_t>(kt) * 64u * (kPacked ? gemm::kPackCols * 2u : n_cols * 2u);
     const uint32_t yk = static_cast<uint32_t>(kt) * y_stage_pitch;
 #pragma unroll
     for (int e = 0; e < T::kWLoads; ++e)
@@ -589,8 +598,10 @@ struct QueryEpi {
   }
 };
 
-// wq_b read as it is stored (input x output): the product's weight operand through the transposing
-// LDS read (n_cols is a multiple of 256 for every supported head count).
+// wq_b read as it is stored (input x output), or packed in 32-column groups: the product's weight
+// operand through the transposing LDS read (n_cols is a multiple of 256 for every supported head
+// count).
+template <bool kPacked>
 __global__ __launch_bounds__(512, 1) void query_gemm_nt_kernel(const uint16_t* __restrict__ wq_b,
                                                                const uint16_t* __restrict__ y,
                                                                const float* __restrict__ rope_cs, int64_t n_tokens,
@@ -600,10 +611,36 @@ __global__ __launch_bounds__(512, 1) void query_gemm_nt_kernel(const uint16_t* _
   const int nt = blockIdx.x % n_tiles;
   const int64_t mt = blockIdx.x / n_tiles;
   const QueryEpi epi{rope_cs, q_out, n_cols, n_tokens, mt * gemm::kBM, nt * gemm::kBN};
-  gemm::nt_tile<true>(wq_b, n_cols, y, n_tokens, kQLora, nt * gemm::kBN, mt * gemm::kBM, 0, kQLora, stage, epi, n_cols);
+  gemm::nt_tile<true, kPacked>(wq_b, n_cols, y, n_tokens, kQLora, nt * gemm::kBN, mt * gemm::kBM, 0, kQLora, stage,
+                               epi, n_cols);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Packed weights: wq_b [1536][n_cols] (input x output) -> [n_cols / 32][1536][32], each group of 32
+// output columns with its 1536 rows of 64 bytes back to back. A column slice of the products above
+// (64, 96, 128 or 256 columns, always whole groups) then streams as a few contiguous runs of 96 KB
+// instead of 1536 pieces of 128-512 bytes spread over the 48 KB rows of the stored matrix, while
+// the LDS images, and so every product and its rounding, stay the same. One thread moves 16 bytes;
+// consecutive threads read consecutive pieces of a stored row.
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_wq_b_kernel(const uint16_t* __restrict__ wq_b, int n_cols,
+                                                        uint16_t* __restrict__ packed) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int pieces_per_row = n_cols / 8;
+  if (t >= static_cast<int64_t>(kQLora) * pieces_per_row) return;
+  const int k = static_cast<int>(t / pieces_per_row), c = static_cast<int>(t % pieces_per_row);
+  const uint4 v = ldg16(wq_b + static_cast<int64_t>(k) * n_cols + 8 * c);
+  *reinterpret_cast<uint4*>(packed + (static_cast<int64_t>(c >> 2) * kQLora + k) * gemm::kPackCols + 8 * (c & 3)) = v;
 }
 
 }  // namespace
+
+hipError_t launch_pack_wq_b(int n_heads, const uint16_t* wq_b, uint16_t* packed, hipStream_t stream) {
+  const int n_cols = n_heads * kQk;
+  const int64_t pieces = static_cast<int64_t>(kQLora) * (n_cols / 8);
+  pack_wq_b_kernel<<<static_cast<unsigned>((pieces + 255) / 256), 256, 0, stream>>>(wq_b, n_cols, packed);
+  return hipGetLastError();
+}
 
 QueryLayout query_layout(int n_heads, int64_t n_tokens) {
   QueryLayout L{};
@@ -621,9 +658,11 @@ QueryLayout query_layout(int n_heads, int64_t n_tokens) {
   return L;
 }
 
-hipError_t launch_query_path(int n_heads, int64_t n_tokens, const uint16_t* q_latent, const float* gamma,
-                             const uint16_t* wq_b, const float* rope_cs, uint16_t* q_out, float* inv_rms,
-                             void* workspace, const QueryLayout& lay, float eps, hipStream_t stream, hipEvent_t* ev) {
+template <bool kPacked>
+static void launch_query_kernels(int n_heads, int64_t n_tokens, const uint16_t* q_latent, const float* gamma,
+                                 const uint16_t* wq_b, const float* rope_cs, uint16_t* q_out, float* inv_rms,
+                                 void* workspace, const QueryLayout& lay, float eps, hipStream_t stream,
+                                 hipEvent_t* ev) {
   const int n_cols = n_heads * kQk;
   mark(ev, 0, stream);
   if (n_tokens <= kSmallM) {
@@ -632,16 +671,18 @@ hipError_t launch_query_path(int n_heads, int64_t n_tokens, const uint16_t* q_la
     // when they do not outnumber the CUs and fill at least half of them (one per block), else 64.
     mark(ev, 1, stream);
     if (n_cols == 256 * SmallCfg<6, 8>::kCols) {
-      query_gemm_small_kernel<6, 8><<<256, 512, 0, stream>>>(q_latent, gamma, wq_b, rope_cs,
-                                                             static_cast<int>(n_tokens), n_cols, eps, inv_rms, q_out);
+      query_gemm_small_kernel<6, 8, kPacked><<<256, 512, 0, stream>>>(q_latent, gamma, wq_b, rope_cs,
+                                                                      static_cast<int>(n_tokens), n_cols, eps,
+                                                                      inv_rms, q_out);
     } else if (n_cols / SmallCfg<8, 4>::kCols <= 256 && n_cols / SmallCfg<8, 4>::kCols >= 128) {
-      query_gemm_small_kernel<8, 4><<<n_cols / SmallCfg<8, 4>::kCols, 256, 0, stream>>>(
+      query_gemm_small_kernel<8, 4, kPacked><<<n_cols / SmallCfg<8, 4>::kCols, 256, 0, stream>>>(
           q_latent, gamma, wq_b, rope_cs, static_cast<int>(n_tokens), n_cols, eps, inv_rms, q_out);
     } else {
       const int n_slices = n_cols / SmallCfg<4, 4>::kCols;
       const int grid = n_slices < 256 ? n_slices : 256;
-      query_gemm_small_kernel<4, 4><<<grid, 256, 0, stream>>>(q_latent, gamma, wq_b, rope_cs,
-                                                           static_cast<int>(n_tokens), n_cols, eps, inv_rms, q_out);
+      query_gemm_small_kernel<4, 4, kPacked><<<grid, 256, 0, stream>>>(q_latent, gamma, wq_b, rope_cs,
+                                                                       static_cast<int>(n_tokens), n_cols, eps,
+                                                                       inv_rms, q_out);
     }
   } else {
     char* ws = static_cast<char*>(workspace);
@@ -652,7 +693,8 @@ hipError_t launch_query_path(int n_heads, int64_t n_tokens, const uint16_t* q_la
                                                                                             0, eps, inv, y);
       mark(ev, 1, stream);
       const int64_t blocks = static_cast<int64_t>(n_cols / gemm::kBN) * ((n_tokens + gemm::kBM - 1) / gemm::kBM);
-      query_gemm_nt_kernel<<<static_cast<unsigned>(blocks), 512, 0, stream>>>(wq_b, y, rope_cs, n_tokens, n_cols, q_out);
+      query_gemm_nt_kernel<kPacked><<<static_cast<unsigned>(blocks), 512, 0, stream>>>(wq_b, y, rope_cs, n_tokens,
+                                                                                        n_cols, q_out);
     } else {
       const int64_t n_tiles = y_tiles(n_tokens);
       normalize_kernel<true><<<static_cast<unsigned>(n_tiles * kYTile / 4), 256, 0, stream>>>(q_latent, gamma, n_tokens,
@@ -661,14 +703,26 @@ hipError_t launch_query_path(int n_heads, int64_t n_tokens, const uint16_t* q_la
       // 96-column tiles when they make exactly 256 (128 heads), else 128
       if (n_cols == 256 * 96) {
         const dim3 grid(256, static_cast<unsigned>((n_tokens + 127) / 128));
-        query_gemm_big_kernel<96, 128><<<grid, 256, 0, stream>>>(y, wq_b, rope_cs, n_tokens, n_cols, q_out);
+        query_gemm_big_kernel<96, 128, kPacked><<<grid, 256, 0, stream>>>(y, wq_b, rope_cs, n_tokens, n_cols, q_out);
       } else {
         const dim3 grid(n_cols / 128, static_cast<unsigned>((n_tokens + 127) / 128));
-        query_gemm_big_kernel<128, 128><<<grid, 256, 0, stream>>>(y, wq_b, rope_cs, n_tokens, n_cols, q_out);
+        query_gemm_big_kernel<128, 128, kPacked><<<grid, 256, 0, stream>>>(y, wq_b, rope_cs, n_tokens, n_cols, q_out);
       }
     }
   }
   mark(ev, 2, stream);
+}
+
+hipError_t launch_query_path(int n_heads, int64_t n_tokens, const uint16_t* q_latent, const float* gamma,
+                             const uint16_t* wq_b, bool packed, const float* rope_cs, uint16_t* q_out,
+                             float* inv_rms, void* workspace, const QueryLayout& lay, float eps, hipStream_t stream,
+                             hipEvent_t* ev) {
+  if (packed)
+    launch_query_kernels<true>(n_heads, n_tokens, q_latent, gamma, wq_b, rope_cs, q_out, inv_rms, workspace, lay, eps,
+                               stream, ev);
+  else
+    launch_query_kernels<false>(n_heads, n_tokens, q_latent, gamma, wq_b, rope_cs, q_out, inv_rms, workspace, lay,
+                                eps, stream, ev);
   return hipGetLastError();
 }
 

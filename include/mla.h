@@ -100,6 +100,26 @@ mla_status_t mla_query_path(const mla_dims_t* dims, int64_t n_tokens,
                             const float* rope_cs, uint16_t* q_out, float* inv_rms,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Query weights in the decode-friendly layout (the same values, rearranged once when the weights
+ * are loaded; "DeepSeek-V3.2-Exp · Query heads": wq_b maps the 1536 query-latent features to the
+ * n_heads*192 query features):
+ *   wq_b         bf16 [q_lora_rank, n_heads*192]           as mla_query_path takes it
+ *   wq_b_packed  bf16 [n_heads*192/32, q_lora_rank, 32]    output: wq_b_packed[g][k][j] = wq_b[k][32g + j],
+ *                                                          the same number of bytes as wq_b
+ * Each group of 32 output columns then holds its 1536 input rows back to back, so that the column
+ * slices the query products stream are a few contiguous runs instead of short pieces of every row.
+ * Pure data movement: bit-exact. Errors: MLA_ERR_INVALID_ARG for a NULL pointer,
+ * MLA_ERR_ALIGNMENT, MLA_ERR_UNSUPPORTED for other widths. */
+mla_status_t mla_wq_b_pack(const mla_dims_t* dims, const uint16_t* wq_b, uint16_t* wq_b_packed, hipStream_t stream);
+
+/* mla_query_path on the packed weights of mla_wq_b_pack: the same arguments, sizes, workspace and
+ * errors, wq_b_packed in place of wq_b, and bit-identical outputs (the products read the same
+ * weight tiles in the same order; only where they come from in memory differs). */
+mla_status_t mla_query_path_packed(const mla_dims_t* dims, int64_t n_tokens,
+                                   const uint16_t* q_latent, const float* q_norm_w, const uint16_t* wq_b_packed,
+                                   const float* rope_cs, uint16_t* q_out, float* inv_rms,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of device workspace mla_decode needs for `batch` sequences of at most max_seqlen cached
  * rows each. Host-only; no HIP call. */
 mla_status_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch, int64_t max_seqlen,
@@ -257,8 +277,8 @@ mla_status_t mla_output_proj(const mla_dims_t* dims, int64_t n_tokens, int32_t d
  * at the boundaries of the library's kernel stages, so a caller can time each stage on the stream
  * it runs on. stage_events is NULL or an array of (number of stages + 1) events, any of which may be
  * NULL: event i is recorded before stage i and the last after the final stage.
- *   mla_query_path_ex: 2 stages (RMSNorm pass -- empty when fused into the product, 32 tokens or
- *                      fewer --, product + RoPE)
+ *   mla_query_path_ex, mla_query_path_packed_ex: 2 stages (RMSNorm pass -- empty when fused into
+ *                      the product, 32 tokens or fewer --, product + RoPE)
  *   mla_decode_ex:     3 stages (absorb + run plan, split-KV attention, log-sum-exp combine + value projection)
  *   mla_decode_sparse_ex: the same 3 stages, the first also compacting the top-k lists
  *   mla_output_proj_ex: 2 stages (product, sum of the K-slice partials -- empty above 64 tokens)
@@ -268,6 +288,11 @@ mla_status_t mla_query_path_ex(const mla_dims_t* dims, int64_t n_tokens,
                                const float* rope_cs, uint16_t* q_out, float* inv_rms,
                                void* workspace, size_t workspace_bytes,
                                hipStream_t stream, hipEvent_t* stage_events);
+mla_status_t mla_query_path_packed_ex(const mla_dims_t* dims, int64_t n_tokens,
+                                      const uint16_t* q_latent, const float* q_norm_w, const uint16_t* wq_b_packed,
+                                      const float* rope_cs, uint16_t* q_out, float* inv_rms,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream, hipEvent_t* stage_events);
 mla_status_t mla_decode_ex(const mla_dims_t* dims, int32_t batch, const uint16_t* q, const uint16_t* wkv_b,
                            const uint16_t* kv_cache, const uint16_t* pe_cache,
                            const int64_t* cache_row_offset, const int32_t* cache_seqlens, int64_t max_seqlen,

@@ -96,6 +96,30 @@ def test_query_path_validation():
     assert q(ctypes.byref(d), 100, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, n.value - 1, None) == 5
 
 
+def test_packed_query_weights_validation():
+    lib = _lib()
+    d = _dims()
+    pk = lib.mla_wq_b_pack
+    assert pk(None, FAKE, FAKE, None) == 1
+    assert pk(ctypes.byref(d), None, FAKE, None) == 1
+    assert pk(ctypes.byref(d), FAKE, None, None) == 1
+    assert pk(ctypes.byref(d), MIS, FAKE, None) == 4
+    assert pk(ctypes.byref(d), FAKE, MIS, None) == 4
+    bad = _dims()
+    bad.n_heads = 48
+    assert pk(ctypes.byref(bad), FAKE, FAKE, None) == 2
+    # the packed query path validates as mla_query_path does
+    q = lib.mla_query_path_packed
+    assert q(None, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 1
+    assert q(ctypes.byref(d), -1, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 3
+    assert q(ctypes.byref(d), 0, None, None, None, None, None, None, None, 0, None) == 0
+    assert q(ctypes.byref(d), 4, FAKE, FAKE, None, FAKE, FAKE, None, None, 0, None) == 1
+    assert q(ctypes.byref(d), 4, FAKE, FAKE, MIS, FAKE, FAKE, None, None, 0, None) == 4
+    n = ctypes.c_size_t(0)
+    assert lib.mla_query_path_workspace_size(ctypes.byref(d), 100, ctypes.byref(n)) == 0
+    assert q(ctypes.byref(d), 100, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, n.value - 1, None) == 5
+
+
 def test_decode_validation_and_workspace():
     lib = _lib()
     d = _dims()

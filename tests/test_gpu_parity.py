@@ -60,6 +60,39 @@ def test_query_path_parity(H, n, with_inv):
         assert_f32_parity(inv, invo, "inv_rms")
 
 
+@pytest.mark.parametrize("H", [16, 64, 128])
+def test_wq_b_pack_is_the_stated_rearrangement(H):
+    """mla_wq_b_pack moves bytes only: packed[g, k, j] == wq_b[k, 32 g + j], bit for bit."""
+    say(f"wq_b_pack H={H}")
+    w = S.query_weights(H, 0, 260 + H)["wq_b"]
+    p = binding.wq_b_pack(dev_bf16(w), H)
+    torch.cuda.synchronize()
+    want = w.reshape(S.Q_LORA, H * 192 // 32, 32).transpose(1, 0, 2)
+    assert np.array_equal(host_bits(p), want)
+
+
+@pytest.mark.parametrize("H,n", [(16, 1), (64, 1), (128, 1), (32, 5), (64, 32), (128, 32), (128, 33),
+                                 (64, 67), (128, 200), (16, 1100), (128, 1024)])
+def test_query_path_packed_matches_stored_weights(H, n):
+    """mla_query_path_packed on mla_wq_b_pack's copy: bit-identical to mla_query_path on wq_b as
+    stored, on every product (n <= 32, 33..1023, >= 1024, and each slice width of the small one),
+    and within the bar of the oracle ("DeepSeek-V3.2-Exp · Query heads", query excerpt)."""
+    say(f"query_path packed H={H} n={n}")
+    x, g, w, cs = _query_case(H, n, 1, 300 + H + n)
+    wd = dev_bf16(w)
+    packed = binding.wq_b_pack(wd, H)
+    inv_p = torch.empty(n, dtype=torch.float32, device="cuda")
+    inv_s = torch.empty(n, dtype=torch.float32, device="cuda")
+    qp, _ = binding.query_path(dev_bf16(x), dev(g), packed, dev(cs), H, inv_rms=inv_p, packed=True)
+    qs, _ = binding.query_path(dev_bf16(x), dev(g), wd, dev(cs), H, inv_rms=inv_s)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(qp), host_bits(qs))
+    assert np.array_equal(inv_p.cpu().numpy().view(np.uint32), inv_s.cpu().numpy().view(np.uint32))
+    qo, invo = O.query_path(x, g, w, cs, H, round_output=False)
+    assert_bf16_parity(host_bits(qp), qo, "q_out (packed weights)")
+    assert_f32_parity(inv_p.cpu().numpy(), invo, "inv_rms (packed weights)")
+
+
 @pytest.mark.slow
 def test_query_path_past_4gib_of_activations():
     """16 heads over 1,398,200 tokens: the normalised activations span 4.3 GB, so one 256-token
