@@ -791,8 +791,8 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
         c.alpha_s[t & 1][hl0 + 16 * hb] = alpha;
       }
     };
-    // Iteration j: the scores of tile j+1 (of a stale stage past the last tile: computed, never
-    // used) and the common softmax part of tile j in one basic block, so that the softmax's vector
+    // Iteration j < n_tiles - 1: the scores of tile j+1 and the common softmax part of tile j in
+    // one basic block, so that the softmax's vector
     // instructions can fill the gaps between MFMAs: four operand reads go out first, then each
     // pair of MFMAs (one per head block) is followed by the next read.
     auto step = [&](int j, const f32x4 (&cur)[2][2], f32x4 (&next)[2][2], bool mask) {
@@ -808,6 +808,12 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       if (__any(above)) softmax_full(j, cur, mask);
     };
+    // The segment's last tile: its masked softmax alone (there is no next tile to score).
+    auto last_step = [&](int j, const f32x4 (&cur)[2][2]) {
+      lds_barrier();   // P(j-1) consumed by the value waves
+      softmax_common(j, cur, true);
+      if (__any(above)) softmax_full(j, cur, true);
+    };
 
     f32x4 sa[2][2], sb[2][2];
     lds_barrier();   // tile 0 landed
@@ -821,9 +827,9 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
     }
     if (n_tiles - j == 2) {
       step(j, sa, sb, false);
-      step(j + 1, sb, sa, true);
+      last_step(j + 1, sb);
     } else {
-      step(j, sa, sb, true);
+      last_step(j, sa);
     }
     lds_barrier();   // P of the last tile published
     // the log-sum-exp from the fp32 weights (the value waves normalise by their rounded sum)
