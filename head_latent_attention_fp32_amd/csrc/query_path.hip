@@ -58,10 +58,16 @@ __global__ __launch_bounds__(256) void normalize_kernel(const uint16_t* __restri
   }
   const uint16_t* row = x + m * kQLora;
   bf16x8 v[kPer];
-  float s = 0.f;
+  float4 gl[kPer][2];   // the gain, loaded with the activation rather than after the reduction
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     v[i] = as_bf16x8(ldg16(row + (i * 64 + lane) * 8));
+    gl[i][0] = *reinterpret_cast<const float4*>(gamma + (i * 64 + lane) * 8);
+    gl[i][1] = *reinterpret_cast<const float4*>(gamma + (i * 64 + lane) * 8 + 4);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float f = static_cast<float>(v[i][e]);
@@ -75,8 +81,7 @@ __global__ __launch_bounds__(256) void normalize_kernel(const uint16_t* __restri
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int k = (i * 64 + lane) * 8;
-    const float4 g0 = *reinterpret_cast<const float4*>(gamma + k);
-    const float4 g1 = *reinterpret_cast<const float4*>(gamma + k + 4);
+    const float4 g0 = gl[i][0], g1 = gl[i][1];
     const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
     float o[8];
 #pragma unroll
@@ -212,6 +217,17 @@ __global__ __launch_bounds__(64 * NW, 1) void query_gemm_small_kernel(
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) xf[mb][st] = as_bf16x8(ldg16(row + st * 32));
   }
+  // With 8 waves (6 k-steps each, registers to spare) the gain goes out with the activation instead
+  // of after the row statistics
+  constexpr int kGainAhead = NW == 8 ? kSteps : 1;
+  float4 gl[kGainAhead][2];
+  if constexpr (NW == 8) {
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      gl[st][0] = *reinterpret_cast<const float4*>(gamma + k0 + st * 32 + grp * 8);
+      gl[st][1] = *reinterpret_cast<const float4*>(gamma + k0 + st * 32 + grp * 8 + 4);
+    }
+  }
   int issued = 0;
   while (issued < C::kRing && issued < total_steps) issue(issued++);
   float ss[2] = {0.f, 0.f};
@@ -244,8 +260,9 @@ __global__ __launch_bounds__(64 * NW, 1) void query_gemm_small_kernel(
   // y = bf16(gamma * (x * inv_rms)), in place
 #pragma unroll
   for (int st = 0; st < kSteps; ++st) {
-    const float4 g0 = *reinterpret_cast<const float4*>(gamma + k0 + st * 32 + grp * 8);
-    const float4 g1 = *reinterpret_cast<const float4*>(gamma + k0 + st * 32 + grp * 8 + 4);
+    const float4 g0 = NW == 8 ? gl[st % kGainAhead][0] : *reinterpret_cast<const float4*>(gamma + k0 + st * 32 + grp * 8);
+    const float4 g1 =
+        NW == 8 ? gl[st % kGainAhead][1] : *reinterpret_cast<const float4*>(gamma + k0 + st * 32 + grp * 8 + 4);
     const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
