@@ -1052,6 +1052,11 @@ __global__ __launch_bounds__(512, 4) void combine_proj_kernel(
   }
 
   const int j = tid >> 5, c0 = (tid & 31) * 16;   // thread group j (32 threads), columns c0 .. c0 + 15
+  // A wave holds thread groups ja and ja + 1: the prefix sums they need are wave-uniform and come
+  // through scalar loads, which do not queue behind W_UV's vector loads (those complete in issue
+  // order, so a vector load of them would wait for all of W_UV)
+  const int ja = 2 * __builtin_amdgcn_readfirstlane(wave);
+  typedef const __attribute__((address_space(4))) int64_t* const_i64_ptr;
   // groups of 16 sequences b0, b0 + 16 gridDim.y, ...: W_UV stays in registers across them
   for (int b0 = gy * 16; b0 < batch; b0 += ngy * 16) {
     // With fewer than 9 sequences in the group, each sequence's runs are shared by `parts` thread
@@ -1065,7 +1070,10 @@ __global__ __launch_bounds__(512, 4) void combine_proj_kernel(
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
     float M = -INFINITY, wsum = 0.f;
     if (js < nseq) {
-      const int64_t x0 = cum[b], x1 = cum[b + 1];
+      const const_i64_ptr cs = (const_i64_ptr)(cum + b0);
+      const int ka = min(ja / parts, nseq - 1), kb = min((ja + 1) / parts, nseq - 1);
+      const int64_t xa0 = cs[ka], xa1 = cs[ka + 1], xb0 = cs[kb], xb1 = cs[kb + 1];
+      const int64_t x0 = j == ja ? xa0 : xb0, x1 = j == ja ? xa1 : xb1;
       if (x1 > x0) {
         // One pass over the runs, kMergeAhead at a time: their loads go out together, then the running
         // maximum M moves to cover them (the sums so far scaled by e^(M_old - M_new)).
