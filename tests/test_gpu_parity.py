@@ -72,7 +72,7 @@ def test_wq_b_pack_is_the_stated_rearrangement(H):
 
 
 @pytest.mark.parametrize("H,n", [(16, 1), (64, 1), (128, 1), (32, 5), (64, 32), (128, 32), (128, 33),
-                                 (64, 67), (128, 200), (16, 1100), (128, 1024)])
+                                 (64, 67), (128, 200), (64, 1023), (16, 1100), (128, 1024)])
 def test_query_path_packed_matches_stored_weights(H, n):
     """mla_query_path_packed on mla_wq_b_pack's copy: bit-identical to mla_query_path on wq_b as
     stored, on every product (n <= 32, 33..1023, >= 1024, and each slice width of the small one),
