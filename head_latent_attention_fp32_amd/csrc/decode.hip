@@ -414,9 +414,10 @@ __global__ __launch_bounds__(256) void topk_compact_kernel(const int32_t* __rest
 //                         S^T[t][h] = sum_k tile[t][k] q[h][k] on MFMA (A operand: ds_read_b128 of
 //                         tile rows, each read feeding both head blocks), then the softmax: per
 //                         head a reference m (log2 units, scale folded in) that moves only when a
-//                         tile's maximum exceeds it by more than 8, so p = 2^(s - m) <= 2^8,
-//                         written to LDS as bf16 (a common part keeps the reference; a full part
-//                         on a branch of its own moves it);
+//                         lane's sum of a tile's weights exceeds 2^16 (then to the head's maximum,
+//                         if that lies more than 8 above it), p = 2^(s - m) written to LDS as bf16
+//                         (a common part keeps the reference; a full part on a branch of its own
+//                         moves it);
 //      value waves 2, 3, 6, 7   value wave v (0..3 in that order) owns latent columns
 //                         [128 v, 128 v + 128) of all 64 heads and adds O^T[c][h] += sum_t
 //                         tile[t][c] P^T[t][h] (A operand: ds_read_b64_tr_b16, the transposing LDS
@@ -667,8 +668,8 @@ __device__ __forceinline__ void load_role(const AttendCtx& c) {
 // ds_read_b128 of tile rows, each read feeding the MFMAs of both head blocks). Iteration j (one
 // barrier each) runs the MFMAs of tile j+1 and, interleaved with them, the softmax of tile j, whose
 // scores the previous iteration left in registers: per head a reference m (log2 units, scale folded
-// in) that moves only when a tile's maximum exceeds it by more than 8, so that p = 2^(s - m) <= 2^8;
-// P goes to LDS as bf16 with the head's rescale factor. They issue no loads: a tile is complete
+// in) that moves only when a lane's sum of a tile's weights p = 2^(s - m) exceeds 2^16; P goes to
+// LDS as bf16 with the head's rescale factor. They issue no loads: a tile is complete
 // once the loader waves, which wait for their own loads of it, reach the next barrier.
 __device__ __forceinline__ void score_role(const AttendCtx& c) {
   const int s = c.wave, lane = c.lane, r = lane & 15, grp = lane >> 4;
@@ -726,15 +727,20 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
           acc[tb][1] = mfma16x16x32(a, qf[1][ks], acc[tb][1]);
         }
     };
-    // per head block: reference (log2 units) and this lane's running sum of its tokens' weights
-    float m_ref[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f}, lsum_prev[2] = {0.f, 0.f};
+    // per head block: reference (log2 units) and this lane's running sum of its tokens' weights. The
+    // reference starts finite, far below any score, so that a masked score (-inf) gives the weight
+    // 0 rather than NaN before the first tile moves it (this file is built without NaN semantics).
+    constexpr float kNoRef = -1e30f;
+    float m_ref[2] = {kNoRef, kNoRef}, lsum[2] = {0.f, 0.f}, lsum_prev[2] = {0.f, 0.f};
     // Softmax of tile t from its scores, in two parts. The common part assumes the references stay
-    // (rescale factor exactly 1): P = 2^(s - m) and the sums, with no cross-lane step, and reports
-    // whether any of the lane's scores exceeds its reference by more than 8. If one does anywhere
-    // in the wave (rare after the first tile of a segment, which always moves the references from
-    // -inf), the full part, on a branch of its own, takes each head's maximum, moves the references
-    // that must move and redoes P, the sums and the factors. kMask: rows at or past the segment
-    // end count as -inf (only the last tile of a segment can have such rows).
+    // (rescale factor exactly 1): P = 2^(s - m) and the sums, with no cross-lane step and no
+    // maximum, and reports whether the lane's sum of its 8 weights of a head exceeds 2^16 (each
+    // weight is below that sum, so the bf16 weights and the fp32 sums stay far inside their range
+    // otherwise). If one does anywhere in the wave (rare after the first tile of a segment, whose
+    // reference kNoRef makes every weight +inf), the full part, on a branch of its own, takes each
+    // head's maximum, moves the references that lie more than 8 below it and redoes P, the sums and
+    // the factors. kMask: rows at or past the segment end count as -inf (only the last tile of a
+    // segment can have such rows).
     bool above = false;
     auto scaled = [&](int t, const f32x4 (&sc)[2][2], int hb, bool mask, float (&y)[8]) {
       const int valid = sg.n_rows - t * kTileTok - 4 * grp;
@@ -747,7 +753,7 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
         }
     };
     // The common part works on the raw scores: p = 2^(s c - m) as one fma and one exp per score
-    // (c = scale log2 e > 0), and the test against the reference on the raw maximum.
+    // (c = scale log2 e > 0), and tests the sum of the lane's weights, which it forms anyway.
     auto softmax_common = [&](int t, const f32x4 (&sc)[2][2], bool mask) {
       const int valid = sg.n_rows - t * kTileTok - 4 * grp;
       bool up = false;
@@ -759,16 +765,15 @@ __device__ __forceinline__ void score_role(const AttendCtx& c) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             x[tb * 4 + j] = (!mask || tb * 16 + j < valid) ? sc[tb][hb][j] : -INFINITY;
-        const float xmax =
-            fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
         const float nm = -m_ref[hb];
 #pragma unroll
         for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(x[i], c.scale_log2, nm));
         lsum_prev[hb] = lsum[hb];
-        lsum[hb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        const float ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        lsum[hb] += ps;
         *reinterpret_cast<bf16x8*>(c.pbuf + (t & 1) * kPBytes + p_wr + hb * 256) = bf16x8_from_f32(p);
         c.alpha_s[t & 1][hl0 + 16 * hb] = 1.f;
-        up |= xmax * c.scale_log2 > m_ref[hb] + 8.f;
+        up |= ps > 65536.f;
       }
       above = up;
     };
