@@ -126,8 +126,8 @@ __device__ __forceinline__ float sum_over_rows(float v) {
 }
 
 // 2^x with the hardware instruction (v_exp_f32): no range reduction around it, so results below
-// 2^-126 flush to zero -- for softmax weights, which are at most 2^8 here, that is below bf16's
-// resolution of any sum they enter. 2^-inf = 0.
+// 2^-126 flush to zero -- for softmax weights, which are at most 2^16 here (2^8 in the prefill),
+// that is far below bf16's resolution of any sum they enter. 2^-inf = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 constexpr float kLog2e = 1.4426950408889634f;
