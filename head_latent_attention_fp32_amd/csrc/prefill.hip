@@ -170,16 +170,24 @@ __global__ __launch_bounds__(256) void vbound_kernel(const uint16_t* __restrict_
   const int tid = threadIdx.x;
   float m = 0.f;
   if (static_cast<int>(blockIdx.x) < n_heads) {
-    // thread = (row 2 * (tid / 4) + {0, 1}, quarter tid % 4 of its 512 columns)
+    // thread = (row 2 * (tid / 4) + {0, 1}, quarter tid % 4 of its 512 columns); the thread's 32
+    // loads go out together (the block's 128 KB in flight at once rather than in rounds)
     const int h = blockIdx.x;
+    uint4 u[2][16];
+#pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       const int row = 2 * (tid >> 2) + rr;
       const uint16_t* w = wkv_b + (static_cast<int64_t>(h) * kKvRows + kNope + row) * kKvLora + (tid & 3) * 128;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) u[rr][c] = ldg16(w + 8 * c);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // (the scheduler would otherwise pair each load with its sums)
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
       float s = 0.f;
-#pragma unroll 4
-      for (int c = 0; c < 128; c += 8) {
-        const uint4 u = ldg16(w + c);
-        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const uint32_t wd[4] = {u[rr][c].x, u[rr][c].y, u[rr][c].z, u[rr][c].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) s += fabsf(bf16_bits_to_f32(wd[k] & 0xFFFFu)) + fabsf(bf16_bits_to_f32(wd[k] >> 16));
       }
