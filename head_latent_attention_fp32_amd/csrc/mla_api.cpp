@@ -119,6 +119,11 @@ mla_status_t mla_wq_b_pack(const mla_dims_t* dims, const uint16_t* wq_b, uint16_
   if (st != MLA_OK) return st;
   if (!wq_b || !wq_b_packed) return MLA_ERR_INVALID_ARG;
   if (!aligned16(wq_b) || !aligned16(wq_b_packed)) return MLA_ERR_ALIGNMENT;
+  // the rearrangement cannot run in place: the two byte ranges must not overlap
+  const uintptr_t a = reinterpret_cast<uintptr_t>(wq_b), b = reinterpret_cast<uintptr_t>(wq_b_packed);
+  const uintptr_t bytes = static_cast<uintptr_t>(dims->q_lora_rank) * dims->n_heads *
+                          (dims->qk_nope_dim + dims->qk_rope_dim) * sizeof(uint16_t);
+  if (a < b + bytes && b < a + bytes) return MLA_ERR_INVALID_ARG;
   hipError_t e = mla::launch_pack_wq_b(dims->n_heads, wq_b, wq_b_packed, stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }

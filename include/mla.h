@@ -108,8 +108,9 @@ mla_status_t mla_query_path(const mla_dims_t* dims, int64_t n_tokens,
  *                                                          the same number of bytes as wq_b
  * Each group of 32 output columns then holds its 1536 input rows back to back, so that the column
  * slices the query products stream are a few contiguous runs instead of short pieces of every row.
- * Pure data movement: bit-exact. Errors: MLA_ERR_INVALID_ARG for a NULL pointer,
- * MLA_ERR_ALIGNMENT, MLA_ERR_UNSUPPORTED for other widths. */
+ * Pure data movement: bit-exact; not in place. Errors: MLA_ERR_INVALID_ARG for a NULL pointer or
+ * for byte ranges of wq_b and wq_b_packed that overlap, MLA_ERR_ALIGNMENT, MLA_ERR_UNSUPPORTED for
+ * other widths. */
 mla_status_t mla_wq_b_pack(const mla_dims_t* dims, const uint16_t* wq_b, uint16_t* wq_b_packed, hipStream_t stream);
 
 /* mla_query_path on the packed weights of mla_wq_b_pack: the same arguments, sizes, workspace and

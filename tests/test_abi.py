@@ -105,6 +105,11 @@ def test_packed_query_weights_validation():
     assert pk(ctypes.byref(d), FAKE, None, None) == 1
     assert pk(ctypes.byref(d), MIS, FAKE, None) == 4
     assert pk(ctypes.byref(d), FAKE, MIS, None) == 4
+    # not in place: overlapping byte ranges are rejected before any launch
+    size = 1536 * d.n_heads * 192 * 2
+    assert pk(ctypes.byref(d), FAKE, FAKE, None) == 1
+    assert pk(ctypes.byref(d), FAKE, FAKE + size - 16, None) == 1
+    assert pk(ctypes.byref(d), FAKE + size - 16, FAKE, None) == 1
     bad = _dims()
     bad.n_heads = 48
     assert pk(ctypes.byref(bad), FAKE, FAKE, None) == 2
