@@ -1299,11 +1299,12 @@ hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16
   mark(ev, 2, stream);
   {
     // At most kMergeBlocks blocks, each with its head's W_UV in registers for as many sequence
-    // groups as that leaves to it. A single group (16 sequences or fewer, whose partials are few)
-    // is merged by up to four blocks per head, each projecting a quarter of the outputs with a
-    // quarter of W_UV, so that W_UV is read by more compute units.
+    // groups as that leaves to it. A single group (16 sequences or fewer) is merged by two blocks
+    // per head, each projecting half of the outputs with half of W_UV, so that W_UV is read by more
+    // compute units; by four when it holds at most four sequences, whose partials are few (every
+    // block of the group merges all of them).
     const int groups = (batch + 15) / 16, per_head = kMergeBlocks / n_heads;
-    const int dsplit = groups == 1 ? (per_head >= 4 ? 4 : (per_head >= 2 ? 2 : 1)) : 1;
+    const int dsplit = groups > 1 ? 1 : (batch <= 4 && per_head >= 4) ? 4 : (per_head >= 2 ? 2 : 1);
     combine_proj_kernel<<<dim3(n_heads, (groups < per_head ? groups : per_head) * dsplit), 512, 0, stream>>>(
         plan, cum, batch, n_heads, part_o, part_s, part_l, wkv_b, dsplit, out, lse);
   }
