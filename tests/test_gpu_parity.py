@@ -162,6 +162,9 @@ DECODE_SMALL = [
     # 72 sequences over 4 merge blocks per head: a block's second group holds 8 sequences
     (128, [(53 * i) % 300 for i in range(72)], "packed"),
     (64, [(29 * i) % 400 + 33 for i in range(40)], "padded"),
+    # one merge group split four ways (at most four sequences) or two ways (5..16), and two groups
+    (128, [700, 1, 2049, 33], "packed"), (128, [(61 * i) % 900 + 1 for i in range(16)], "padded"),
+    (128, [(67 * i) % 800 for i in range(17)], "packed"),
 ]
 
 
