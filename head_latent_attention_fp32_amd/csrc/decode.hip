@@ -48,18 +48,23 @@ struct RunStart {
 __device__ __forceinline__ int64_t run_of(int64_t x, int64_t N, int64_t G) { return ((x + 1) * G - 1) / N; }
 
 // ---------------------------------------------------------------------------------------------
-// 1. q_lat[b,h,c] = bf16(sum_d q[b,h,d] W_UK[h,d,c]); block (h, 1 + 64-column slice of c).
+// 1. q_lat[b,h,c] = bf16(sum_d q[b,h,d] W_UK[h,d,c]); block (h, 1 + kCols-column slice of c).
 //    W_UK[h] rows are stored with c contiguous; the slice goes to LDS as it is and the transposing
 //    LDS read gives the MFMA B operand eight consecutive d per lane. Block (0, 0), dispatched
 //    first, builds the plan.
 // ---------------------------------------------------------------------------------------------
-constexpr int kWrPitch = 64 * 2 + 16;   // bytes per W_UK row of a 64-column slice in LDS
+// W_UK columns per absorb block: 128 from 32 sequences up (each query row is then read by four
+// blocks instead of eight, and a block writes 256 contiguous bytes of it), else 64 (more blocks to
+// stream W_UK when it dominates). Bytes per W_UK row of a slice in LDS: kCols * 2 + 16.
+constexpr int kAbsWideFrom = 32;
 
+template <int kCols>
 __global__ __launch_bounds__(256) void absorb_plan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ wkv_b, int batch, int n_heads,
     uint16_t* __restrict__ q_lat, const int32_t* __restrict__ seqlens, int64_t max_seqlen,
     int units, int min_unit_tokens, Plan* __restrict__ plan, int64_t* __restrict__ cum,
     const int64_t* __restrict__ row_offset, int64_t cache_rows_per_seq, RunStart* __restrict__ runs) {
+  constexpr int kAbsCols = kCols, kAbsCb = kCols / 16, kWrPitch = kCols * 2 + 16;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
 
@@ -193,11 +198,11 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
     return;
   }
 
-  // Block (h, 1 + slice): columns 64 slice .. +63 for every query. Wave w takes the query groups
+  // Block (h, 1 + slice): columns kCols slice .. + kCols - 1 for every query. Wave w takes the query groups
   // (16 queries each) w, w + 4, ...; a wave's first kAhead groups are loaded before the weight
   // slice, so that their latency overlaps its load, and every later group kAhead products ahead.
   const int h = blockIdx.x;
-  const int c0 = (blockIdx.y - 1) * 64;
+  const int c0 = (blockIdx.y - 1) * kAbsCols;
   const int r = lane & 15, grp = lane >> 4;
   const int n_grp = (batch + 15) / 16;
   constexpr int kAhead = 4;
@@ -211,12 +216,12 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
   for (int i = 0; i < kAhead; ++i)
     if (wave + 4 * i < n_grp) load_q(wave + 4 * i, qa[i]);
 
-  // W_UK[h][0:128][c0:c0+64], row-major in LDS (rows kWrPitch bytes apart)
+  // W_UK[h][0:128][c0:c0+kCols], row-major in LDS (rows kWrPitch bytes apart)
   const uint16_t* wk = wkv_b + static_cast<int64_t>(h) * kKvRows * kKvLora + c0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kAbsCols / 16; ++i) {
     const int idx = tid + 256 * i;
-    const int d = idx >> 3, ch = idx & 7;
+    const int d = idx / (kAbsCols / 8), ch = idx % (kAbsCols / 8);
     *reinterpret_cast<uint4*>(wr + d * kWrPitch + ch * 16) = ldg16(wk + static_cast<int64_t>(d) * kKvLora + ch * 8);
   }
   __syncthreads();
@@ -224,9 +229,9 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
 
   // B operand of column block cb, k-step ks: column c = 16 cb + r, rows d = 32 ks + 8 grp .. +7,
   // by two transposing reads (rows +0..3 and +4..7 of the 16-column block)
-  bf16x8 bw[4][4];
+  bf16x8 bw[kAbsCb][4];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+  for (int cb = 0; cb < kAbsCb; ++cb)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const uint8_t* p = wr + (32 * ks + 8 * grp + (r >> 2)) * kWrPitch + (16 * cb + 4 * (r & 3)) * 2;
@@ -236,14 +241,14 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(
       bw[cb][ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 
-  // q_lat^T = W_UK^T q^T for the slice's 64 columns x 16 queries: lane (r, grp) ends with columns
-  // 16 cb + 4 grp .. +3 of query 16 gi + r (one 8-byte store per column block: 128 contiguous
-  // bytes of the query's row per wave)
+  // q_lat^T = W_UK^T q^T for the slice's kCols columns x 16 queries: lane (r, grp) ends with
+  // columns 16 cb + 4 grp .. +3 of query 16 gi + r (one 8-byte store per column block: 2 kCols
+  // contiguous bytes of the query's row per wave)
   auto product = [&](int gi, const uint4 (&a)[4]) {
     const int b = 16 * gi + r;
     uint16_t* dst = q_lat + (static_cast<int64_t>(b) * n_heads + h) * kKvLora + c0 + grp * 4;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cb = 0; cb < kAbsCb; ++cb) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(bw[cb][ks], as_bf16x8(a[ks]), acc);
@@ -1282,9 +1287,14 @@ hipError_t launch_decode(int n_heads, int batch, const uint16_t* q, const uint16
                                                             table, list, counts);
   }
   // the run plan covers the attended rows: L_b per sequence, or the count of its top-k positions
-  absorb_plan_kernel<<<dim3(n_heads, 1 + kKvLora / 64), 256, 0, stream>>>(
-      q, wkv_b, batch, n_heads, q_lat, sparse ? counts : seqlens, sparse ? topk : max_seqlen, lay.units,
-      lay.min_unit_tokens, plan, cum, row_offset, max_seqlen, runs);
+  if (batch >= kAbsWideFrom)
+    absorb_plan_kernel<128><<<dim3(n_heads, 1 + kKvLora / 128), 256, 0, stream>>>(
+        q, wkv_b, batch, n_heads, q_lat, sparse ? counts : seqlens, sparse ? topk : max_seqlen, lay.units,
+        lay.min_unit_tokens, plan, cum, row_offset, max_seqlen, runs);
+  else
+    absorb_plan_kernel<64><<<dim3(n_heads, 1 + kKvLora / 64), 256, 0, stream>>>(
+        q, wkv_b, batch, n_heads, q_lat, sparse ? counts : seqlens, sparse ? topk : max_seqlen, lay.units,
+        lay.min_unit_tokens, plan, cum, row_offset, max_seqlen, runs);
   mark(ev, 1, stream);
   {
     const int n_groups = (n_heads + 63) / 64;
